@@ -1,0 +1,300 @@
+"""Pins of the oracle's compression, scoring, selection and attention.
+
+Each check compares the oracle with something other than itself: a closed form
+(block mean, one-hot gate, the hand-derived example in
+tests/golden/pool_worked_example.txt), an invariant (RoPE norms and relative
+positions, softmax shift invariance), a pure-Python loop on tiny inputs, exact
+rational arithmetic (MXFP4 dot products), or torch's scaled-dot-product
+attention in float64 (dense causal, sliding-window and duplicated-key forms).
+"""
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as A
+from oracle import compress as C
+from oracle import formats as F
+from oracle import indexer as I
+from oracle import model as M
+from oracle import rope as R
+
+GOLDEN = os.path.join(os.path.dirname(__file__), 'golden')
+
+
+# ------------------------------------------------------------------ RoPE ----
+
+def test_rope_identity_at_zero_and_norms():
+    g = np.random.default_rng(0)
+    x = g.standard_normal((5, 192))
+    assert np.array_equal(R.apply(x, np.zeros(5, np.int64)), x)
+    y = R.apply(x, np.array([1, 7, 4095, 65535, 1048575]))
+    assert np.array_equal(y[:, :128], x[:, :128])
+    pn = lambda z: z[:, 128::2] ** 2 + z[:, 129::2] ** 2
+    assert np.allclose(pn(y), pn(x), rtol=1e-13, atol=0)
+
+
+def test_rope_relative_position():
+    g = np.random.default_rng(1)
+    q, k = g.standard_normal(128), g.standard_normal(128)
+    ref = R.apply(q, np.int64(1000)) @ R.apply(k, np.int64(990))
+    for p in (10, 5000, 1048575):
+        assert abs(R.apply(q, np.int64(p)) @ R.apply(k, np.int64(p - 10)) - ref) < 1e-9
+
+
+def test_rope_complex_multiplication():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((3, 128))
+    pos = np.array([3, 100000, 1048575])
+    y = R.apply(x, pos, 10000.0)
+    z = x[:, 64::2] + 1j * x[:, 65::2]
+    theta = np.array([10000.0 ** (-(2 * i) / 64) for i in range(32)])
+    zz = z * np.exp(1j * (pos[:, None] * theta[None, :]))
+    assert np.allclose(y[:, 64::2], zz.real, atol=1e-12) and np.allclose(y[:, 65::2], zz.imag, atol=1e-12)
+
+
+# --------------------------------------------------------------- pooling ----
+
+def test_pool_worked_example():
+    x = np.array([[[1.0], [2.0], [3.0], [4.0]]])
+    l5 = math.log(5.0)
+    a1 = C.gate_weights(np.array([[0, 0, 0, l5]], np.float32), np.zeros(4, np.float32))
+    a2 = C.gate_weights(np.array([[0, 0, 0, l5]], np.float32), np.array([l5, 0, 0, -l5], np.float32))
+    assert abs(C.pool(x, a1)[0, 0, 0] - 3.25) < 1e-6
+    assert abs(C.pool(x, a2)[0, 0, 0] - 1.75) < 1e-6
+    lines = [l for l in open(os.path.join(GOLDEN, 'pool_worked_example.txt')) if l.startswith('case')]
+    assert [float(l.split()[-1]) for l in lines] == [3.25, 1.75]
+
+
+@pytest.mark.parametrize('m', [1, 2, 4, 8, 128])
+def test_pool_uniform_gate_is_block_mean(m):
+    g = np.random.default_rng(m)
+    T = 4 * m
+    k = g.standard_normal((2, T, 192)).astype(np.float32)
+    v = g.standard_normal((2, T, 192)).astype(np.float32)
+    gate = np.full((2, T), 0.7, np.float32)
+    beta = np.full(m, -0.3, np.float32)
+    ek, ev, _ = C.compress(k, v, gate, beta, pos0=8 * m)
+    mean_v = v.reshape(2, 4, m, 192).mean(2)
+    assert np.allclose(ev, mean_v, rtol=1e-6, atol=1e-6)
+    rot = R.apply(k.astype(np.float64), (8 * m + np.arange(T))[None, :])
+    assert np.allclose(ek, rot.reshape(2, 4, m, 192).mean(2), rtol=1e-6, atol=1e-6)
+
+
+def test_pool_one_hot_and_shift_invariance():
+    g = np.random.default_rng(3)
+    v = g.standard_normal((1, 8, 128)).astype(np.float32)
+    gate = np.zeros((1, 8), np.float32)
+    gate[0, 2] = 200.0
+    gate[0, 7] = 200.0
+    _, ev, _ = C.compress(v, v, gate, np.zeros(4, np.float32), 0)
+    assert np.allclose(ev[0, 0], v[0, 2]) and np.allclose(ev[0, 1], v[0, 7])
+    # dyadic values, so that the shifted inputs are exact in float32
+    gate = (np.round(g.standard_normal((1, 8)) * 1024) / 1024).astype(np.float32)
+    beta = (np.round(g.standard_normal(4) * 1024) / 1024).astype(np.float32)
+    a = C.gate_weights(gate, beta)
+    b = C.gate_weights(gate + np.float32(3.0), beta - np.float32(1.5))
+    assert np.allclose(a, b, rtol=1e-12, atol=0)
+
+
+def test_pool_m1_is_rotated_token():
+    g = np.random.default_rng(4)
+    k = g.standard_normal((1, 5, 128)).astype(np.float32)
+    ek, ev, _ = C.compress(k, k, g.standard_normal((1, 5)).astype(np.float32), np.array([0.3], np.float32), 17)
+    assert np.array_equal(ev, k)
+    assert np.array_equal(ek, R.apply(k.astype(np.float64), (17 + np.arange(5))[None, :]).astype(np.float32))
+
+
+def test_pool_python_loop():
+    g = np.random.default_rng(5)
+    m, T, D = 4, 8, 128
+    k = g.standard_normal((1, T, D)).astype(np.float32)
+    v = g.standard_normal((1, T, D)).astype(np.float32)
+    u = g.standard_normal((1, T, 64)).astype(np.float32)
+    gate = g.standard_normal((1, T)).astype(np.float32)
+    beta = (0.1 * g.standard_normal(m)).astype(np.float32)
+    ek, ev, eu = C.compress(k, v, gate, beta, pos0=400, raw_ik=u)
+    for e in range(T // m):
+        z = [float(gate[0, e * m + r]) + float(beta[r]) for r in range(m)]
+        mx = max(z)
+        ex = [math.exp(zz - mx) for zz in z]
+        alpha = [x / sum(ex) for x in ex]
+        for d in range(D):
+            acc_v = sum(alpha[r] * float(v[0, e * m + r, d]) for r in range(m))
+            assert abs(acc_v - ev[0, e, d]) <= 1e-6 * max(1, abs(acc_v))
+        for i in range(32):
+            acc_x = acc_y = 0.0
+            for r in range(m):
+                p = 400 + e * m + r
+                ang = p * 10000.0 ** (-2 * i / 64)
+                x0, y0 = float(k[0, e * m + r, 64 + 2 * i]), float(k[0, e * m + r, 65 + 2 * i])
+                acc_x += alpha[r] * (x0 * math.cos(ang) - y0 * math.sin(ang))
+                acc_y += alpha[r] * (x0 * math.sin(ang) + y0 * math.cos(ang))
+            assert abs(acc_x - ek[0, e, 64 + 2 * i]) <= 1e-6 and abs(acc_y - ek[0, e, 65 + 2 * i]) <= 1e-6
+        for d in range(64):
+            acc_u = sum(alpha[r] * float(u[0, e * m + r, d]) for r in range(m))
+            assert abs(acc_u - eu[0, e, d]) <= 1e-6 * max(1, abs(acc_u))
+
+
+# --------------------------------------------------------------- indexer ----
+
+def test_index_scores_python_loop():
+    g = np.random.default_rng(6)
+    H, d, N = 3, 8, 11
+    iq, w, keys = g.standard_normal((H, d)), g.uniform(-1, 1, H).astype(np.float32), g.standard_normal((N, d))
+    got = I.index_scores(iq, w, keys)
+    for e in range(N):
+        ref = 0.0
+        for h in range(H):
+            dot = sum(iq[h, j] * keys[e, j] for j in range(d))
+            ref += float(w[h]) * (dot if dot > 0 else 0.0)
+        assert abs(ref - got[e]) < 1e-12
+
+
+def test_mxfp4_dot_products_are_exact():
+    g = np.random.default_rng(7)
+    x = (g.standard_normal((6, 128)) * 3).astype(np.float32)
+    y = (g.standard_normal((9, 128)) * 0.01).astype(np.float32)
+    px, sx = F.mxfp4_quantize(x)
+    py, sy = F.mxfp4_quantize(y)
+    dx, dy = F.mxfp4_dequantize(px, sx), F.mxfp4_dequantize(py, sy)
+    cx, cy = F.mxfp4_unpack(px), F.mxfp4_unpack(py)
+    got = dx @ dy.T
+    half = {c: Fraction(int(round(2 * abs(F.E2M1_VALUES[c])))) * (-1 if c & 8 else 1) for c in range(16)}
+    for i in range(6):
+        for j in range(9):
+            tot = Fraction(0)
+            for b in range(4):
+                e = int(sx[i, b]) - 127 + int(sy[j, b]) - 127
+                s = sum(half[cx[i, 32 * b + t]] * half[cy[j, 32 * b + t]] for t in range(32))
+                tot += s * (Fraction(2) ** e) / 4     # each element is (half-units)/2
+            assert Fraction(got[i, j]) == tot
+
+
+def test_topk_brute_force_and_ties():
+    g = np.random.default_rng(8)
+    for trial in range(50):
+        n = int(g.integers(1, 300))
+        k = int(g.integers(1, 80))
+        s = np.round(g.standard_normal(n + 5) * 4) / 4          # many exact ties
+        if trial % 7 == 0:
+            s[:n // 2] = 0.0
+            s[1] = -0.0
+        sel = I.topk_select(s, n, k)
+        order = sorted(range(n), key=lambda e: (-float(np.float32(s[e])), e))[:min(k, n)]
+        ref = np.full(k, -1, np.int32)
+        ref[:len(order)] = sorted(order)
+        assert np.array_equal(sel, ref)
+
+
+def test_topk_nan_ranks_last():
+    s = np.array([1.0, np.nan, 0.5, -np.inf, 2.0])
+    assert list(I.topk_select(s, 5, 4)) == [0, 2, 3, 4]
+
+
+# ------------------------------------------------------------- attention ----
+
+def _sdpa(q, K, V, scale, mask=None):
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        attn_mask=None if mask is None else torch.from_numpy(mask)[None], scale=scale)
+    return out[0].numpy()
+
+
+def _raw_case(seed, T, D=128, H=4):
+    g = np.random.default_rng(seed)
+    k = (g.standard_normal((1, T, D)) / 8).astype(np.float32)
+    v = g.standard_normal((1, T, D)).astype(np.float32)
+    q = (g.standard_normal((H, D)) / 8).astype(np.float32)
+    return k, v, q
+
+
+@pytest.mark.parametrize('T,t', [(40, 39), (40, 17), (9, 0)])
+def test_m1_all_selected_no_window_is_dense_causal(T, t):
+    k, v, q = _raw_case(T + t, T)
+    caches = M.build_caches(k, v, np.zeros((1, T), np.float32), np.zeros(1, np.float32), 'f32')
+    o, lse = A.attend_query(q, t, np.arange(t + 1), caches['dk'][0], caches['dv'][0],
+                            caches['dwk'][0], caches['dwv'][0], W=0)
+    qr = R.apply(q.astype(np.float64), np.int64(t))
+    kr = R.apply(k[0].astype(np.float64), np.arange(T))[:t + 1]
+    ref = _sdpa(qr, kr, v[0, :t + 1].astype(np.float64), 1 / math.sqrt(128))
+    assert np.allclose(o, ref, rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize('W', [1, 5, 128])
+def test_m1_all_selected_with_window_duplicates_keys(W):
+    T, t = 60, 50
+    k, v, q = _raw_case(W, T)
+    caches = M.build_caches(k, v, np.zeros((1, T), np.float32), np.zeros(1, np.float32), 'f32')
+    o, _ = A.attend_query(q, t, np.arange(t + 1), caches['dk'][0], caches['dv'][0],
+                          caches['dwk'][0], caches['dwv'][0], W=W)
+    qr = R.apply(q.astype(np.float64), np.int64(t))
+    kr = R.apply(k[0].astype(np.float64), np.arange(T))[:t + 1]
+    mask = np.zeros((q.shape[0], t + 1))
+    mask[:, max(0, t - W + 1):] = math.log(2.0)   # a key present twice weighs twice
+    ref = _sdpa(qr, kr, v[0, :t + 1].astype(np.float64), 1 / math.sqrt(128), mask)
+    assert np.allclose(o, ref, rtol=1e-6, atol=1e-6)
+
+
+def test_window_only_is_sliding_window_attention():
+    T, t, W = 300, 250, 128
+    k, v, q = _raw_case(11, T)
+    caches = M.build_caches(k, v, g := np.random.default_rng(1).standard_normal((1, T)).astype(np.float32),
+                            np.zeros(4, np.float32), 'f32')
+    o, _ = M.window_query(q, t, caches['dwk'][0], caches['dwv'][0], W)
+    o2, _ = M.hca_query(q, t, caches['dk'][0], caches['dv'][0], caches['dwk'][0], caches['dwv'][0], 4, W,
+                        n_entries=0)
+    qr = R.apply(q.astype(np.float64), np.int64(t))
+    kr = R.apply(k[0].astype(np.float64), np.arange(T))[t - W + 1:t + 1]
+    ref = _sdpa(qr, kr, v[0, t - W + 1:t + 1].astype(np.float64), 1 / math.sqrt(128))
+    assert np.allclose(o, ref, rtol=1e-6, atol=1e-6) and np.array_equal(o, o2)
+    # before the first block completes a CSA/HCA layer is window-only as well
+    o3, _ = M.hca_query(q, 2, caches['dk'][0], caches['dv'][0], caches['dwk'][0], caches['dwv'][0], 4, W)
+    o4, _ = M.window_query(q, 2, caches['dwk'][0], caches['dwv'][0], W)
+    assert np.array_equal(o3, o4)
+
+
+def test_single_key_returns_its_value():
+    g = np.random.default_rng(12)
+    V = g.standard_normal((1, 192))
+    o, lse = A.attend(g.standard_normal((7, 192)), g.standard_normal((1, 192)), V, 0.1)
+    assert np.allclose(o, np.repeat(V, 7, 0), rtol=1e-15, atol=0)
+
+
+def test_csa_with_all_selected_equals_hca():
+    g = np.random.default_rng(13)
+    T, m, t = 256, 4, 255
+    k = g.standard_normal((1, T, 192)).astype(np.float32)
+    v = g.standard_normal((1, T, 192)).astype(np.float32)
+    u = g.standard_normal((1, T, 128)).astype(np.float32)
+    caches = M.build_caches(k, v, g.standard_normal((1, T)).astype(np.float32),
+                            (0.1 * g.standard_normal(m)).astype(np.float32), 'e4m3_bf16', raw_ik=u, ik_fmt='mxfp4')
+    q = g.standard_normal((8, 192)).astype(np.float32)
+    iq = F.mxfp4_dequantize(*F.mxfp4_quantize(g.standard_normal((4, 128)).astype(np.float32)))
+    w = g.uniform(0, 1, 4).astype(np.float32)
+    o1, l1, sel, _ = M.csa_query(q, t, iq, w, caches['dik'][0], caches['dk'][0], caches['dv'][0],
+                                 caches['dwk'][0], caches['dwv'][0], m, k=1000)
+    o2, l2 = M.hca_query(q, t, caches['dk'][0], caches['dv'][0], caches['dwk'][0], caches['dwv'][0], m)
+    assert list(sel[:64]) == list(range(64)) and np.all(sel[64:] == -1)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12) and np.allclose(l1, l2)
+
+
+def test_visibility_rule():
+    assert [I.n_visible(t, 4) for t in (0, 2, 3, 4, 7, 8)] == [0, 0, 1, 1, 2, 2]
+    assert I.n_visible(1048575, 128) == 8192 and I.n_visible(1048575, 4) == 262144
+    assert list(A.window_positions(5, 128)) == list(range(6))
+    assert list(A.window_positions(300, 128)) == list(range(173, 301))
+
+
+def test_page_constants_fixture():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, 'page_constants.txt')):
+        if line.strip() and not line.startswith('#'):
+            name, val = line.split()[:2]
+            vals[name] = int(val)
+    assert vals['csa_ratio'] == 4 and vals['hca_ratio'] == 128 and vals['window'] == M.WINDOW
+    assert vals['rope_dims'] == F.ROPE_DIM and vals['topk_pro'] == 1024 and vals['topk_flash'] == 512
