@@ -1,0 +1,127 @@
+// Device helpers shared by the v4attn kernels (gfx950, wave64).
+//
+// Number formats (the pages name FP8, BF16, FP4/MXFP4 for the caches and the
+// indexer; the encodings are the OCP ones):
+//  * E4M3: OCP OFP8 rev 1.0 E4M3; round to nearest even, finite overflow
+//    saturates to +-448, NaN -> 0x7F.
+//  * BF16: top half of a float32 after round to nearest even.
+//  * E2M1 + E8M0: OCP MX v1.0; shared exponent floor(log2 amax) - 2.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "v4attn_internal.hpp"
+
+namespace v4a {
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// ------------------------------------------------------------ reductions ----
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        T u = __shfl_xor(v, o, 64);
+        v = (u > v) ? u : v;
+    }
+    return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+// Max over a 32-lane half of the wave (lanes 0..31 and 32..63 reduce separately).
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) {
+        float u = __shfl_xor(v, o, 64);
+        v = (u > v || __builtin_isnan(u)) ? u : v;
+    }
+    return v;
+}
+// NaN-propagating max of magnitudes.
+__device__ __forceinline__ float amax_acc(float m, float x) {
+    float a = __builtin_fabsf(x);
+    return (a > m || __builtin_isnan(a)) ? a : m;
+}
+__device__ __forceinline__ float wave_amax(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        float u = __shfl_xor(v, o, 64);
+        v = (u > v || __builtin_isnan(u)) ? u : v;
+    }
+    return v;
+}
+
+// ------------------------------------------------------------------ BF16 ----
+__device__ __forceinline__ uint16_t bf16_encode(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_decode(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// ------------------------------------------------------------------ E4M3 ----
+__device__ __forceinline__ uint8_t e4m3_encode(float x) {
+    if (__builtin_isnan(x)) return 0x7F;
+    uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+    float a = __builtin_fabsf(x);
+    if (a >= 448.0f) return (uint8_t)(sign | 0x7Eu);
+    if (a < 0.015625f) {                        // subnormal range: quantum 2^-9
+        float n = __builtin_rintf(a * 512.0f);  // exact scaling, round half to even
+        return (uint8_t)(sign | (uint32_t)n);   // n == 8 is the smallest normal
+    }
+    int e = (int)((__float_as_uint(a) >> 23) & 0xFFu) - 127;  // floor(log2 a), a normal
+    float sc = __builtin_rintf(__builtin_ldexpf(a, 3 - e));   // 8 .. 16
+    uint32_t code = (uint32_t)((e + 7) << 3) + ((uint32_t)sc - 8u);
+    if (code > 0x7Eu) code = 0x7Eu;
+    return (uint8_t)(sign | code);
+}
+__device__ __forceinline__ float e4m3_decode(uint8_t c) {
+    uint32_t e = (c >> 3) & 0xFu, m = c & 7u;
+    float v;
+    if (e == 15u && m == 7u) v = __builtin_nanf("");
+    else if (e == 0u) v = (float)m * 0.001953125f;  // m/8 * 2^-6
+    else v = __builtin_ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+    return (c & 0x80u) ? -v : v;
+}
+
+// ------------------------------------------------------------- E2M1/MX ----
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+    uint32_t s = __builtin_signbit(v) ? 8u : 0u;
+    float a = __builtin_fabsf(v);
+    uint32_t code;
+    if (a < 2.0f) {
+        code = (uint32_t)__builtin_rintf(a * 2.0f);  // 0..4 (4 == 2.0)
+    } else if (a < 4.0f) {
+        code = (uint32_t)__builtin_rintf(a) + 2u;   // 4..6
+    } else {
+        float q = __builtin_rintf(a * 0.5f);         // 2..
+        code = q >= 3.0f ? 7u : 6u;                  // 4.0 -> 6, 6.0 (and above) -> 7
+    }
+    return s | code;
+}
+// Shared exponent of an MX block from its amax (finite); returns E.
+__device__ __forceinline__ int mx_exponent(float amax) {
+    uint32_t ex = (__float_as_uint(amax) >> 23) & 0xFFu;
+    if (ex == 0u) return -127;                       // zero or subnormal amax
+    int e = (int)ex - 127 - 2;
+    return e < -127 ? -127 : e;
+}
+
+// --------------------------------------------------- order-preserving key ----
+// Larger float -> larger key; -0 == +0; NaN -> 0 (below every number).
+__device__ __forceinline__ uint32_t score_key(float s) {
+    if (__builtin_isnan(s)) return 0u;
+    uint32_t u = __float_as_uint(s + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+}  // namespace v4a

@@ -1,0 +1,175 @@
+// csa_compress: softmax-gated pooling of m raw tokens into one cache entry.
+//
+// [chaosnode.de, "DeepSeek-V4: 1 Million Token Context endlich nutzbar",
+// section "Hybrid Attention: CSA und HCA"]: CSA compresses KV entries 4x along
+// the sequence by softmax-gated pooling with a learned positional bias; HCA
+// compresses 128x. [golem.de, "... Bei Deepseek V4 haben kleine Änderungen
+// große Wirkung", section "Komprimierte Erinnerung für längere Kontexte"]: the
+// last 64 values carry RoPE and stay BF16, the rest is FP8.
+//
+// One wave per (entry, batch element). The gate weights, the RoPE rotation
+// and the weighted sum are evaluated in float64 and the entry is rounded to
+// float32 before it is encoded, so every encoding decision (FP8 scale and
+// codes, BF16 rounding, MX exponent and E2M1 codes) is taken on a float32
+// value. Compression is a negligible share of decode time (one block per m
+// tokens), so the kernel favours exactness over speed.
+
+#include "common.hpp"
+
+namespace v4a {
+
+constexpr int MAX_M = 1024;
+
+template <int ACT>
+__device__ __forceinline__ double load_act(const void *base, int64_t i) {
+    if (ACT == 0) return (double)((const float *)base)[i];
+    return (double)bf16_decode(((const uint16_t *)base)[i]);
+}
+
+__device__ __forceinline__ int64_t kv_row(const KvView &s, int64_t e) { return s.ring > 0 ? e % s.ring : e; }
+
+// Encode one float32 row held across the wave (nope dims lane + 64*i, rope
+// pair `lane` for lanes < 32) into a KV store row.
+__device__ void store_kv_row(const KvView &s, int b, int64_t row, const float *nope, int n_nope_it,
+                             float rx, float ry) {
+    const int lane = lane_id();
+    const int Dn = s.dim - ROPE_DIM;
+    if (s.fmt == 0) {
+        float *dst = (float *)(s.f32 + b * s.f32_bs + row * s.f32_rs);
+        for (int i = 0; i < n_nope_it; ++i) dst[lane + 64 * i] = nope[i];
+        if (lane < ROPE_PAIRS) {
+            dst[Dn + 2 * lane] = rx;
+            dst[Dn + 2 * lane + 1] = ry;
+        }
+        return;
+    }
+    uint8_t *codes = (uint8_t *)(s.nope + b * s.nope_bs + row * s.nope_rs);
+    float *scales = (float *)(s.scale + b * s.scale_bs + row * s.scale_rs);
+    for (int g = 0; g < n_nope_it / 2; ++g) {  // groups of 128 dims = two lane iterations
+        float a = amax_acc(0.0f, nope[2 * g]);
+        a = amax_acc(a, nope[2 * g + 1]);
+        a = wave_amax(a);
+        float sc = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+        if (__builtin_isnan(a)) sc = a;
+        codes[128 * g + lane] = e4m3_encode(__fdiv_rn(nope[2 * g], sc));
+        codes[128 * g + 64 + lane] = e4m3_encode(__fdiv_rn(nope[2 * g + 1], sc));
+        if (lane == 0) scales[g] = sc;
+    }
+    if (lane < ROPE_PAIRS) {
+        uint32_t *r = (uint32_t *)(s.rope + b * s.rope_bs + row * s.rope_rs);
+        r[lane] = (uint32_t)bf16_encode(rx) | ((uint32_t)bf16_encode(ry) << 16);
+    }
+}
+
+template <int ACT>
+__global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
+    __shared__ double alpha[MAX_M];
+    const int lane = lane_id();
+    const int j = blockIdx.x;  // block within the chunk
+    const int b = blockIdx.y;
+    const int m = p.m;
+    const int64_t tok0 = (int64_t)j * m;                 // first raw token of the block (chunk-relative)
+    const int64_t entry = p.pos0 / m + j;
+
+    // alpha_r = softmax_r(gate + pos_bias), float64
+    double zmax = -__builtin_inf();
+    for (int r = lane; r < m; r += 64) {
+        double z = (double)p.gate[(int64_t)b * p.t_new + tok0 + r] + (double)p.pos_bias[r];
+        alpha[r] = z;
+        zmax = z > zmax ? z : zmax;
+    }
+    zmax = wave_max(zmax);
+    double zsum = 0.0;
+    for (int r = lane; r < m; r += 64) {
+        double e = exp(alpha[r] - zmax);
+        alpha[r] = e;
+        zsum += e;
+    }
+    zsum = wave_sum(zsum);
+    for (int r = lane; r < m; r += 64) alpha[r] = alpha[r] / zsum;
+    __syncthreads();
+
+    // A ring store keeps only the last `ring` entries written by one call.
+    const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
+    if (p.has_kv && kv_keep) {
+        const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
+        const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * D;
+        // values (never rotated) and keys (rotated at each token's position)
+        for (int which = 0; which < 2; ++which) {
+            const void *src = which == 0 ? p.raw_k : p.raw_v;
+            float nope[4];
+            for (int i = 0; i < nit; ++i) {
+                double acc = 0.0;
+                for (int r = 0; r < m; ++r) acc += alpha[r] * load_act<ACT>(src, rowbase + (int64_t)r * D + lane + 64 * i);
+                nope[i] = (float)acc;
+            }
+            float rx = 0.0f, ry = 0.0f;
+            if (lane < ROPE_PAIRS) {
+                double ax = 0.0, ay = 0.0;
+                const double f = p.inv_freq[lane];
+                for (int r = 0; r < m; ++r) {
+                    double x = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane);
+                    double y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
+                    if (which == 0) {
+                        double sn, cs;
+                        sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                        double xr = x * cs - y * sn;
+                        double yr = x * sn + y * cs;
+                        x = xr;
+                        y = yr;
+                    }
+                    ax += alpha[r] * x;
+                    ay += alpha[r] * y;
+                }
+                rx = (float)ax;
+                ry = (float)ay;
+            }
+            const KvView &dst = which == 0 ? p.k : p.v;
+            store_kv_row(dst, b, kv_row(dst, entry), nope, nit, rx, ry);
+        }
+    }
+
+    if (p.has_ik) {
+        const int dI = p.dI, nit = dI / 64 + (dI % 64 ? 1 : 0);
+        const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * dI;
+        const IkView &s = p.ik;
+        for (int i = 0; i < nit; ++i) {
+            const int d = lane + 64 * i;
+            const bool on = d < dI;
+            double acc = 0.0;
+            if (on)
+                for (int r = 0; r < m; ++r) acc += alpha[r] * load_act<ACT>(p.raw_ik, rowbase + (int64_t)r * dI + d);
+            float x = (float)acc;
+            if (s.fmt == 0) {
+                if (on) ((float *)(s.f32 + b * s.f32_bs + entry * s.f32_rs))[d] = x;
+                continue;
+            }
+            // MX block of 32 = one half of the wave
+            bool bad = !__builtin_isfinite(x) && on;
+            float a = on ? amax_acc(0.0f, x) : 0.0f;
+            a = half_max(a);
+            int nbad = __builtin_popcountll(__ballot(bad) & ((lane < 32) ? 0xFFFFFFFFull : 0xFFFFFFFF00000000ull));
+            uint32_t code = 0;
+            int E = 0;
+            if (nbad == 0) {
+                E = mx_exponent(a);
+                code = e2m1_encode(__builtin_ldexpf(x, -E));
+            }
+            uint32_t nb = __shfl_down(code, 1, 64);
+            if (on && (lane & 1) == 0)
+                ((uint8_t *)(s.e2m1 + b * s.e2m1_bs + entry * s.e2m1_rs))[d >> 1] = (uint8_t)(code | (nb << 4));
+            if (on && (lane & 31) == 0)
+                ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[d >> 5] = nbad ? 0xFF : (uint8_t)(E + 127);
+        }
+    }
+}
+
+hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
+    dim3 grid(p.t_new / p.m, p.B);
+    if (grid.x == 0 || grid.y == 0) return hipSuccess;
+    if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, grid, dim3(64), 0, s, p);
+    else hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace v4a

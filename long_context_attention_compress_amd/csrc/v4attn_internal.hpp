@@ -1,0 +1,91 @@
+// Internal plans passed from the C ABI layer (abi.cpp) to the kernel launchers.
+// Plain structs, copied by value into kernel arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace v4a {
+
+constexpr int ROPE_DIM = 64;
+constexpr int ROPE_PAIRS = 32;
+
+// Device view of a v4a_kv_store: byte pointers and byte strides.
+struct KvView {
+    int fmt;       // 0 f32, 1 e4m3+bf16
+    int dim;
+    int64_t rows;
+    int64_t ring;  // 0: linear
+    const char *f32;   int64_t f32_rs, f32_bs;
+    const char *nope;  int64_t nope_rs, nope_bs;
+    const char *rope;  int64_t rope_rs, rope_bs;
+    const char *scale; int64_t scale_rs, scale_bs;
+};
+
+struct IkView {
+    int fmt;       // 0 f32, 1 mxfp4
+    int dim;
+    int64_t rows;
+    const char *f32;  int64_t f32_rs, f32_bs;
+    const char *e2m1; int64_t e2m1_rs, e2m1_bs;
+    const char *e8m0; int64_t e8m0_rs, e8m0_bs;
+};
+
+struct CompressPlan {
+    int B, t_new, m, act;  // act: 0 f32, 1 bf16
+    int64_t pos0;
+    int D, dI;
+    int has_kv, has_ik;
+    const void *raw_k, *raw_v, *raw_ik;
+    const float *gate, *pos_bias;
+    KvView k, v;
+    IkView ik;
+    double inv_freq[ROPE_PAIRS];
+};
+
+struct IndexPlan {
+    int Q, Tq, H, dI, k, m;
+    int chunk;       // entries scored per workgroup
+    int n_chunks;    // workgroups per query
+    int s_local;     // candidates a chunk keeps at least (its local top-s)
+    int region_cap;  // candidate slots per chunk in the workspace
+    const int64_t *q_pos;
+    const void *iq;
+    const uint8_t *iq_scale;
+    const float *w;
+    IkView keys;
+    int32_t *out_idx;
+    float *out_score;
+    uint32_t *counters;  // [Q]
+    uint32_t *meta;      // [Q][n_chunks][2]: candidate count, lower key bound
+    uint32_t *reg_key;   // [Q][n_chunks][region_cap]
+    int32_t *reg_idx;    // [Q][n_chunks][region_cap]
+};
+
+struct AttnPlan {
+    int Q, Tq, H, D, W, m;
+    int sparse;        // 1: key list is idx[q][0..k); 0: entries 0..n_ent-1
+    int k;             // sparse list length
+    int64_t n_override;  // dense: cap on entries (< 0: none)
+    int has_ent;
+    int n_split;       // workgroups per query
+    int keys_per_split;
+    const int64_t *q_pos;
+    const void *q;
+    KvView ek, ev, wk, wv;
+    const int32_t *idx;
+    float sm_scale;
+    double inv_freq[ROPE_PAIRS];
+    void *o;
+    int o_bf16;      // output format: 1 bfloat16, 0 float32
+    float *lse;
+    float *part_o;   // [Q][n_split][H][D]
+    float *part_ml;  // [Q][n_split][H][2]
+};
+
+hipError_t launch_compress(const CompressPlan &p, hipStream_t s);
+hipError_t launch_index(const IndexPlan &p, hipStream_t s);
+hipError_t launch_attn(const AttnPlan &p, hipStream_t s);
+hipError_t launch_fill_zero(void *ptr, size_t bytes, hipStream_t s);
+
+}  // namespace v4a

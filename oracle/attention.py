@@ -47,15 +47,15 @@ def attend(q, K, V, sm_scale):
     return o, (mx + np.log(l))[:, 0]
 
 
-def gather_keys(t, entry_ids, ent_k, ent_v, win_k, win_v, W):
+def gather_keys(t, entry_ids, ent_k, ent_v, win_k, win_v, W, win_first=0):
     """Key list for a query at position t.
 
     entry_ids: ids into ent_k/ent_v (ids < 0 are padding and skipped);
-    win_k/win_v: indexable by absolute position (row p holds position p).
+    win_k/win_v: row i holds raw position win_first + i.
     """
     ids = np.asarray(entry_ids, np.int64)
     ids = ids[ids >= 0]
-    wp = window_positions(t, W)
+    wp = window_positions(t, W) - int(win_first)
     K = np.concatenate([np.asarray(ent_k)[ids].reshape(-1, ent_k.shape[-1]),
                         np.asarray(win_k)[wp].reshape(-1, win_k.shape[-1])], axis=0)
     V = np.concatenate([np.asarray(ent_v)[ids].reshape(-1, ent_v.shape[-1]),
@@ -63,11 +63,12 @@ def gather_keys(t, entry_ids, ent_k, ent_v, win_k, win_v, W):
     return K, V
 
 
-def attend_query(q_raw, t, entry_ids, ent_k, ent_v, win_k, win_v, W, base=10000.0, sm_scale=None):
+def attend_query(q_raw, t, entry_ids, ent_k, ent_v, win_k, win_v, W, base=10000.0, sm_scale=None,
+                 win_first=0):
     """One query token: q_raw [H, D] before RoPE, at position t."""
     q_raw = np.asarray(q_raw, np.float64)
     D = q_raw.shape[-1]
     sigma = 1.0 / np.sqrt(D) if not sm_scale else float(sm_scale)
     q = rope.apply(q_raw, np.int64(t), base)
-    K, V = gather_keys(t, entry_ids, ent_k, ent_v, win_k, win_v, W)
+    K, V = gather_keys(t, entry_ids, ent_k, ent_v, win_k, win_v, W, win_first)
     return attend(q, K, V, sigma)

@@ -23,8 +23,8 @@ The pages do not define the formats; the definitions are the OCP ones:
   0xFF and zero elements.
 
 The FP8 row scale is a reading (the configuration asks for "a per-128 scale"
-without a format): s = amax / 448 in float32 (amax == 0 gives s = 1), codes are
-E4M3(x / s) with IEEE float32 division.
+without a format): s = amax / 448 in float32 (amax == 0 gives s = 1, a NaN in
+the group gives s = NaN), codes are E4M3(x / s) with IEEE float32 division.
 
 Parity: every codec is pinned in the test suite against torch's float8_e4m3fn
 and bfloat16 conversions, brute-force nearest-value search, and the OCP
@@ -175,9 +175,11 @@ def mxfp4_dequantize(packed, scales):
 # ------------------------------------------------ FP8 + BF16 KV split -------
 
 def fp8_row_scale(amax):
+    """amax / 448 in float32; 1 for an all-zero group; NaN when the group holds a NaN."""
     amax = np.asarray(amax, np.float32)
     s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
-    return np.where(amax > 0, s, np.float32(1.0)).astype(np.float32)
+    s = np.where(amax > 0, s, np.float32(1.0))
+    return np.where(np.isnan(amax), np.float32(np.nan), s).astype(np.float32)
 
 
 def kv_quantize(x):

@@ -38,7 +38,8 @@ def index_scores(iq, w, keys):
     iq = np.asarray(iq, np.float64)
     keys = np.asarray(keys, np.float64)
     dots = keys @ iq.T                           # [N, H]
-    return np.maximum(dots, 0.0) @ np.asarray(w, np.float32).astype(np.float64)
+    # max(0, x) as IEEE maxNum: a NaN dot product counts as 0
+    return np.fmax(dots, 0.0) @ np.asarray(w, np.float32).astype(np.float64)
 
 
 def topk_select(scores, n_vis, k):

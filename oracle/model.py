@@ -25,7 +25,7 @@ WINDOW = 128      # [webconsulting] "Das Wichtigste": the last 128 tokens stay u
 
 
 def csa_query(q_raw, t, iq, w, ik, ent_k, ent_v, win_k, win_v, m, k, W=WINDOW,
-              base=10000.0, sm_scale=None):
+              base=10000.0, sm_scale=None, win_first=0):
     """CSA layer for one query. ik/ent_k/ent_v dequantized [rows, .]; win_* by position.
 
     Returns (o [H, D], lse [H], selected ids [k], scores of the visible entries).
@@ -33,23 +33,25 @@ def csa_query(q_raw, t, iq, w, ik, ent_k, ent_v, win_k, win_v, m, k, W=WINDOW,
     n_vis = I.n_visible(t, m, rows=ik.shape[0])
     scores = I.index_scores(iq, w, ik[:n_vis])
     sel = I.topk_select(scores, n_vis, k)
-    o, lse = A.attend_query(q_raw, t, sel, ent_k, ent_v, win_k, win_v, W, base, sm_scale)
+    o, lse = A.attend_query(q_raw, t, sel, ent_k, ent_v, win_k, win_v, W, base, sm_scale, win_first)
     return o, lse, sel, scores
 
 
 def hca_query(q_raw, t, ent_k, ent_v, win_k, win_v, m, W=WINDOW, base=10000.0,
-              sm_scale=None, n_entries=None):
+              sm_scale=None, n_entries=None, win_first=0):
     """HCA layer for one query (n_entries = 0 gives a window-only layer)."""
     n_vis = I.n_visible(t, m, rows=ent_k.shape[0])
     if n_entries is not None:
         n_vis = min(n_vis, int(n_entries))
-    return A.attend_query(q_raw, t, np.arange(n_vis), ent_k, ent_v, win_k, win_v, W, base, sm_scale)
+    return A.attend_query(q_raw, t, np.arange(n_vis), ent_k, ent_v, win_k, win_v, W, base, sm_scale,
+                          win_first)
 
 
-def window_query(q_raw, t, win_k, win_v, W=WINDOW, base=10000.0, sm_scale=None):
+def window_query(q_raw, t, win_k, win_v, W=WINDOW, base=10000.0, sm_scale=None, win_first=0):
     """Window-only layer (the first two layers of the stack)."""
     empty = np.zeros((0, win_k.shape[-1]))
-    return A.attend_query(q_raw, t, np.zeros(0, np.int64), empty, empty, win_k, win_v, W, base, sm_scale)
+    return A.attend_query(q_raw, t, np.zeros(0, np.int64), empty, empty, win_k, win_v, W, base, sm_scale,
+                          win_first)
 
 
 def build_caches(raw_k, raw_v, gate, pos_bias, kv_fmt, base=10000.0, raw_ik=None, ik_fmt=None):

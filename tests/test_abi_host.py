@@ -1,0 +1,163 @@
+"""Host-side checks of the C ABI library (no GPU needed).
+
+The library loads and exports every symbol include/v4attn.h declares, and
+every malformed call is rejected with its status code before anything is
+enqueued. Only invalid calls are made here: validation runs before any HIP
+call, so no device is touched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_attention_compress_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7f0000000000      # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    src = open(os.path.join(ROOT, 'include', 'v4attn.h')).read()
+    src = re.sub(r'/\*.*?\*/', '', src, flags=re.S)
+    return set(re.findall(r'\b([a-z_0-9]+)\s*\([^;{]*\)\s*;', src)) - {'if', 'sizeof'}
+
+
+def test_exports_every_declared_symbol():
+    lib = _abi.load()
+    names = _declared()
+    assert {'csa_compress', 'lightning_index_topk', 'sparse_window_attn', 'hca_attn'} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(_abi.EXPORTS) == names
+
+
+def test_strerror_and_version():
+    lib = _abi.load()
+    assert lib.v4a_strerror(0) == b'ok'
+    assert lib.v4a_strerror(-5).startswith(b'workspace')
+    assert b'gfx950' in lib.v4a_version()
+
+
+def _plane(ptr=FAKE, rs=256, bs=256 * 4096):
+    return _abi.Plane(ptr, rs, bs)
+
+
+def _kv(fmt=_abi.KV_E4M3_BF16, dim=192, rows=4096, ring=0):
+    s = _abi.KvStoreC()
+    s.fmt, s.dim, s.rows, s.ring = fmt, dim, rows, ring
+    if fmt == _abi.KV_F32:
+        s.f32 = _plane(rs=4 * dim)
+    else:
+        s.nope, s.rope, s.scale = _plane(rs=128), _plane(rs=128), _plane(rs=4)
+    return s
+
+
+def _ik(fmt=_abi.IK_MXFP4, dim=128, rows=4096):
+    s = _abi.IkStoreC()
+    s.fmt, s.dim, s.rows = fmt, dim, rows
+    s.e2m1, s.e8m0 = _plane(rs=64), _plane(rs=4)
+    return s
+
+
+def _status(fn, *args):
+    lib = _abi.load()
+    r = getattr(lib, fn)(*args)
+    return r, lib.v4a_last_error().decode()
+
+
+def test_compress_rejections():
+    k, v, ik = _kv(), _kv(), _ik()
+
+    def args(**kw):
+        a = _abi.CompressArgs()
+        a.B, a.t_new, a.pos0, a.m, a.act_fmt, a.rope_base = 2, 16, 0, 4, _abi.ACT_BF16, 1e4
+        a.raw_k = a.raw_v = a.gate = a.pos_bias = a.raw_ik = FAKE
+        a.k_out, a.v_out, a.ik_out = ctypes.pointer(k), ctypes.pointer(v), ctypes.pointer(ik)
+        for n, val in kw.items():
+            setattr(a, n, val)
+        return ctypes.byref(a)
+
+    cases = [
+        (dict(m=0), _abi.V4A_EINVAL), (dict(m=2000), _abi.V4A_EINVAL), (dict(pos0=2), _abi.V4A_EINVAL),
+        (dict(t_new=6), _abi.V4A_EINVAL), (dict(gate=None), _abi.V4A_ENULL), (dict(act_fmt=7), _abi.V4A_EFORMAT),
+        (dict(raw_ik=None), _abi.V4A_ENULL), (dict(pos0=4096 * 4), _abi.V4A_EINVAL), (dict(raw_k=FAKE + 1), _abi.V4A_EALIGN),
+        (dict(k_out=None, v_out=None, ik_out=None, raw_ik=None), _abi.V4A_EINVAL),
+    ]
+    for kw, want in cases:
+        r, msg = _status('csa_compress', args(**kw), None)
+        assert r == want, (kw, r, msg)
+    bad_dim = _kv(dim=128)
+    r, _ = _status('csa_compress', args(k_out=ctypes.pointer(bad_dim), v_out=ctypes.pointer(bad_dim)), None)
+    assert r == _abi.V4A_EFORMAT
+    bad_align = _kv()
+    bad_align.nope = _plane(ptr=FAKE + 8)
+    r, _ = _status('csa_compress', args(k_out=ctypes.pointer(bad_align)), None)
+    assert r == _abi.V4A_EALIGN
+
+
+def test_index_rejections():
+    keys = _ik()
+
+    def args(**kw):
+        a = _abi.IndexArgs()
+        a.B, a.Tq, a.H_I, a.k, a.m = 2, 1, 64, 512, 4
+        a.q_pos = a.iq = a.iq_scale = a.w = a.out_idx = FAKE
+        a.keys = ctypes.pointer(keys)
+        for n, val in kw.items():
+            setattr(a, n, val)
+        return a
+
+    lib = _abi.load()
+    assert lib.lightning_index_topk_workspace(ctypes.byref(args())) > 0
+    assert lib.lightning_index_topk_workspace(ctypes.byref(args(k=0))) == 0
+    cases = [(dict(k=0), _abi.V4A_EINVAL), (dict(k=5000), _abi.V4A_EINVAL), (dict(H_I=20), _abi.V4A_EFORMAT),
+             (dict(iq_scale=None), _abi.V4A_ENULL), (dict(q_pos=None), _abi.V4A_ENULL),
+             (dict(iq=FAKE + 4), _abi.V4A_EALIGN), (dict(m=0), _abi.V4A_EINVAL)]
+    for kw, want in cases:
+        r, msg = _status('lightning_index_topk', ctypes.byref(args(**kw)), FAKE, 1 << 30, None)
+        assert r == want, (kw, r, msg)
+    # missing / short workspace
+    r, _ = _status('lightning_index_topk', ctypes.byref(args()), None, 0, None)
+    assert r == _abi.V4A_EWORKSPACE
+    r, _ = _status('lightning_index_topk', ctypes.byref(args()), FAKE, 16, None)
+    assert r == _abi.V4A_EWORKSPACE
+    bad = _ik(dim=64)
+    r, _ = _status('lightning_index_topk', ctypes.byref(args(keys=ctypes.pointer(bad))), FAKE, 1 << 30, None)
+    assert r == _abi.V4A_EFORMAT
+
+
+def test_attention_rejections():
+    ek, ev, wk, wv = _kv(), _kv(), _kv(ring=128, rows=128), _kv(ring=128, rows=128)
+
+    def args(**kw):
+        a = _abi.AttnArgs()
+        a.B, a.Tq, a.H_q, a.dim = 4, 1, 64, 192
+        a.q_pos = a.q = a.o = FAKE
+        a.q_fmt = a.o_fmt = _abi.ACT_BF16
+        a.ent_k, a.ent_v, a.win_k, a.win_v = (ctypes.pointer(s) for s in (ek, ev, wk, wv))
+        a.m, a.W, a.sm_scale, a.rope_base = 4, 128, 0.0, 1e4
+        for n, val in kw.items():
+            setattr(a, n, val)
+        return ctypes.byref(a)
+
+    lib = _abi.load()
+    assert lib.hca_attn_workspace(args(), -1) > 0
+    f32 = _kv(fmt=_abi.KV_F32, dim=192)
+    cases = [(dict(H_q=24), _abi.V4A_EFORMAT), (dict(q_fmt=_abi.ACT_F32), _abi.V4A_EFORMAT),
+             (dict(W=-1), _abi.V4A_EINVAL), (dict(q=None), _abi.V4A_ENULL), (dict(o=FAKE + 2), _abi.V4A_EALIGN),
+             (dict(ent_v=None), _abi.V4A_ENULL), (dict(sm_scale=float('nan')), _abi.V4A_EINVAL),
+             (dict(ent_k=ctypes.pointer(f32)), _abi.V4A_EFORMAT), (dict(dim=128), _abi.V4A_EFORMAT)]
+    for kw, want in cases:
+        r, msg = _status('hca_attn', args(**kw), -1, FAKE, 1 << 30, None)
+        assert r == want, (kw, r, msg)
+    r, _ = _status('hca_attn', args(), -1, None, 0, None)
+    assert r == _abi.V4A_EWORKSPACE
+    r, _ = _status('sparse_window_attn', args(), None, 1024, FAKE, 1 << 30, None)
+    assert r == _abi.V4A_ENULL
+    r, _ = _status('sparse_window_attn', args(), FAKE, 0, FAKE, 1 << 30, None)
+    assert r == _abi.V4A_EINVAL
+    ring_ent = _kv(ring=64)
+    r, _ = _status('hca_attn', args(ent_k=ctypes.pointer(ring_ent)), -1, FAKE, 1 << 30, None)
+    assert r == _abi.V4A_EINVAL

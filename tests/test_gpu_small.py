@@ -1,0 +1,348 @@
+"""GPU parity at small sizes: every entry point against the oracle, through the C ABI.
+
+Shapes span several tiles/chunks with ragged tails; edge cases cover empty and
+short visibility, fewer visible entries than k, window shorter than W,
+window-only layers, clustered winners (the exact fallback of the top-k merge)
+and exact score ties.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_compress_amd as v4
+import synth
+from oracle import compress as OC
+from oracle import formats as F
+from oracle import indexer as OI
+from oracle import model as OM
+from tests.helpers import (TOL_BF16, TOL_F32, assert_close_rms, assert_codes_e4m3, assert_topk, bf16_dev, dev,
+                           host_ik, host_kv, ik_store, kv_store, ring_rows)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------- compress ----
+
+@pytest.mark.parametrize('m,pos0,T,ring', [(4, 256, 64, 0), (1, 8, 40, 64), (1, 8, 200, 64), (128, 0, 384, 0)])
+def test_compress_f32(m, pos0, T, ring):
+    print(f'compress f32 m={m} pos0={pos0} T={T} ring={ring}', flush=True)
+    raw = synth.raw_tokens(100 + m, 2, T, 128, m, 64, std=0.09, bf16=False)
+    rows = (pos0 + T) // m if ring == 0 else ring
+    ks = v4.KVStore.empty(2, rows, 128, v4.KV_F32, ring)
+    vs = v4.KVStore.empty(2, rows, 128, v4.KV_F32, ring)
+    iks = v4.IKStore.empty(2, (pos0 + T) // m, 64, v4.IK_F32)
+    v4.csa_compress(dev(raw['gate']), dev(raw['pos_bias']), pos0, dev(raw['raw_k']), dev(raw['raw_v']), ks, vs,
+                    dev(raw['raw_ik']), iks)
+    torch.cuda.synchronize()
+    k32, v32, u32 = OC.compress(raw['raw_k'], raw['raw_v'], raw['gate'], raw['pos_bias'], pos0, raw_ik=raw['raw_ik'])
+    e0, ne = pos0 // m, T // m
+    gk, gv, gu = host_kv(ks)['f32'], host_kv(vs)['f32'], host_ik(iks)['f32']
+    if ring:
+        keep = min(ne, ring)
+        k32 = ring_rows(k32[:, ne - keep:], e0 + ne - keep, ring)
+        v32 = ring_rows(v32[:, ne - keep:], e0 + ne - keep, ring)
+        filled = [(e0 + i) % ring for i in range(ne - keep, ne)]
+        assert_close_rms(gk[:, filled], k32[:, filled], 1e-6, 'k')
+        assert_close_rms(gv[:, filled], v32[:, filled], 1e-6, 'v')
+    else:
+        assert_close_rms(gk[:, e0:], k32, 1e-6, 'k')
+        assert_close_rms(gv[:, e0:], v32, 1e-6, 'v')
+        assert np.all(gk[:, :e0] == 0)
+    assert_close_rms(gu[:, e0:], u32, 1e-6, 'ik')
+
+
+@pytest.mark.parametrize('m,pos0,T', [(4, 1024, 256), (1, 4000, 128), (128, 131072, 512)])
+def test_compress_fp8_mxfp4(m, pos0, T):
+    print(f'compress fp8 m={m} pos0={pos0} T={T}', flush=True)
+    B = 2
+    raw = synth.raw_tokens(200 + m, B, T, 192, m, 128, bf16=True)
+    raw['raw_k'][0, 3, :] *= 30.0           # an outlier row: large scale
+    raw['raw_v'][1, 5, :128] = 0.0          # a row whose E4M3 group is all zero when m == 1
+    raw['raw_k'] = synth.to_bf16_values(raw['raw_k'])
+    ring = 128 if m == 1 else 0
+    rows = ring if ring else (pos0 + T) // m
+    ks = v4.KVStore.empty(B, rows, 192, v4.KV_E4M3_BF16, ring)
+    vs = v4.KVStore.empty(B, rows, 192, v4.KV_E4M3_BF16, ring)
+    iks = v4.IKStore.empty(B, (pos0 + T) // m, 128, v4.IK_MXFP4)
+    v4.csa_compress(dev(raw['gate']), dev(raw['pos_bias']), pos0, bf16_dev(raw['raw_k']), bf16_dev(raw['raw_v']),
+                    ks, vs, bf16_dev(raw['raw_ik']), iks)
+    torch.cuda.synchronize()
+    k32, v32, u32 = OC.compress(raw['raw_k'], raw['raw_v'], raw['gate'], raw['pos_bias'], pos0, raw_ik=raw['raw_ik'])
+    e0, ne = pos0 // m, T // m
+    for name, x32, st in (('k', k32, ks), ('v', v32, vs)):
+        g = host_kv(st)
+        if ring:
+            x32 = ring_rows(x32, e0, ring)
+            sl = slice(None)
+        else:
+            sl = slice(e0, e0 + ne)
+        codes, rope_bits, scale = F.kv_quantize(x32)
+        assert np.array_equal(g['scale'][:, sl], scale), f'{name}: scales differ'
+        assert np.array_equal(g['rope'][:, sl], rope_bits), f'{name}: bf16 RoPE dims differ'
+        q = (x32[..., :128] / scale).astype(np.float32)
+        assert_codes_e4m3(g['nope'][:, sl], codes, q, name)
+    packed, scales = F.mxfp4_quantize(u32)
+    gi = host_ik(iks)
+    assert np.array_equal(gi['e8m0'][:, e0:e0 + ne], scales)
+    assert np.array_equal(gi['e2m1'][:, e0:e0 + ne], packed)
+
+
+# ---------------------------------------------------------------- index ----
+
+def _index_case_mx(seed, B, rows, q_pos, k, m=4, cluster=None, ties=False):
+    H, dI = 64, 128
+    g = np.random.default_rng(seed)
+    keys = synth.normal(seed, 'ik', (B, rows, dI))
+    iq = synth.normal(seed, 'iq', (B, q_pos.shape[1], H, dI))
+    w = synth.uniform(seed, 'w', (B, q_pos.shape[1], H))
+    if cluster is not None:          # winners packed into one chunk: exercises the exact fallback
+        b, lo, n = cluster
+        d = (w[b, 0][:, None] * iq[b, 0]).sum(0)
+        keys[b, lo:lo + n] = 6.0 * np.sqrt(dI) * d / np.linalg.norm(d) + 0.05 * g.standard_normal((n, dI))
+    if ties:                         # many exact duplicates of a few keys
+        keys[:, 1::3] = keys[:, 0:1]
+    packed, sc = F.mxfp4_quantize(keys)
+    ip, isc = F.mxfp4_quantize(iq)
+    return dict(packed=packed, sc=sc, ip=ip, isc=isc, w=w, q_pos=q_pos, k=k, m=m,
+                dkeys=F.mxfp4_dequantize(packed, sc), diq=F.mxfp4_dequantize(ip, isc))
+
+
+def _run_index(c, fmt='mx'):
+    if fmt == 'mx':
+        store = v4.IKStore(v4.IK_MXFP4, 128, e2m1=dev(c['packed']), e8m0=dev(c['sc']))
+        iq, iqs = dev(c['ip']), dev(c['isc'])
+    else:
+        store = v4.IKStore(v4.IK_F32, c['keys'].shape[-1], f32=dev(c['keys']))
+        iq, iqs = dev(c['iq']), None
+    B, Tq = c['q_pos'].shape
+    score = torch.zeros(B, Tq, c['k'], dtype=torch.float32, device='cuda')
+    idx = v4.lightning_index_topk(dev(c['q_pos']), iq, dev(c['w']), store, c['k'], c['m'], iq_scale=iqs,
+                                  out_score=score)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), score.cpu().numpy()
+
+
+def _check_index(c, idx, score, dkeys, diq):
+    B, Tq = c['q_pos'].shape
+    rows = dkeys.shape[1]
+    for b in range(B):
+        for i in range(Tq):
+            t = int(c['q_pos'][b, i])
+            n_vis = OI.n_visible(t, c['m'], rows) if t >= 0 else 0
+            s = OI.index_scores(diq[b, i], c['w'][b, i], dkeys[b, :n_vis])
+            assert_topk(idx[b, i], s, n_vis, c['k'], f'b{b} i{i} t{t}')
+            kk = min(c['k'], n_vis)
+            sel = idx[b, i, :kk]
+            ref = s[sel].astype(np.float32)
+            assert np.allclose(score[b, i, :kk], ref, rtol=2e-6, atol=1e-30), f'scores b{b} i{i}'
+            assert np.all(score[b, i, kk:] == 0)
+
+
+def test_index_mxfp4_shapes_and_edges():
+    q_pos = np.array([[19999, 12345], [7, 3000], [2047, -1], [2, 1]], np.int64)
+    c = _index_case_mx(1, 4, 5000, q_pos, 512)
+    print('index mxfp4 edges', flush=True)
+    idx, score = _run_index(c)
+    _check_index(c, idx, score, c['dkeys'], c['diq'])
+
+
+def test_index_mxfp4_clustered_winners_and_ties():
+    q_pos = np.array([[40000 * 4 - 1], [20000]], np.int64)
+    c = _index_case_mx(2, 2, 40000, q_pos, 1024, cluster=(0, 3000, 1500), ties=True)
+    print('index mxfp4 clustered', flush=True)
+    idx, score = _run_index(c)
+    _check_index(c, idx, score, c['dkeys'], c['diq'])
+
+
+def test_index_mxfp4_repeat_is_bitwise_identical():
+    q_pos = np.array([[12000 * 4 - 1]], np.int64)
+    c = _index_case_mx(3, 1, 12000, q_pos, 256)
+    a = _run_index(c)
+    b = _run_index(c)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_index_f32_small():
+    seed, B, Tq, rows, H, dI = 4, 1, 16, 1024, 4, 64
+    keys = synth.normal(seed, 'k', (B, rows, dI), 0.125)
+    iq = synth.normal(seed, 'q', (B, Tq, H, dI), 0.125)
+    w = synth.uniform(seed, 'w', (B, Tq, H))
+    q_pos = np.arange(4096 - Tq, 4096, dtype=np.int64)[None]
+    q_pos[0, 0] = 9            # 2 visible entries
+    q_pos[0, 1] = 300          # 75 visible: more than k
+    c = dict(keys=keys, iq=iq, w=w, q_pos=q_pos, k=64, m=4)
+    idx, score = _run_index(c, 'f32')
+    _check_index(c, idx, score, keys.astype(np.float64), iq.astype(np.float64))
+
+
+# ------------------------------------------------------------ attention ----
+
+def _attn_case(seed, B, Tq, H, D, rows, q_pos, fmt, W=128, ring=0):
+    outl = 0.01 if fmt == 'fp8' else 0.0
+    std = 1.0 if fmt == 'fp8' else 0.09
+    ent_k = synth.normal(seed, 'ek', (B, rows, D), std, outl)
+    ent_v = synth.normal(seed, 'ev', (B, rows, D), std, outl)
+    # raw window rows: a linear store of every position up to the latest query
+    # (ring == 0), or a ring holding the last `ring` positions
+    tmax = int(q_pos.max())
+    first = max(0, tmax - ring + 1) if ring else 0
+    win_k = synth.normal(seed, 'wk', (B, tmax - first + 1, D), std, outl)
+    win_v = synth.normal(seed, 'wv', (B, tmax - first + 1, D), std, outl)
+    q = synth.normal(seed, 'q', (B, Tq, H, D), std, outl)
+    if fmt == 'fp8':
+        q = synth.to_bf16_values(q)
+    kvf = 'f32' if fmt == 'f32' else 'e4m3_bf16'
+    enc = {n: OC.encode_kv(x, kvf) for n, x in (('ek', ent_k), ('ev', ent_v), ('wk', win_k), ('wv', win_v))}
+    dec = {n: OC.decode_kv(e) for n, e in enc.items()}
+    ring_enc = {}
+    for n in ('wk', 'wv'):
+        ring_enc[n] = {pk: (ring_rows(pv, first, ring) if ring else pv) for pk, pv in enc[n].items()}
+    return dict(q=q, q_pos=q_pos, enc=enc, dec=dec, ring_enc=ring_enc, first=first, W=W, ring=ring, fmt=fmt,
+                H=H, D=D)
+
+
+def _stores(c):
+    return (kv_store(c['enc']['ek']), kv_store(c['enc']['ev']), kv_store(c['ring_enc']['wk'], c['ring']),
+            kv_store(c['ring_enc']['wv'], c['ring']))
+
+
+def _qdev(c):
+    return bf16_dev(c['q']) if c['fmt'] == 'fp8' else dev(c['q'])
+
+
+def _oracle_attn(c, b, i, ids):
+    t = int(c['q_pos'][b, i])
+    return OM.A.attend_query(c['q'][b, i], t, ids, c['dec']['ek'][b], c['dec']['ev'][b], c['dec']['wk'][b],
+                             c['dec']['wv'][b], c['W'], win_first=c['first'])
+
+
+@pytest.mark.parametrize('fmt', ['f32', 'fp8'])
+def test_attn_sparse(fmt):
+    B, Tq, rows, k = 2, 3, 1000, 192
+    H, D = (16, 128) if fmt == 'f32' else (64, 192)
+    q_pos = np.array([[3999, 3998, 3900], [3999, 3000, 3999]], np.int64)
+    c = _attn_case(10, B, Tq, H, D, rows, q_pos, fmt)
+    g = np.random.default_rng(11)
+    idx = np.full((B, Tq, k), -1, np.int32)
+    for b in range(B):
+        for i in range(Tq):
+            n = [k, 150, 37][i]
+            idx[b, i, :n] = np.sort(g.choice(rows, n, replace=False))
+    idx[1, 2, 5] = rows + 7           # out-of-range ids are skipped
+    ek, ev, wk, wv = _stores(c)
+    lse = torch.zeros(B, Tq, H, dtype=torch.float32, device='cuda')
+    print(f'attn sparse {fmt}', flush=True)
+    o = v4.sparse_window_attn(_qdev(c), dev(q_pos), ek, ev, 4, wk, wv, c['W'], dev(idx), lse=lse)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    tol = TOL_F32 if fmt == 'f32' else TOL_BF16
+    for b in range(B):
+        for i in range(Tq):
+            ids = idx[b, i]
+            ids = ids[(ids >= 0) & (ids < rows)]
+            ro, rl = _oracle_attn(c, b, i, ids)
+            assert_close_rms(o[b, i], ro, tol, f'o b{b} i{i}')
+            assert np.allclose(lse[b, i], rl, atol=1e-4 if fmt == 'f32' else 2e-2), f'lse b{b} i{i}'
+
+
+@pytest.mark.parametrize('fmt', ['f32', 'fp8'])
+@pytest.mark.parametrize('override', [-1, 0, 100])
+def test_attn_dense(fmt, override):
+    B, Tq, rows, m = 2, 2, 700, 4
+    H, D = (16, 128) if fmt == 'f32' else (64, 192)
+    q_pos = np.array([[2799, 60], [1234, 2799]], np.int64)    # 60: window shorter than W, 15 entries
+    c = _attn_case(12, B, Tq, H, D, rows, q_pos, fmt)
+    ek, ev, wk, wv = _stores(c)
+    print(f'attn dense {fmt} override={override}', flush=True)
+    o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'], n_entries_override=override)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    tol = TOL_F32 if fmt == 'f32' else TOL_BF16
+    for b in range(B):
+        for i in range(Tq):
+            t = int(q_pos[b, i])
+            n = min((t + 1) // m, rows)
+            if override >= 0:
+                n = min(n, override)
+            ro, _ = _oracle_attn(c, b, i, np.arange(n))
+            assert_close_rms(o[b, i], ro, tol, f'o b{b} i{i}')
+
+
+@pytest.mark.parametrize('t_last', [128, 1000])
+def test_attn_window_only_ring(t_last):
+    # one query per batch element at the ring's newest position, plus early positions
+    B, Tq, H, D = 1, 2, 64, 192
+    q_pos = np.array([[t_last - 1, t_last]], np.int64)
+    c = _attn_case(13, B, Tq, H, D, 8, q_pos, 'fp8', ring=129)
+    ek, ev, wk, wv = _stores(c)
+    o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, 4, wk, wv, 128, n_entries_override=0)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    for i in range(Tq):
+        ro, _ = _oracle_attn(c, 0, i, np.zeros(0, np.int64))
+        assert_close_rms(o[0, i], ro, TOL_BF16, f'o i{i}')
+
+
+def test_attn_window_only_first_positions():
+    B, Tq, H, D = 1, 4, 64, 192
+    q_pos = np.array([[0, 1, 127, 128]], np.int64)
+    c = _attn_case(14, B, Tq, H, D, 8, q_pos, 'fp8')
+    ek, ev, wk, wv = _stores(c)
+    o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, 4, wk, wv, 128, n_entries_override=0)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    for i in range(Tq):
+        ro, _ = _oracle_attn(c, 0, i, np.zeros(0, np.int64))
+        assert_close_rms(o[0, i], ro, TOL_BF16, f'o i{i}')
+
+
+# ---------------------------------------------------------- end to end ----
+
+def test_c0_fp32_layer_end_to_end():
+    """The fp32 CSA workload (4,096 tokens, decode of the last 16): compress, index, attend on the GPU."""
+    cfg, x = synth.c0(0)
+    T, D, m, k, W = cfg['T'], cfg['D'], cfg['m'], cfg['k'], cfg['W']
+    N = T // m
+    ks, vs = v4.KVStore.empty(1, N, D, v4.KV_F32), v4.KVStore.empty(1, N, D, v4.KV_F32)
+    iks = v4.IKStore.empty(1, N, cfg['d_I'], v4.IK_F32)
+    ring = 256    # holds the windows of all 16 queries (positions 3953 .. 4095)
+    wk, wv = v4.KVStore.empty(1, ring, D, v4.KV_F32, ring), v4.KVStore.empty(1, ring, D, v4.KV_F32, ring)
+    rk, rv, gate = dev(x['raw_k']), dev(x['raw_v']), dev(x['gate'])
+    v4.csa_compress(gate, dev(x['pos_bias']), 0, rk, rv, ks, vs, dev(x['raw_ik']), iks)
+    v4.csa_compress(gate, torch.zeros(1, device='cuda'), 0, rk, rv, wk, wv)
+    q_pos = dev(x['q_pos'])
+    idx = v4.lightning_index_topk(q_pos, dev(x['iq']), dev(x['w']), iks, k, m)
+    o = v4.sparse_window_attn(dev(x['q']), q_pos, ks, vs, m, wk, wv, W, idx)
+    torch.cuda.synchronize()
+    idx, o = idx.cpu().numpy(), o.cpu().numpy()
+    caches = OM.build_caches(x['raw_k'], x['raw_v'], x['gate'], x['pos_bias'], 'f32', raw_ik=x['raw_ik'], ik_fmt='f32')
+    for i in range(cfg['Tq']):
+        t = int(x['q_pos'][0, i])
+        ro, _, sel, scores = OM.csa_query(x['q'][0, i], t, x['iq'][0, i], x['w'][0, i], caches['dik'][0],
+                                          caches['dk'][0], caches['dv'][0], caches['dwk'][0], caches['dwv'][0], m, k, W)
+        assert_topk(idx[0, i], scores, OI.n_visible(t, m, N), k, f'q{i}')
+        if np.array_equal(np.sort(idx[0, i]), np.sort(sel)):
+            assert_close_rms(o[0, i], ro, TOL_F32, f'o q{i}')
+        else:   # a tie-band swap: check the GPU attention on the oracle's selection instead
+            o2 = v4.sparse_window_attn(dev(x['q'][:, i:i + 1]), q_pos[:, i:i + 1], ks, vs, m, wk, wv, W,
+                                       dev(sel[None, None]))
+            assert_close_rms(o2.cpu().numpy()[0, 0], ro, TOL_F32, f'o q{i} (oracle selection)')
+
+
+def test_attn_bf16_output():
+    """bfloat16 output: the kernel's error plus the output's own rounding (2^-8 relative)."""
+    B, Tq, rows, H, D = 1, 2, 600, 64, 192
+    q_pos = np.array([[2399, 1000]], np.int64)
+    c = _attn_case(15, B, Tq, H, D, rows, q_pos, 'fp8')
+    ek, ev, wk, wv = _stores(c)
+    o = torch.empty(B, Tq, H, D, dtype=torch.bfloat16, device='cuda')
+    v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, 4, wk, wv, c['W'], o=o)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    for i in range(Tq):
+        t = int(q_pos[0, i])
+        ro, _ = _oracle_attn(c, 0, i, np.arange(min((t + 1) // 4, rows)))
+        rms = np.sqrt(np.mean(ro ** 2))
+        assert np.all(np.abs(o[0, i] - ro) <= TOL_BF16 * rms + 2.0 ** -8 * np.abs(ro))
