@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Decode throughput of the hybrid compressed attention hot path at 1M-token context.
+
+One step is one decode token for a batch of 4 sequences through one CSA layer
+and one HCA layer, each at 1,048,576 tokens of context:
+
+  CSA (m = 4, 262,144 compressed entries, MXFP4 indexer 64 x 128, top-1024):
+      append the new raw token to the 128-token window (csa_compress, m = 1),
+      every 4th step compress the finished block of 4 (csa_compress, m = 4),
+      lightning_index_topk, sparse_window_attn;
+  HCA (m = 128, 8,192 compressed entries):
+      append to its window, every 128th step compress the finished block of
+      128, hca_attn over all entries plus the window.
+
+64 query heads share one KV head of dim 192 (128 E4M3 dims + 64 BF16 RoPE
+dims). Steps rotate through --layers distinct layer caches (default 16, about
+10 GB) so that the 256 MB last-level cache cannot serve repeats. All inputs are
+synthetic, seeded, resident in HBM before timing starts.
+
+The timed region is enqueued behind a spin kernel so that host-side launch
+cost never shows up as GPU idle time; HIP events bracket the region and, in a
+second instrumented pass, every launch of the indexer (the dominant kernel).
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+METRIC = 'decode query-tokens/s at 1M ctx (CSA top-1024 / HCA) + % of HBM peak'
+HBM_PEAK_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+B, T, D, H, HI, DI, K, W = 4, 1 << 20, 192, 64, 64, 128, 1024, 128
+M_CSA, M_HCA = 4, 128
+N_CSA, N_HCA = T // M_CSA, T // M_HCA
+ROW_KV = 128 + 128 + 4          # E4M3 codes + BF16 RoPE dims + float32 scale, per K or V row
+ROW_IK = DI // 2 + DI // 32     # MXFP4 key: 64 B of E2M1 + 4 E8M0 scales
+
+
+def index_bytes():
+    """Algorithmic HBM bytes of one lightning_index_topk launch (whole batch)."""
+    per_q = N_CSA * ROW_IK + HI * ROW_IK + HI * 4 + K * 4 + 8
+    return B * per_q
+
+
+Q_O = H * D * 2 + H * D * 4                           # bf16 query in, float32 output out
+APPEND = 2 * D * 2 + 2 * ROW_KV                       # one window append: raw K,V in, two rows out
+
+
+def csa_bytes():
+    """Algorithmic HBM bytes of the CSA layer of one step (whole batch, block compression amortised)."""
+    block = (M_CSA * (2 * D + DI) * 2 + 2 * ROW_KV + ROW_IK) / M_CSA
+    return index_bytes() + B * ((K + W) * 2 * ROW_KV + K * 4 + Q_O + APPEND + block)
+
+
+def hca_bytes():
+    block = (M_HCA * 2 * D * 2 + 2 * ROW_KV) / M_HCA
+    return B * ((N_HCA + W) * 2 * ROW_KV + Q_O + APPEND + block)
+
+
+def step_bytes():
+    """Algorithmic HBM bytes of one step (CSA layer + HCA layer, whole batch)."""
+    return csa_bytes() + hca_bytes()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ('index.hip', 'common.hpp'):
+        h.update(open(os.path.join(ROOT, 'long_context_attention_compress_amd', 'csrc', f), 'rb').read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per indexer launch from the committed rocprofv3 counter summary, when it
+    was taken on the current kernel source; otherwise None."""
+    p = os.path.join(ROOT, 'profiles', 'index_topk_c3_1m_traffic.json')
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except Exception:
+        return None
+    if d.get('source_hash') != source_hash():
+        return None
+    return d.get('bytes_per_launch')
+
+
+def build_layers(v4, synth, torch, L, seed):
+    """Caches of one CSA and one HCA layer, drawn on the GPU and encoded by the library's own
+    compression kernel, then replicated into L distinct copies."""
+    dev = 'cuda'
+    zero1 = torch.zeros(1, device=dev)
+    g1 = torch.zeros(1, T, device=dev)
+    # --- CSA layer: entry-level keys/values (m = 1 encodes each row as one entry)
+    ek, ev = v4.KVStore.empty(B, N_CSA, D), v4.KVStore.empty(B, N_CSA, D)
+    ik = v4.IKStore.empty(B, N_CSA, DI)
+    iq_f = synth.gpu_normal(seed, 'csa/iq', (B, 1, HI, DI), outlier_frac=0.01)
+    w = synth.gpu_uniform(seed, 'csa/w', (B, 1, HI))
+    ikf = synth.gpu_normal(seed, 'csa/ik', (B, N_CSA, DI))
+    synth.gpu_plant(seed, ikf, iq_f, w, n_plant=64)
+    gate_n = torch.zeros(1, N_CSA, device=dev)
+    for b in range(B):
+        kb = v4.KVStore(v4.KV_E4M3_BF16, D, 0, nope=ek.nope[b:b + 1], rope=ek.rope[b:b + 1], scale=ek.scale[b:b + 1])
+        vb = v4.KVStore(v4.KV_E4M3_BF16, D, 0, nope=ev.nope[b:b + 1], rope=ev.rope[b:b + 1], scale=ev.scale[b:b + 1])
+        ib = v4.IKStore(v4.IK_MXFP4, DI, e2m1=ik.e2m1[b:b + 1], e8m0=ik.e8m0[b:b + 1])
+        kf = synth.gpu_normal(seed, f'csa/ek/{b}', (1, N_CSA, D), dtype=torch.bfloat16)
+        vf = synth.gpu_normal(seed, f'csa/ev/{b}', (1, N_CSA, D), dtype=torch.bfloat16)
+        v4.csa_compress(gate_n, zero1, 0, kf, vf, kb, vb, ikf[b:b + 1].to(torch.bfloat16).contiguous(), ib)
+        del kf, vf
+    del ikf
+    # indexer query: MXFP4-encoded by the same kernel (one row per head)
+    iq_store = v4.IKStore.empty(1, B * HI, DI)
+    v4.csa_compress(torch.zeros(1, B * HI, device=dev), zero1, 0, raw_ik=iq_f.reshape(1, B * HI, DI), ik_out=iq_store)
+    iq = iq_store.e2m1.reshape(B, 1, HI, DI // 2)
+    iq_scale = iq_store.e8m0.reshape(B, 1, HI, DI // 32)
+    # --- HCA layer: raw tokens compressed 128x
+    hk, hv = v4.KVStore.empty(B, N_HCA, D), v4.KVStore.empty(B, N_HCA, D)
+    bias128 = synth.gpu_normal(seed, 'hca/pos_bias', (M_HCA,), 0.1)
+    raw_tail = []
+    for b in range(B):
+        kb = v4.KVStore(v4.KV_E4M3_BF16, D, 0, nope=hk.nope[b:b + 1], rope=hk.rope[b:b + 1], scale=hk.scale[b:b + 1])
+        vb = v4.KVStore(v4.KV_E4M3_BF16, D, 0, nope=hv.nope[b:b + 1], rope=hv.rope[b:b + 1], scale=hv.scale[b:b + 1])
+        kf = synth.gpu_normal(seed, f'hca/raw_k/{b}', (1, T, D), dtype=torch.bfloat16)
+        vf = synth.gpu_normal(seed, f'hca/raw_v/{b}', (1, T, D), dtype=torch.bfloat16)
+        gate = synth.gpu_normal(seed, f'hca/gate/{b}', (1, T))
+        v4.csa_compress(gate, bias128, 0, kf, vf, kb, vb)
+        raw_tail.append((kf[:, T - W:].clone(), vf[:, T - W:].clone()))
+        del kf, vf, gate
+    # --- windows (last 128 raw tokens, ring of 128)
+    def window(rk, rv):
+        wk, wv = v4.KVStore.empty(B, W, D, ring=W), v4.KVStore.empty(B, W, D, ring=W)
+        v4.csa_compress(torch.zeros(B, W, device=dev), zero1, T - W, rk, rv, wk, wv)
+        return wk, wv
+    cwk, cwv = window(synth.gpu_normal(seed, 'csa/wk', (B, W, D), dtype=torch.bfloat16),
+                      synth.gpu_normal(seed, 'csa/wv', (B, W, D), dtype=torch.bfloat16))
+    hwk, hwv = window(torch.cat([t[0] for t in raw_tail]), torch.cat([t[1] for t in raw_tail]))
+    torch.cuda.synchronize()
+
+    def clone_kv(s):
+        return v4.KVStore(s.fmt, s.dim, s.ring, nope=s.nope.clone(), rope=s.rope.clone(), scale=s.scale.clone())
+
+    layers = []
+    for l in range(L):
+        c = (lambda s: s) if l == 0 else clone_kv
+        layers.append(dict(
+            ik=ik if l == 0 else v4.IKStore(v4.IK_MXFP4, DI, e2m1=ik.e2m1.clone(), e8m0=ik.e8m0.clone()),
+            ek=c(ek), ev=c(ev), cwk=c(cwk), cwv=c(cwv), hk=c(hk), hv=c(hv), hwk=c(hwk), hwv=c(hwv)))
+    torch.cuda.synchronize()
+    inputs = dict(iq=iq, iq_scale=iq_scale, w=w,
+                  q_csa=synth.gpu_normal(seed, 'csa/q', (B, 1, H, D), outlier_frac=0.01, dtype=torch.bfloat16),
+                  q_hca=synth.gpu_normal(seed, 'hca/q', (B, 1, H, D), dtype=torch.bfloat16),
+                  bias4=synth.gpu_normal(seed, 'csa/pos_bias', (M_CSA,), 0.1), bias128=bias128)
+    return layers, inputs
+
+
+def prepare_calls(v4, synth, torch, layers, inputs, seed):
+    """Prepared launches of every step of every layer (argument structs built once)."""
+    dev = 'cuda'
+    pos = torch.full((B, 1), T - 1, dtype=torch.int64, device=dev)
+    zero1 = torch.zeros(1, device=dev)
+    new_k = synth.gpu_normal(seed, 'step/k', (B, 1, D), dtype=torch.bfloat16)
+    new_v = synth.gpu_normal(seed, 'step/v', (B, 1, D), dtype=torch.bfloat16)
+    blk_k4 = synth.gpu_normal(seed, 'step/k4', (B, M_CSA, D), dtype=torch.bfloat16)
+    blk_v4 = synth.gpu_normal(seed, 'step/v4', (B, M_CSA, D), dtype=torch.bfloat16)
+    blk_u4 = synth.gpu_normal(seed, 'step/u4', (B, M_CSA, DI), dtype=torch.bfloat16)
+    blk_k128 = synth.gpu_normal(seed, 'step/k128', (B, M_HCA, D), dtype=torch.bfloat16)
+    blk_v128 = synth.gpu_normal(seed, 'step/v128', (B, M_HCA, D), dtype=torch.bfloat16)
+    g1, g4, g128 = (synth.gpu_normal(seed, f'step/g{m}', (B, m)) for m in (1, M_CSA, M_HCA))
+    idx = torch.zeros(B, 1, K, dtype=torch.int32, device=dev)
+    o_csa = torch.zeros(B, 1, H, D, dtype=torch.float32, device=dev)
+    o_hca = torch.zeros(B, 1, H, D, dtype=torch.float32, device=dev)
+    ws_i, ws_s, ws_h = v4.Workspace(), v4.Workspace(), v4.Workspace()
+    calls = []
+    for Ld in layers:
+        calls.append(dict(
+            csa_append=v4.csa_compress(g1, zero1, T - 1, new_k, new_v, Ld['cwk'], Ld['cwv'], prepare=True),
+            csa_block=v4.csa_compress(g4, inputs['bias4'], T - M_CSA, blk_k4, blk_v4, Ld['ek'], Ld['ev'],
+                                      blk_u4, Ld['ik'], prepare=True),
+            index=v4.lightning_index_topk(pos, inputs['iq'], inputs['w'], Ld['ik'], K, M_CSA,
+                                          iq_scale=inputs['iq_scale'], out_idx=idx, workspace=ws_i, prepare=True),
+            sparse=v4.sparse_window_attn(inputs['q_csa'], pos, Ld['ek'], Ld['ev'], M_CSA, Ld['cwk'], Ld['cwv'], W,
+                                         idx, o=o_csa, workspace=ws_s, prepare=True),
+            hca_append=v4.csa_compress(g1, zero1, T - 1, new_k, new_v, Ld['hwk'], Ld['hwv'], prepare=True),
+            hca_block=v4.csa_compress(g128, inputs['bias128'], T - M_HCA, blk_k128, blk_v128, Ld['hk'], Ld['hv'],
+                                      prepare=True),
+            hca=v4.hca_attn(inputs['q_hca'], pos, Ld['hk'], Ld['hv'], M_HCA, Ld['hwk'], Ld['hwv'], W, o=o_hca,
+                            workspace=ws_h, prepare=True)))
+    return calls, dict(idx=idx, o_csa=o_csa, o_hca=o_hca)
+
+
+def run_step(calls, s, L, ev=None):
+    c = calls[s % L]
+    if ev is not None:
+        ev[0].record()
+    c['csa_append']()
+    if s % M_CSA == M_CSA - 1:
+        c['csa_block']()
+    if ev is not None:
+        ev[1].record()
+    c['index']()
+    if ev is not None:
+        ev[2].record()
+    c['sparse']()
+    if ev is not None:
+        ev[3].record()
+    c['hca_append']()
+    if s % M_HCA == M_HCA - 1:
+        c['hca_block']()
+    c['hca']()
+    if ev is not None:
+        ev[4].record()
+
+
+def sleep_cycles_per_ms(torch):
+    """Calibrate torch.cuda._sleep (a spin kernel) against HIP events."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    a.record()
+    torch.cuda._sleep(20_000_000)
+    b.record()
+    torch.cuda.synchronize()
+    return 20_000_000 / max(a.elapsed_time(b), 1e-3)
+
+
+def timed(torch, calls, L, first, steps, instrument, cyc_per_ms):
+    """Enqueue `steps` steps behind a spin kernel long enough to cover the host enqueue time."""
+    t0 = time.perf_counter()
+    for s in range(first, first + 4):
+        run_step(calls, s, L)
+    torch.cuda.synchronize()
+    per_step_host = (time.perf_counter() - t0) / 4
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)] if instrument else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    park_ms = max(20.0, 2.0 * per_step_host * steps * 1e3)
+    torch.cuda._sleep(int(park_ms * cyc_per_ms))
+    start.record()
+    for i in range(steps):
+        run_step(calls, first + 4 + i, L, evs[i] if instrument else None)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    out = dict(total_ms=total_ms, host_ms_per_step=per_step_host * 1e3)
+    if instrument:
+        seg = lambda a, b: [e[a].elapsed_time(e[b]) for e in evs]
+        out['csa_append_ms'] = seg(0, 1)
+        out['index_ms'] = seg(1, 2)
+        out['sparse_ms'] = seg(2, 3)
+        out['hca_ms'] = seg(3, 4)
+    return out
+
+
+def cpu_baseline(seed):
+    """The oracle on one query of the CSA layer and one of the HCA layer (same shapes)."""
+    import numpy as np
+    import synth
+    from oracle import formats as F
+    from oracle import model as OM
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get('num_threads', 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    x = synth.entry_decode(seed, 1, N_CSA, T - 1, D, H, HI, DI, W, 0.01, n_plant=64)
+    ik = F.mxfp4_dequantize(*F.mxfp4_quantize(x['ik'][0]))
+    ek = F.kv_dequantize(*F.kv_quantize(x['ent_k'][0]))
+    evv = F.kv_dequantize(*F.kv_quantize(x['ent_v'][0]))
+    wk = F.kv_dequantize(*F.kv_quantize(x['win_k'][0]))
+    wv = F.kv_dequantize(*F.kv_quantize(x['win_v'][0]))
+    iq = F.mxfp4_dequantize(*F.mxfp4_quantize(x['iq'][0, 0]))
+    hx = synth.entries(seed + 1, 1, N_HCA, D, 0, W)
+    hk = F.kv_dequantize(*F.kv_quantize(hx['ent_k'][0]))
+    hv = F.kv_dequantize(*F.kv_quantize(hx['ent_v'][0]))
+    hwk = F.kv_dequantize(*F.kv_quantize(hx['win_k'][0]))
+    hwv = F.kv_dequantize(*F.kv_quantize(hx['win_v'][0]))
+    t0 = time.perf_counter()
+    OM.csa_query(x['q'][0, 0], T - 1, iq, x['w'][0, 0], ik, ek, evv, wk, wv, M_CSA, K, W, win_first=T - W)
+    t1 = time.perf_counter()
+    OM.hca_query(x['q'][0, 0], T - 1, hk, hv, hwk, hwv, M_HCA, W, win_first=T - W)
+    t2 = time.perf_counter()
+    return {'value': round(1.0 / (t2 - t0), 4), 'unit': 'query-tokens/s', 'cores': int(threads), 'kind': 'oracle',
+            'sample': (f'one query token (batch element 0) through the CSA layer ({t1 - t0:.2f} s: score '
+                       f'{N_CSA} MXFP4 keys, top-{K}, attend {K}+{W} keys) and the HCA layer ({t2 - t1:.2f} s: '
+                       f'attend {N_HCA}+{W} keys); float64 numpy, decoding of the caches not timed')}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
+    ap.add_argument('--gpus', type=int, default=1)
+    ap.add_argument('--steps', type=int, default=64)
+    ap.add_argument('--warmup', type=int, default=16)
+    ap.add_argument('--layers', type=int, default=16)
+    ap.add_argument('--seed', type=int, default=7)
+    ap.add_argument('--no-cpu-baseline', action='store_true')
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print('bench.py measures one GPU: the hot path is data-parallel over sequences and needs no '
+              'inter-GPU exchange, so N GPUs each run this same single-GPU workload on their own batch. '
+              'Run it with --gpus 1.', file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import long_context_attention_compress_amd as v4
+    import synth
+    L = a.layers
+    print(f'[bench] building {L} layer caches (B={B}, context {T})', file=sys.stderr, flush=True)
+    layers, inputs = build_layers(v4, synth, torch, L, a.seed)
+    calls, outs = prepare_calls(v4, synth, torch, layers, inputs, a.seed)
+    print('[bench] warmup', file=sys.stderr, flush=True)
+    for s in range(a.warmup):
+        run_step(calls, s, L)
+    torch.cuda.synchronize()
+    print('[bench] timed', file=sys.stderr, flush=True)
+    cyc = sleep_cycles_per_ms(torch)
+    clean = timed(torch, calls, L, a.warmup, a.steps, False, cyc)
+    inst = timed(torch, calls, L, a.warmup + a.steps + 4, a.steps, True, cyc)
+    ms = clean['total_ms'] / a.steps
+    value = B / (ms * 1e-3)
+    idx_ms = sum(inst['index_ms']) / len(inst['index_ms'])
+    achieved = index_bytes() / (idx_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile()
+    csa_ms = (sum(inst['csa_append_ms']) + sum(inst['index_ms']) + sum(inst['sparse_ms'])) / a.steps
+    hca_ms = sum(inst['hca_ms']) / a.steps
+    rec = {
+        'metric': METRIC, 'value': round(value, 1), 'unit': 'query-tokens/s', 'n_gpus': 1,
+        'steps': a.steps, 'warmup': a.warmup, 'ms_per_step': round(ms, 6), 'higher_is_better': True,
+        'scaling': 'weak', 'vs_baseline': None, 'dtype': 'mxfp4+e4m3/bf16', 'data': 'synthetic',
+        'config': {'workload': 'decode at 1,048,576-token context, batch 4: one CSA layer (m=4, 262,144 entries, '
+                               'MXFP4 indexer 64x128, top-1024, window 128) + one HCA layer (m=128, 8,192 entries, '
+                               'window 128) per step; 64 query heads, KV dim 192 (E4M3 + BF16 RoPE)',
+                   'batch': B, 'context': T, 'layers_rotated': L, 'parallelism': 'single GPU'},
+        'hbm_frac_step': round(step_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        'roofline': {'bound': 'hbm', 'kernel': 'lightning_index_topk', 'achieved': round(achieved, 1),
+                     'peak': HBM_PEAK_GBS, 'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
+                     'traffic': traffic},
+        'breakdown_us': {'csa_layer': round(csa_ms * 1e3, 2), 'index': round(idx_ms * 1e3, 2),
+                         'sparse_attn': round(sum(inst['sparse_ms']) / a.steps * 1e3, 2),
+                         'hca_layer': round(hca_ms * 1e3, 2)},
+        'csa_qtok_s': round(B / (csa_ms * 1e-3), 1), 'hca_qtok_s': round(B / (hca_ms * 1e-3), 1),
+        'csa_hbm_frac': round(csa_bytes() / (csa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        'hca_hbm_frac': round(hca_bytes() / (hca_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        'host_us_per_step': round(clean['host_ms_per_step'] * 1e3, 1),
+    }
+    if not a.no_cpu_baseline:
+        print('[bench] cpu baseline (oracle)', file=sys.stderr, flush=True)
+        rec['cpu_baseline'] = cpu_baseline(a.seed)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == '__main__':
+    main()

@@ -18,7 +18,7 @@ import torch
 from . import _abi
 from ._abi import (ACT_BF16, ACT_F32, IK_F32, IK_MXFP4, KV_E4M3_BF16, KV_F32)
 
-__all__ = ['KVStore', 'IKStore', 'Workspace', 'V4AError', 'csa_compress', 'lightning_index_topk',
+__all__ = ['KVStore', 'IKStore', 'Workspace', 'V4AError', 'Call', 'csa_compress', 'lightning_index_topk',
            'sparse_window_attn', 'hca_attn', 'lib', 'ROPE_DIM']
 
 ROPE_DIM = 64
@@ -158,9 +158,32 @@ def _need(t, name, dtype=None):
     return t
 
 
+class Call:
+    """A prepared launch: the argument structs are built once; calling it only enqueues.
+
+    It keeps references to every tensor, store and workspace buffer it points at.
+    """
+
+    def __init__(self, fn, args, keep):
+        self.fn, self.args, self.keep = fn, args, keep
+
+    def __call__(self):
+        _check(self.fn(*self.args))
+
+
+def _finish(fn, args, keep, prepare):
+    call = Call(fn, args, keep)
+    if prepare:
+        return call
+    call()
+    return None
+
+
 def csa_compress(gate, pos_bias, pos0, raw_k=None, raw_v=None, k_out=None, v_out=None,
-                 raw_ik=None, ik_out=None, rope_base=10000.0, stream=None):
-    """Pool blocks of m = len(pos_bias) raw tokens into entries pos0/m ... of the stores."""
+                 raw_ik=None, ik_out=None, rope_base=10000.0, stream=None, prepare=False):
+    """Pool blocks of m = len(pos_bias) raw tokens into entries pos0/m ... of the stores.
+
+    With prepare=True nothing is launched; a Call that enqueues this operation is returned."""
     _need(gate, 'gate', torch.float32)
     _need(pos_bias, 'pos_bias', torch.float32)
     ref = raw_k if raw_k is not None else raw_ik
@@ -179,11 +202,12 @@ def csa_compress(gate, pos_bias, pos0, raw_k=None, raw_v=None, k_out=None, v_out
         a.raw_ik = _ptr(raw_ik)
         a.ik_out = ik_out.c()
     a.gate, a.pos_bias = _ptr(gate), _ptr(pos_bias)
-    _check(lib().csa_compress(ctypes.byref(a), _stream(stream)))
+    keep = (a, gate, pos_bias, raw_k, raw_v, k_out, v_out, raw_ik, ik_out)
+    return _finish(lib().csa_compress, (ctypes.byref(a), _stream(stream)), keep, prepare)
 
 
 def lightning_index_topk(q_pos, iq, w, keys, k, m, iq_scale=None, out_idx=None, out_score=None,
-                         workspace=None, stream=None):
+                         workspace=None, stream=None, prepare=False):
     """Top-k entry ids per query: q_pos [B, Tq] int64; iq [B, Tq, H_I, dim/2] uint8 (MXFP4)
     with iq_scale [B, Tq, H_I, dim/32] uint8, or [B, Tq, H_I, dim] float32; w [B, Tq, H_I]."""
     _need(q_pos, 'q_pos', torch.int64)
@@ -201,9 +225,11 @@ def lightning_index_topk(q_pos, iq, w, keys, k, m, iq_scale=None, out_idx=None, 
     a.out_score = _ptr(out_score) if out_score is not None else None
     L = lib()
     nbytes = L.lightning_index_topk_workspace(ctypes.byref(a))
-    ptr, size = _workspace(workspace, w, 'index').get(nbytes, stream)
-    _check(L.lightning_index_topk(ctypes.byref(a), ptr, size, _stream(stream)))
-    return out_idx
+    ws = _workspace(workspace, w, 'index')
+    ptr, size = ws.get(nbytes, stream)
+    keep = (a, q_pos, iq, iq_scale, w, keys, out_idx, out_score, ws.buf)
+    call = _finish(L.lightning_index_topk, (ctypes.byref(a), ptr, size, _stream(stream)), keep, prepare)
+    return call if prepare else out_idx
 
 
 def _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse):
@@ -226,24 +252,28 @@ def _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, 
 
 
 def sparse_window_attn(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, idx, sm_scale=0.0,
-                       rope_base=10000.0, o=None, lse=None, workspace=None, stream=None):
+                       rope_base=10000.0, o=None, lse=None, workspace=None, stream=None, prepare=False):
     """CSA attention over the entries idx [B, Tq, k] (int32, -1 padded) plus the window."""
     a, o = _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse)
     _need(idx, 'idx', torch.int32)
     k = idx.shape[-1]
     L = lib()
     nbytes = L.sparse_window_attn_workspace(ctypes.byref(a), k)
-    ptr, size = _workspace(workspace, q, 'attn').get(nbytes, stream)
-    _check(L.sparse_window_attn(ctypes.byref(a), _ptr(idx), k, ptr, size, _stream(stream)))
-    return o
+    ws = _workspace(workspace, q, 'attn')
+    ptr, size = ws.get(nbytes, stream)
+    keep = (a, q, q_pos, ent_k, ent_v, win_k, win_v, idx, o, lse, ws.buf)
+    call = _finish(L.sparse_window_attn, (ctypes.byref(a), _ptr(idx), k, ptr, size, _stream(stream)), keep, prepare)
+    return call if prepare else o
 
 
 def hca_attn(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, n_entries_override=-1, sm_scale=0.0,
-             rope_base=10000.0, o=None, lse=None, workspace=None, stream=None):
+             rope_base=10000.0, o=None, lse=None, workspace=None, stream=None, prepare=False):
     """HCA attention over every visible entry plus the window (n_entries_override=0: window only)."""
     a, o = _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse)
     L = lib()
     nbytes = L.hca_attn_workspace(ctypes.byref(a), n_entries_override)
-    ptr, size = _workspace(workspace, q, 'attn').get(nbytes, stream)
-    _check(L.hca_attn(ctypes.byref(a), n_entries_override, ptr, size, _stream(stream)))
-    return o
+    ws = _workspace(workspace, q, 'attn')
+    ptr, size = ws.get(nbytes, stream)
+    keep = (a, q, q_pos, ent_k, ent_v, win_k, win_v, o, lse, ws.buf)
+    call = _finish(L.hca_attn, (ctypes.byref(a), n_entries_override, ptr, size, _stream(stream)), keep, prepare)
+    return call if prepare else o

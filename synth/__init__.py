@@ -200,3 +200,44 @@ def c4_queries(seed, layer, T0=None, T1=None):
                   prefix=f'c4q/{layer}/{T0}:{T1}')
     out['q_pos'] = (T0 + np.arange(T1, dtype=np.int64))[None, :]
     return out
+
+
+# ------------------------------------------------------- device-side draws ----
+# The same recipes drawn with torch's generator on the GPU, for workloads too
+# large to draw on the host quickly (the benchmark's caches). Still no method
+# arithmetic: random floats, outlier masks and bf16 rounding of inputs only.
+
+def _torch_gen(seed, name, device):
+    h = int.from_bytes(hashlib.sha256(name.encode()).digest()[:4], 'little')
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) << 32) ^ h)
+    return g
+
+
+def gpu_normal(seed, name, shape, std=1.0, outlier_frac=0.0, outlier_mult=20.0, dtype=torch.float32,
+               device='cuda'):
+    g = _torch_gen(seed, name, device)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    if outlier_frac > 0:
+        mask = torch.rand(shape, generator=g, device=device) < outlier_frac
+        x[mask] *= outlier_mult
+    return x.to(dtype)
+
+
+def gpu_uniform(seed, name, shape, device='cuda'):
+    return torch.rand(shape, generator=_torch_gen(seed, name, device), device=device, dtype=torch.float32)
+
+
+def gpu_plant(seed, ik, iq, w, n_plant=64, c=8.0, noise=0.1):
+    """Device version of plant(): ik [B, N, d_I] float32 (modified), iq [B, 1, H, d_I], w [B, 1, H]."""
+    B, N, d_I = ik.shape
+    g = _torch_gen(seed, 'plant/ids', ik.device)
+    ids = torch.stack([torch.randperm(N, generator=g, device=ik.device)[:n_plant].sort().values for _ in range(B)])
+    for b in range(B):
+        d = (w[b, 0][:, None].double() * iq[b, 0].double()).sum(0)
+        d = d / d.norm()
+        nz = gpu_normal(seed, f'plant/noise/{b}', (n_plant, d_I), noise, device=ik.device)
+        ik[b, ids[b]] = (c * d_I ** 0.5 * d[None, :]).float() + nz
+    return ids
