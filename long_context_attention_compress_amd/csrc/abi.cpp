@@ -10,7 +10,7 @@
 #include <algorithm>
 #include <string>
 
-#include "../../include/v4attn.h"
+#include "v4attn.h"
 #include "v4attn_internal.hpp"
 
 using namespace v4a;
@@ -105,6 +105,8 @@ int check_ik(const v4a_ik_store *s, const char *name, IkView *v) {
     } else if (s->fmt == V4A_IK_MXFP4) {
         if (s->dim <= 0 || s->dim > 256 || s->dim % 32) return fail(V4A_EFORMAT, "%s: MXFP4 dim must be a multiple of 32, <= 256", name);
         if ((r = check_plane(s->e2m1, name, 16)) || (r = check_plane(s->e8m0, name, 1))) return r;
+        if (s->e2m1.row_stride >= (1 << 20) || s->e8m0.row_stride >= (1 << 20))
+            return fail(V4A_EINVAL, "%s: row strides must be below 1 MiB", name);
         v->e2m1 = (const char *)s->e2m1.ptr;
         v->e2m1_rs = s->e2m1.row_stride;
         v->e2m1_bs = s->e2m1.batch_stride;
@@ -134,7 +136,7 @@ IndexLayout index_layout(const v4a_index_args *a) {
     L.n_chunks = (int)((rows + L.chunk - 1) / L.chunk);
     L.s_local = 2 * ((a->k + L.n_chunks - 1) / L.n_chunks) + 8;
     L.region_cap = std::min(L.chunk, std::max(2 * L.s_local + 64, 128));
-    L.off_meta = align_up((size_t)Q * 4, 256);
+    L.off_meta = 0;
     L.off_key = align_up(L.off_meta + (size_t)Q * L.n_chunks * 8, 256);
     L.off_idx = align_up(L.off_key + (size_t)Q * L.n_chunks * L.region_cap * 4, 256);
     L.total = align_up(L.off_idx + (size_t)Q * L.n_chunks * L.region_cap * 4, 256);
@@ -384,7 +386,6 @@ int lightning_index_topk(const v4a_index_args *a, void *ws, size_t ws_bytes, v4a
     P.out_idx = a->out_idx;
     P.out_score = a->out_score;
     char *w = (char *)ws;
-    P.counters = (uint32_t *)w;
     P.meta = (uint32_t *)(w + L.off_meta);
     P.reg_key = (uint32_t *)(w + L.off_key);
     P.reg_idx = (int32_t *)(w + L.off_idx);

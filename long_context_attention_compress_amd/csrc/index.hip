@@ -9,7 +9,7 @@
 // compressed blocks per query, indexer in FP4. The score formula is a reading
 // (the pages give none): I_e = sum_h w_h * max(0, q_h . u_e).
 //
-// Structure (one launch):
+// Structure (two launches on the caller's stream):
 //  1. Workgroup (chunk, query) scores `chunk` consecutive entries. MXFP4 keys:
 //     V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the indexer heads as M (16 per
 //     tile), 16 keys as N and the whole 128-dim key as K; the E8M0 block
@@ -20,12 +20,12 @@
 //     histogram (top 16 bits of the order-preserving score key) finds a
 //     threshold; every entry at or above it is written, in index order, to the
 //     chunk's candidate region with the threshold as the region's lower bound.
-//  3. The last workgroup of a query to arrive (device-scope counter) merges:
-//     radix-selects the k-th key over the candidates, checks that no chunk
-//     could have withheld an entry at or above it (lower bound > k-th key), and
-//     writes the selection in ascending id order. If a chunk could have
-//     withheld one (clustered winners, huge ties, region overflow) the merge
-//     falls back to an exact radix select that rescores every visible entry.
+//  3. A merge kernel (one workgroup per query) radix-selects the k-th key over
+//     the candidates held in registers, checks that no chunk could have
+//     withheld an entry at or above it (lower bound > k-th key), and writes the
+//     selection in ascending id order. If a chunk could have withheld one
+//     (clustered winners, huge ties, region overflow) the merge falls back to
+//     an exact radix select that rescores every visible entry.
 
 #include "common.hpp"
 
@@ -50,15 +50,25 @@ __device__ __forceinline__ int64_t visible_entries(const IndexPlan &p, int q) {
     return n < p.keys.rows ? n : p.keys.rows;
 }
 
+// Inclusive prefix sum over a wave with DPP row shifts and row broadcasts
+// (VALU only; no LDS round trips).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+    // within each row of 16 lanes
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    // across rows: lane 15 of each row is broadcast into the following row(s)
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // Inclusive prefix sum over the workgroup in thread order; *total gets the sum.
 __device__ uint32_t block_scan(uint32_t v, IdxSmem &sm, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
+    (void)lane;
     __syncthreads();
     if (lane == 63) sm.scan[wave] = x;
     __syncthreads();
@@ -93,36 +103,47 @@ __device__ int find_bin(IdxSmem &sm, uint32_t need, uint32_t *above) {
 
 // ------------------------------------------------------------- scoring ----
 
+// max(0, x) as one VALU op (IEEE maxNum: a quiet-NaN x gives 0). The compiler's
+// fmaxf would first canonicalise x, doubling the epilogue's VALU work.
+__device__ __forceinline__ float relu1(float x) {
+    float r;
+    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+// Sum over the four 16-lane rows holding the same key column, on the VALU
+// (gfx950 lane-swap instructions instead of LDS-routed shuffles).
+__device__ __forceinline__ float sum_rows(float s) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 template <int NT>
-__device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const v8i &B, uint32_t sB,
+__device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const v4i &kv, uint32_t sB,
                                           const float (&wv)[4][4]) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
+    const v8i B = {kv[0], kv[1], kv[2], kv[3], 0, 0, 0, 0};
+    v4f acc[4];
+    acc[0] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, z, 4, 4, 0, sA, 0, sB);
+    if (NT > 1) acc[1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, z, 4, 4, 1, sA, 0, sB);
+    if (NT > 2) acc[2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, z, 4, 4, 2, sA, 0, sB);
+    if (NT > 3) acc[3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, z, 4, 4, 3, sA, 0, sB);
     float s = 0.f;
-    v4f acc;
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[0], B, z, 4, 4, 0, sA, 0, sB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) s += wv[0][j] * __builtin_fmaxf(acc[j], 0.f);
-    if (NT > 1) {
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[1], B, z, 4, 4, 1, sA, 0, sB);
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s += wv[1][j] * __builtin_fmaxf(acc[j], 0.f);
-    }
-    if (NT > 2) {
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[2], B, z, 4, 4, 2, sA, 0, sB);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s += wv[2][j] * __builtin_fmaxf(acc[j], 0.f);
-    }
-    if (NT > 3) {
-        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[3], B, z, 4, 4, 3, sA, 0, sB);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) s += wv[3][j] * __builtin_fmaxf(acc[j], 0.f);
-    }
+        for (int j = 0; j < 4; ++j) s = __builtin_fmaf(wv[i][j], relu1(acc[i][j]), s);
     return s;
 }
 
-constexpr int MX_BATCH = 8;  // key tiles whose loads are in flight together per wave
+constexpr int MX_BATCH = 4;  // key tiles per wave per batch; two batches are in flight
 
 // Scores of entries [c0, c0+cnt) -> skey[0..cnt) (order-preserving keys).
+// Wave w takes tiles w, w+4, w+8, ...; each lane loads one 16-byte quarter of
+// one key row per tile, addressed as a uniform base plus a 32-bit offset, and
+// the next batch's loads are issued before the current batch is consumed.
 template <int NT>
 __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int cnt, uint32_t *skey) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -146,32 +167,40 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
 #pragma unroll
         for (int j = 0; j < 4; ++j) wv[i][j] = (i < NT) ? w[16 * i + 4 * grp + j] : 0.f;
     }
-    const char *kc = p.keys.e2m1 + (int64_t)b * p.keys.e2m1_bs + 16 * grp;
-    const char *ks = p.keys.e8m0 + (int64_t)b * p.keys.e8m0_bs + grp;
-    const int64_t krs = p.keys.e2m1_rs, srs = p.keys.e8m0_rs;
+    const char *kbase = p.keys.e2m1 + (int64_t)b * p.keys.e2m1_bs + c0 * p.keys.e2m1_rs;
+    const char *sbase = p.keys.e8m0 + (int64_t)b * p.keys.e8m0_bs + c0 * p.keys.e8m0_rs;
+    const uint32_t krs = (uint32_t)p.keys.e2m1_rs, srs = (uint32_t)p.keys.e8m0_rs;
     const int ntiles = (cnt + 15) >> 4;
-    for (int t0 = wave; t0 < ntiles; t0 += 4 * MX_BATCH) {
-        v4i kv[MX_BATCH];
-        uint32_t sB[MX_BATCH];
+    constexpr int STRIDE = 4 * MX_BATCH;  // tiles per batch over the 4 waves
+    v4i ka[MX_BATCH], kb[MX_BATCH];
+    uint32_t sa[MX_BATCH], sb[MX_BATCH];
+    auto issue = [&](v4i (&kv)[MX_BATCH], uint32_t (&sv)[MX_BATCH], int t0) {
 #pragma unroll
         for (int u = 0; u < MX_BATCH; ++u) {
-            const int tile = t0 + 4 * u;
-            int r = tile * 16 + col;
-            r = r < cnt ? r : 0;  // tail lanes reload row c0 (always valid); masked below
-            kv[u] = __builtin_nontemporal_load((const v4i *)(kc + (c0 + r) * krs));
-            sB[u] = (uint8_t)__builtin_nontemporal_load((const char *)(ks + (c0 + r) * srs));
+            int r = (t0 + 4 * u) * 16 + col;
+            r = r < cnt ? r : cnt - 1;  // tail lanes reload the last valid row; masked below
+            kv[u] = __builtin_nontemporal_load((const v4i *)(kbase + (uint32_t)r * krs + 16 * grp));
+            sv[u] = (uint8_t)__builtin_nontemporal_load(sbase + (uint32_t)r * srs + grp);
         }
+    };
+    auto consume = [&](const v4i (&kv)[MX_BATCH], const uint32_t (&sv)[MX_BATCH], int t0) {
 #pragma unroll
         for (int u = 0; u < MX_BATCH; ++u) {
             const int tile = t0 + 4 * u;
             if (tile >= ntiles) break;
-            v8i B = {kv[u][0], kv[u][1], kv[u][2], kv[u][3], 0, 0, 0, 0};
-            float s = head_sum<NT>(A, sA, B, sB[u], wv);
-            s += __shfl_xor(s, 16, 64);
-            s += __shfl_xor(s, 32, 64);
+            const float s = sum_rows(head_sum<NT>(A, sA, kv[u], sv[u], wv));
             const int r = tile * 16 + col;
             if (grp == 0 && r < cnt) skey[r] = score_key(s);
         }
+    };
+    int t = wave;
+    issue(ka, sa, t);
+    for (; t < ntiles; t += 2 * STRIDE) {
+        if (t + STRIDE < ntiles) issue(kb, sb, t + STRIDE);
+        consume(ka, sa, t);
+        if (t + STRIDE >= ntiles) break;
+        if (t + 2 * STRIDE < ntiles) issue(ka, sa, t + 2 * STRIDE);
+        consume(kb, sb, t + STRIDE);
     }
 }
 
@@ -271,7 +300,7 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
 
 // ------------------------------------------------------------- merge ----
 
-constexpr int REG_CAND = 32;  // candidates a merge thread keeps in registers
+constexpr int REG_CAND = 32;  // candidates a merge thread holds in registers
 
 template <int MODE>
 __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, int kk, uint32_t *skey,
@@ -342,123 +371,12 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
     }
 }
 
-template <int MODE>
-__device__ void merge(const IndexPlan &p, int q, int b, int64_t nvis, uint32_t *skey, const float *sq,
-                      IdxSmem &sm) {
-    const int tid = threadIdx.x;
-    const int kk = (int)(nvis < p.k ? nvis : p.k);
-    int32_t *oidx = p.out_idx + (size_t)q * p.k;
-    float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
-    if (kk == 0) {
-        for (int i = tid; i < p.k; i += IT) {
-            oidx[i] = -1;
-            if (osc) osc[i] = 0.f;
-        }
-        return;
-    }
-    // thread t owns chunks [t*cpt, t*cpt + cpt) (in order)
-    const int cpt = (p.n_chunks + IT - 1) / IT;
-    const int cA = tid * cpt, cB = min(cA + cpt, p.n_chunks);
-    const uint32_t *meta = p.meta + (size_t)q * p.n_chunks * 2;
-    const uint32_t *rk = p.reg_key + (size_t)q * p.n_chunks * p.region_cap;
-    const int32_t *ri = p.reg_idx + (size_t)q * p.n_chunks * p.region_cap;
-    int bad = 0;
-    uint32_t mycnt = 0;
-    for (int c = cA; c < cB; ++c) {
-        uint32_t n = meta[2 * c];
-        if (n == 0xFFFFFFFFu) bad = 1;
-        else mycnt += n;
-    }
-    const bool in_regs = (cB - cA == 1) && mycnt <= REG_CAND;
-    uint32_t keys[REG_CAND];
-    if (in_regs) {
-#pragma unroll
-        for (int i = 0; i < REG_CAND; ++i) keys[i] = (i < (int)mycnt) ? rk[(size_t)cA * p.region_cap + i] : 0u;
-    }
-    if (__syncthreads_or(bad)) {
-        exact_fallback<MODE>(p, q, b, nvis, kk, skey, sq, sm);
-        return;
-    }
-    // radix select of the kk-th largest candidate key
-    uint32_t prefix = 0, mask = 0, need = (uint32_t)kk;
-    for (int d = 3; d >= 0; --d) {
-        for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
-        __syncthreads();
-        const int sh = 8 * d;
-        if (in_regs) {
-#pragma unroll
-            for (int i = 0; i < REG_CAND; ++i)
-                if (i < (int)mycnt && (keys[i] & mask) == prefix) atomicAdd(&sm.hist[(keys[i] >> sh) & 255u], 1u);
-        } else {
-            for (int c = cA; c < cB; ++c) {
-                const uint32_t n = meta[2 * c];
-                for (uint32_t i = 0; i < n; ++i) {
-                    const uint32_t kx = rk[(size_t)c * p.region_cap + i];
-                    if ((kx & mask) == prefix) atomicAdd(&sm.hist[(kx >> sh) & 255u], 1u);
-                }
-            }
-        }
-        __syncthreads();
-        uint32_t above;
-        const int bin = find_bin(sm, need, &above);
-        need -= above;
-        prefix |= (uint32_t)bin << sh;
-        mask |= 255u << sh;
-    }
-    const uint32_t kth = prefix;
-    // a chunk whose emitted lower bound lies above the k-th key may have withheld winners
-    int sat = 0;
-    for (int c = cA; c < cB; ++c) sat |= meta[2 * c + 1] > kth;
-    if (__syncthreads_or(sat)) {
-        exact_fallback<MODE>(p, q, b, nvis, kk, skey, sq, sm);
-        return;
-    }
-    // emit: keys > kth, and the first `need` keys == kth in id order
-    uint32_t nt = 0;
-    if (in_regs) {
-#pragma unroll
-        for (int i = 0; i < REG_CAND; ++i) nt += (i < (int)mycnt) && keys[i] == kth;
-    } else {
-        for (int c = cA; c < cB; ++c)
-            for (uint32_t i = 0; i < meta[2 * c]; ++i) nt += rk[(size_t)c * p.region_cap + i] == kth;
-    }
-    uint32_t tot;
-    uint32_t tb = block_scan(nt, sm, &tot) - nt;
-    uint32_t ns = 0;
-    {
-        uint32_t t2 = tb;
-        for (int c = cA; c < cB; ++c)
-            for (uint32_t i = 0; i < meta[2 * c]; ++i) {
-                const uint32_t kx = rk[(size_t)c * p.region_cap + i];
-                if (kx > kth) ++ns;
-                else if (kx == kth) ns += (t2++ < need);
-            }
-    }
-    uint32_t pos = block_scan(ns, sm, &tot) - ns;
-    for (int c = cA; c < cB; ++c)
-        for (uint32_t i = 0; i < meta[2 * c]; ++i) {
-            const uint32_t kx = rk[(size_t)c * p.region_cap + i];
-            bool take = kx > kth;
-            if (kx == kth) take = (tb++ < need);
-            if (take) {
-                oidx[pos] = ri[(size_t)c * p.region_cap + i];
-                if (osc) osc[pos] = key_score(kx);
-                ++pos;
-            }
-        }
-    for (int i = kk + tid; i < p.k; i += IT) {
-        oidx[i] = -1;
-        if (osc) osc[i] = 0.f;
-    }
-}
-
-// ------------------------------------------------------------- kernel ----
+// ------------------------------------------------------------ kernels ----
 
 template <int MODE>
-__global__ __launch_bounds__(IT) void index_topk_kernel(IndexPlan p) {
+__global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
     extern __shared__ uint32_t dyn[];
     __shared__ IdxSmem sm;
-    __shared__ int last;
     uint32_t *skey = dyn;                                 // [chunk]
     float *sq = (float *)(dyn + p.chunk);                 // f32 mode: query [H][dI]
     const int chunk = blockIdx.x, q = blockIdx.y;
@@ -473,49 +391,199 @@ __global__ __launch_bounds__(IT) void index_topk_kernel(IndexPlan p) {
     const int kk = (int)(nvis < p.k ? nvis : p.k);
     const int64_t c0 = (int64_t)chunk * p.chunk;
     const int cnt = (int)(nvis - c0 <= 0 ? 0 : (nvis - c0 < p.chunk ? nvis - c0 : p.chunk));
-    if (cnt > 0) {
-        score_chunk<MODE>(p, q, b, c0, cnt, skey, sq);
+    if (cnt == 0) {
+        if (tid == 0) {
+            uint32_t *meta = p.meta + ((size_t)q * p.n_chunks + chunk) * 2;
+            meta[0] = 0;
+            meta[1] = 0;
+        }
+        return;
+    }
+    score_chunk<MODE>(p, q, b, c0, cnt, skey, sq);
+    __syncthreads();
+    // every full chunk keeps enough that the union holds at least kk entries
+    const int64_t n_active = (nvis + p.chunk - 1) / p.chunk;
+    int s_want = p.s_local;
+    const int64_t div = n_active > 1 ? n_active - 1 : 1;
+    const int64_t spread = (kk + div - 1) / div;
+    if (spread > s_want) s_want = (int)spread;
+    if (s_want > cnt) s_want = cnt;
+    chunk_emit(p, q, chunk, c0, cnt, s_want, skey, sm);
+}
+
+// One workgroup per query. The chunks' candidates are taken in chunk order
+// (ascending entry ids) and split into equal contiguous runs, one per thread,
+// held in registers; a 4 x 8-bit radix select finds the k-th key.
+template <int MODE>
+__global__ __launch_bounds__(IT) void index_merge_kernel(IndexPlan p) {
+    extern __shared__ uint32_t dyn[];
+    __shared__ IdxSmem sm;
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int b = q / p.Tq;
+    uint32_t *pre = dyn;                                  // [n_chunks + 1] candidate offsets
+    uint32_t *skey = dyn + p.n_chunks + 1;                // [chunk] (exact fallback)
+    float *sq = (float *)(skey + p.chunk);                // f32 mode query
+    if (MODE == 0) {
+        const float *iq = (const float *)p.iq + (size_t)q * p.H * p.dI;
+        for (int i = tid; i < p.H * p.dI; i += IT) sq[i] = iq[i];
+    }
+    const int64_t nvis = visible_entries(p, q);
+    const int kk = (int)(nvis < p.k ? nvis : p.k);
+    int32_t *oidx = p.out_idx + (size_t)q * p.k;
+    float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
+    if (kk == 0) {
+        for (int i = tid; i < p.k; i += IT) {
+            oidx[i] = -1;
+            if (osc) osc[i] = 0.f;
+        }
+        return;
+    }
+    const uint32_t *meta = p.meta + (size_t)q * p.n_chunks * 2;
+    // exclusive prefix of candidate counts over chunks
+    int bad = 0;
+    uint32_t carry = 0;
+    for (int c0 = 0; c0 < p.n_chunks; c0 += IT) {
+        const int c = c0 + tid;
+        uint32_t n = c < p.n_chunks ? meta[2 * c] : 0u;
+        if (n == 0xFFFFFFFFu) {
+            bad = 1;
+            n = 0;
+        }
+        uint32_t tot;
+        const uint32_t inc = block_scan(n, sm, &tot);
+        if (c < p.n_chunks) pre[c] = carry + inc - n;
+        carry += tot;
         __syncthreads();
-        // every full chunk keeps enough that the union holds at least kk entries
-        const int64_t n_active = (nvis + p.chunk - 1) / p.chunk;
-        int s_want = p.s_local;
-        const int64_t spread = (kk + (n_active > 1 ? n_active - 1 : 1) - 1) / (n_active > 1 ? n_active - 1 : 1);
-        if (spread > s_want) s_want = (int)spread;
-        if (s_want > cnt) s_want = cnt;
-        chunk_emit(p, q, chunk, c0, cnt, s_want, skey, sm);
-    } else if (tid == 0) {
-        uint32_t *meta = p.meta + ((size_t)q * p.n_chunks + chunk) * 2;
-        meta[0] = 0;
-        meta[1] = 0;
     }
-    // arrive; the last workgroup of this query merges
-    __threadfence();
+    if (tid == 0) pre[p.n_chunks] = carry;
+    const uint32_t total = carry;
+    const uint32_t per = (total + IT - 1) / IT;
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(&p.counters[q], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        last = (prev == (uint32_t)p.n_chunks - 1);
+    if (__syncthreads_or(bad) || per > REG_CAND) {
+        exact_fallback<MODE>(p, q, b, nvis, kk, skey, sq, sm);
+        return;
     }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    merge<MODE>(p, q, b, nvis, skey, sq, sm);
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(&p.counters[q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t keys[REG_CAND];
+    int32_t ids[REG_CAND];
+    int mine;
+    if (p.n_chunks <= IT && __syncthreads_and(tid >= p.n_chunks || pre[tid + 1] - pre[tid] <= REG_CAND)) {
+        // one chunk per thread: its whole region, in order
+        mine = tid < p.n_chunks ? (int)(pre[tid + 1] - pre[tid]) : 0;
+        const size_t base = ((size_t)q * p.n_chunks + tid) * p.region_cap;
+#pragma unroll
+        for (int i = 0; i < REG_CAND; ++i) {
+            keys[i] = i < mine ? p.reg_key[base + i] : 0u;
+            ids[i] = i < mine ? p.reg_idx[base + i] : -1;
+        }
+    } else {
+        // equal contiguous runs [lo, hi) of the flattened candidate list
+        const uint32_t lo = min(total, tid * per), hi = min(total, lo + per);
+        int c = 0;
+        {
+            int l = 0, r = p.n_chunks;  // last chunk with pre[c] <= lo
+            while (r - l > 1) {
+                const int mid = (l + r) >> 1;
+                if (pre[mid] <= lo) l = mid;
+                else r = mid;
+            }
+            c = l;
+        }
+#pragma unroll
+        for (int i = 0; i < REG_CAND; ++i) {
+            keys[i] = 0u;
+            ids[i] = -1;
+            const uint32_t f = lo + i;
+            if (f < hi) {
+                while (pre[c + 1] <= f) ++c;
+                const size_t slot = ((size_t)q * p.n_chunks + c) * p.region_cap + (f - pre[c]);
+                keys[i] = p.reg_key[slot];
+                ids[i] = p.reg_idx[slot];
+            }
+        }
+        mine = (int)(hi - lo);
+    }
+    // radix select of the kk-th largest key
+    uint32_t prefix = 0, mask = 0, need = (uint32_t)kk;
+    for (int d = 3; d >= 0; --d) {
+        for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
+        __syncthreads();
+        const int sh = 8 * d;
+        // runs of equal bins are counted in a register first: the candidates
+        // cluster in few bins, and same-address LDS atomics serialise
+        uint32_t run_bin = 0xFFFFFFFFu, run = 0;
+#pragma unroll
+        for (int i = 0; i < REG_CAND; ++i) {
+            if (i < mine && (keys[i] & mask) == prefix) {
+                const uint32_t bin = (keys[i] >> sh) & 255u;
+                if (bin != run_bin) {
+                    if (run) atomicAdd(&sm.hist[run_bin], run);
+                    run_bin = bin;
+                    run = 0;
+                }
+                ++run;
+            }
+        }
+        if (run) atomicAdd(&sm.hist[run_bin], run);
+        __syncthreads();
+        uint32_t above;
+        const int bin = find_bin(sm, need, &above);
+        need -= above;
+        prefix |= (uint32_t)bin << sh;
+        mask |= 255u << sh;
+    }
+    const uint32_t kth = prefix;
+    // a chunk whose emitted lower bound lies above the k-th key may have withheld winners
+    int sat = 0;
+    for (int cc = tid; cc < p.n_chunks; cc += IT) sat |= meta[2 * cc + 1] > kth;
+    if (__syncthreads_or(sat)) {
+        exact_fallback<MODE>(p, q, b, nvis, kk, skey, sq, sm);
+        return;
+    }
+    // keys > kth, and the first `need` keys == kth in id order
+    uint32_t nt = 0, ngt = 0;
+#pragma unroll
+    for (int i = 0; i < REG_CAND; ++i) {
+        nt += (i < mine) && keys[i] == kth;
+        ngt += (i < mine) && keys[i] > kth;
+    }
+    uint32_t tot;
+    uint32_t tb = block_scan(nt, sm, &tot) - nt;
+    const uint32_t ntake = ngt + (tb < need ? min(nt, need - tb) : 0u);
+    uint32_t pos = block_scan(ntake, sm, &tot) - ntake;
+#pragma unroll
+    for (int i = 0; i < REG_CAND; ++i) {
+        if (i < mine) {
+            bool take = keys[i] > kth;
+            if (keys[i] == kth) take = (tb++ < need);
+            if (take) {
+                oidx[pos] = ids[i];
+                if (osc) osc[pos] = key_score(keys[i]);
+                ++pos;
+            }
+        }
+    }
+    for (int i = kk + tid; i < p.k; i += IT) {
+        oidx[i] = -1;
+        if (osc) osc[i] = 0.f;
+    }
+}
+
+template <int MODE>
+static void launch_mode(const IndexPlan &p, hipStream_t s) {
+    const size_t q_lds = MODE == 0 ? (size_t)p.H * p.dI * 4 : 0;
+    hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, p.Q), dim3(IT), (size_t)p.chunk * 4 + q_lds, s, p);
+    hipLaunchKernelGGL(index_merge_kernel<MODE>, dim3(p.Q), dim3(IT),
+                       (size_t)(p.n_chunks + 1 + p.chunk) * 4 + q_lds, s, p);
 }
 
 hipError_t launch_index(const IndexPlan &p, hipStream_t s) {
-    dim3 grid(p.n_chunks, p.Q);
-    size_t lds = (size_t)p.chunk * 4 + (p.keys.fmt == 0 ? (size_t)p.H * p.dI * 4 : 0);
-    if (p.keys.fmt == 0) {
-        hipLaunchKernelGGL(index_topk_kernel<0>, grid, dim3(IT), lds, s, p);
-    } else {
-        switch (p.H / 16) {
-            case 1: hipLaunchKernelGGL(index_topk_kernel<1>, grid, dim3(IT), lds, s, p); break;
-            case 2: hipLaunchKernelGGL(index_topk_kernel<2>, grid, dim3(IT), lds, s, p); break;
-            case 3: hipLaunchKernelGGL(index_topk_kernel<3>, grid, dim3(IT), lds, s, p); break;
-            default: hipLaunchKernelGGL(index_topk_kernel<4>, grid, dim3(IT), lds, s, p); break;
+    if (p.keys.fmt == 0) launch_mode<0>(p, s);
+    else switch (p.H / 16) {
+            case 1: launch_mode<1>(p, s); break;
+            case 2: launch_mode<2>(p, s); break;
+            case 3: launch_mode<3>(p, s); break;
+            default: launch_mode<4>(p, s); break;
         }
-    }
     return hipGetLastError();
 }
 

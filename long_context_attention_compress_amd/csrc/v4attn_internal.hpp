@@ -56,7 +56,6 @@ struct IndexPlan {
     IkView keys;
     int32_t *out_idx;
     float *out_score;
-    uint32_t *counters;  // [Q]
     uint32_t *meta;      // [Q][n_chunks][2]: candidate count, lower key bound
     uint32_t *reg_key;   // [Q][n_chunks][region_cap]
     int32_t *reg_idx;    // [Q][n_chunks][region_cap]

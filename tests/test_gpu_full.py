@@ -1,0 +1,239 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the benchmark times.
+
+Where the oracle cannot afford every output it checks a sample it computes one
+by one (named in each test); every top-k set it does compute is checked modulo
+the tie band, and attention outputs within tolerance. Inputs come from synth;
+the oracle encodes what it needs from the same floats with its own codecs.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_compress_amd as v4
+import synth
+from oracle import compress as OC
+from oracle import formats as F
+from oracle import indexer as OI
+from oracle import model as OM
+from tests.helpers import TOL_BF16, TOL_F32, assert_close_rms, assert_topk, bf16_dev, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_rows(x, pos):
+    """The oracle's own m = 1 encoding of rows x [n, D] at positions pos: (keys, values) dequantized.
+
+    Keys are rotated at their position, values are not."""
+    from oracle import rope
+    kr = rope.apply(x.astype(np.float64), np.asarray(pos)).astype(np.float32)
+    return F.kv_dequantize(*F.kv_quantize(kr)), F.kv_dequantize(*F.kv_quantize(x.astype(np.float32)))
+
+
+def _decode_check(x, cfg, k, idx, o, ik_deq, iq_deq, m, N, run_oracle_sel):
+    """Per batch element: top-k set modulo ties, and attention over the selection."""
+    B = x['q'].shape[0]
+    t = int(x['q_pos'][0, 0])
+    W = cfg['W']
+    swaps = 0
+    for b in range(B):
+        scores = OI.index_scores(iq_deq[b, 0], x['w'][b, 0], ik_deq[b])
+        swaps += assert_topk(idx[b, 0], scores, N, k, f'b{b}')
+        sel = OI.topk_select(scores, N, k)
+        if 'planted' in x:
+            assert set(x['planted'][b].tolist()) <= set(idx[b, 0].tolist()), 'a planted entry was missed'
+        # oracle keys/values of the selected entries (rotated at their row position) and of the window
+        ids = sel[sel >= 0]
+        ek, _ = _oracle_rows(x['ent_k'][b, ids], ids)
+        _, ev = _oracle_rows(x['ent_v'][b, ids], ids)
+        wpos = np.arange(t - W + 1, t + 1)
+        wk, _ = _oracle_rows(x['win_k'][b], wpos)
+        _, wv = _oracle_rows(x['win_v'][b], wpos)
+        ro, _ = OM.A.attend(OM.A.rope.apply(x['q'][b, 0].astype(np.float64), np.int64(t)),
+                            np.concatenate([ek, wk]), np.concatenate([ev, wv]), 1 / np.sqrt(x['q'].shape[-1]))
+        if np.array_equal(np.sort(idx[b, 0]), np.sort(sel)):
+            assert_close_rms(o[b, 0], ro, TOL_BF16, f'o b{b}')
+        else:
+            assert_close_rms(run_oracle_sel(b, sel)[0], ro, TOL_BF16, f'o b{b} (oracle selection)')
+    return swaps
+
+
+def _csa_decode(x, cfg, k):
+    B, N, D = x['ent_k'].shape
+    t = int(x['q_pos'][0, 0])
+    W, m = cfg['W'], cfg['m']
+    packed, scales = F.mxfp4_quantize(x['ik'])
+    ik = v4.IKStore(v4.IK_MXFP4, 128, e2m1=dev(packed), e8m0=dev(scales))
+    iqp, iqs = F.mxfp4_quantize(x['iq'])
+    def kv_pair(kf, vf, pos0, ring=0):
+        # entry-level rows encoded on the GPU as m = 1 entries (keys rotated at their row position)
+        rows = ring if ring else pos0 + kf.shape[1]
+        ks, vs = v4.KVStore.empty(B, rows, D, ring=ring), v4.KVStore.empty(B, rows, D, ring=ring)
+        v4.csa_compress(torch.zeros(B, kf.shape[1], device='cuda'), torch.zeros(1, device='cuda'), pos0,
+                        dev(kf), dev(vf), ks, vs)
+        return ks, vs
+    ek, ev = kv_pair(x['ent_k'], x['ent_v'], 0)
+    wk, wv = kv_pair(x['win_k'], x['win_v'], t - W + 1, ring=W)
+    pos = dev(x['q_pos'])
+    q = bf16_dev(x['q'])
+    print(f'csa decode B={B} N={N} k={k}: index', flush=True)
+    idx = v4.lightning_index_topk(pos, dev(iqp), dev(x['w']), ik, k, m, iq_scale=dev(iqs))
+    print('sparse attention', flush=True)
+    o = v4.sparse_window_attn(q, pos, ek, ev, m, wk, wv, W, idx)
+    torch.cuda.synchronize()
+
+    def rerun(b, sel):
+        oo = v4.sparse_window_attn(q[b:b + 1], pos[b:b + 1],
+                                   *(v4.KVStore(s.fmt, s.dim, s.ring, nope=s.nope[b:b + 1], rope=s.rope[b:b + 1],
+                                                scale=s.scale[b:b + 1]) for s in (ek, ev)),
+                                   m, *(v4.KVStore(s.fmt, s.dim, s.ring, nope=s.nope[b:b + 1], rope=s.rope[b:b + 1],
+                                                   scale=s.scale[b:b + 1]) for s in (wk, wv)),
+                                   W, dev(sel[None, None].astype(np.int32)))
+        return oo.cpu().numpy()[0]
+
+    print('oracle', flush=True)
+    return _decode_check(x, cfg, k, idx.cpu().numpy(), o.cpu().numpy(), F.mxfp4_dequantize(packed, scales),
+                         F.mxfp4_dequantize(iqp, iqs), m, N, rerun)
+
+
+def test_c1_csa_decode_64k():
+    """64K context, batch 8, top-512: every query checked."""
+    cfg, x = synth.c1(1)
+    _csa_decode(x, cfg, cfg['k'])
+
+
+def test_c3_csa_decode_1m():
+    """1M context, batch 4, top-1024, 64 planted winners per query: every query checked."""
+    cfg, x = synth.c3(3)
+    _csa_decode(x, cfg, cfg['k'])
+
+
+def test_c2_hca_decode_1m():
+    """1M raw tokens per sequence compressed 128x on the GPU; HCA attention of the last position.
+
+    Compression: every entry of batch elements 0 and 3 and 256 sampled entries of the others
+    against the oracle's codes; attention: all 4 queries against the oracle's own compression.
+    """
+    cfg, xq = synth.c2_queries(2)
+    B, T, D, m, W = cfg['B'], cfg['T'], cfg['D'], cfg['m'], cfg['W']
+    N = T // m
+    ek, ev = v4.KVStore.empty(B, N, D), v4.KVStore.empty(B, N, D)
+    wk, wv = v4.KVStore.empty(B, W, D, ring=W), v4.KVStore.empty(B, W, D, ring=W)
+    raws = []
+    for b in range(B):
+        print(f'c2 batch {b}: generate + compress', flush=True)
+        r = synth.c2_batch(2, b)
+        raws.append(r)
+        sl = lambda s: v4.KVStore(s.fmt, s.dim, s.ring, nope=s.nope[b:b + 1], rope=s.rope[b:b + 1],
+                                  scale=s.scale[b:b + 1])
+        rk, rv = bf16_dev(r['raw_k']), bf16_dev(r['raw_v'])
+        v4.csa_compress(dev(r['gate']), dev(r['pos_bias']), 0, rk, rv, sl(ek), sl(ev))
+        v4.csa_compress(torch.zeros(1, W, device='cuda'), torch.zeros(1, device='cuda'), T - W,
+                        rk[:, T - W:].contiguous(), rv[:, T - W:].contiguous(), sl(wk), sl(wv))
+        del rk, rv
+    q = bf16_dev(xq['q'])
+    pos = dev(xq['q_pos'])
+    print('hca attention', flush=True)
+    o = v4.hca_attn(q, pos, ek, ev, m, wk, wv, W)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    g = np.random.default_rng(0)
+    for b in range(B):
+        print(f'oracle batch {b}', flush=True)
+        r = raws[b]
+        dk, dv = np.empty((N, D)), np.empty((N, D))
+        gk, gv = ek.nope[b].cpu().numpy(), ev.nope[b].cpu().numpy()
+        check = np.arange(N) if b in (0, B - 1) else np.sort(g.choice(N, 256, replace=False))
+        step = 8192 // 4     # compress in slices of 2,048 entries to bound memory
+        for e0 in range(0, N, step):
+            sl = slice(e0 * m, (e0 + step) * m)
+            k32, v32, _ = OC.compress(r['raw_k'][:, sl], r['raw_v'][:, sl], r['gate'][:, sl], r['pos_bias'], e0 * m)
+            kc, vc = F.kv_quantize(k32[0]), F.kv_quantize(v32[0])
+            dk[e0:e0 + step], dv[e0:e0 + step] = F.kv_dequantize(*kc), F.kv_dequantize(*vc)
+            sel = check[(check >= e0) & (check < e0 + step)] - e0
+            assert np.array_equal(gk[e0 + sel], kc[0][sel]) or np.mean(gk[e0 + sel] != kc[0][sel]) < 1e-4
+            assert np.array_equal(gv[e0 + sel], vc[0][sel]) or np.mean(gv[e0 + sel] != vc[0][sel]) < 1e-4
+        wk32, wv32, _ = OC.compress(r['raw_k'][:, T - W:], r['raw_v'][:, T - W:], np.zeros((1, W), np.float32),
+                                    np.zeros(1, np.float32), T - W)
+        dwk = F.kv_dequantize(*F.kv_quantize(wk32[0]))
+        dwv = F.kv_dequantize(*F.kv_quantize(wv32[0]))
+        ro, _ = OM.hca_query(xq['q'][b, 0], T - 1, dk, dv, dwk, dwv, m, W, win_first=T - W)
+        assert_close_rms(o[b, 0], ro, TOL_BF16, f'o b{b}')
+
+
+def _c4_layer(layer):
+    cfg = synth.WORKLOADS['c4_prefill_128k']
+    T0, T1, D, W, k = cfg['T0'], cfg['T1'], cfg['D'], cfg['W'], cfg['k']
+    T = T0 + T1
+    kind, r = synth.c4_layer(4, layer)
+    m = cfg['m_csa'] if kind == 'csa' else cfg['m_hca']
+    N = T // m
+    print(f'c4 layer {layer} ({kind}): compress', flush=True)
+    ring = 128 * ((T1 + W + 127) // 128)      # holds the window of every new query
+    ek, ev = v4.KVStore.empty(1, N, D), v4.KVStore.empty(1, N, D)
+    wk, wv = v4.KVStore.empty(1, ring, D, ring=ring), v4.KVStore.empty(1, ring, D, ring=ring)
+    ik = v4.IKStore.empty(1, N, 128) if kind == 'csa' else None
+    rk, rv = bf16_dev(r['raw_k']), bf16_dev(r['raw_v'])
+    ru = bf16_dev(r['raw_ik']) if kind == 'csa' else None
+    gate, bias = dev(r['gate']), dev(r['pos_bias'])
+    # setup: the old context; checked path: the new chunk's entries and window rows
+    for lo, hi in ((0, T0), (T0, T)):
+        v4.csa_compress(gate[:, lo:hi].contiguous(), bias, lo, rk[:, lo:hi].contiguous(), rv[:, lo:hi].contiguous(),
+                        ek, ev, None if ru is None else ru[:, lo:hi].contiguous(), ik)
+    v4.csa_compress(torch.zeros(1, T1 + W, device='cuda'), torch.zeros(1, device='cuda'), T0 - W,
+                    rk[:, T0 - W:].contiguous(), rv[:, T0 - W:].contiguous(), wk, wv)
+    xq = synth.c4_queries(4, layer)
+    pos = dev(xq['q_pos'])
+    q = bf16_dev(xq['q'])
+    if kind == 'csa':
+        iqp, iqs = F.mxfp4_quantize(xq['iq'])
+        print('index (8,192 queries)', flush=True)
+        idx = v4.lightning_index_topk(pos, dev(iqp), dev(xq['w']), ik, k, m, iq_scale=dev(iqs))
+        print('sparse attention', flush=True)
+        o = v4.sparse_window_attn(q, pos, ek, ev, m, wk, wv, W, idx)
+    else:
+        print('hca attention (8,192 queries)', flush=True)
+        o = v4.hca_attn(q, pos, ek, ev, m, wk, wv, W)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy()
+    print('oracle', flush=True)
+    caches = OM.build_caches(r['raw_k'], r['raw_v'], r['gate'], r['pos_bias'], 'e4m3_bf16',
+                             raw_ik=r.get('raw_ik'), ik_fmt='mxfp4')
+    # the new chunk's compressed entries and window rows are part of the checked path
+    gk = ek.nope[0].cpu().numpy()
+    ck = caches['ent_k']['nope'][0]
+    new = slice(T0 // m, T // m)
+    assert np.mean(gk[new] != ck[new]) < 1e-4, 'new entries differ'
+    if kind == 'csa':
+        assert np.mean(ik.e2m1[0].cpu().numpy()[new] != caches['ik']['e2m1'][0][new]) < 1e-4
+    g = np.random.default_rng(layer)
+    sample = sorted({0, 1, 2, 3, 127, 128, T1 - 1, *g.choice(T1, 24, replace=False).tolist()})
+    diq = F.mxfp4_dequantize(iqp, iqs) if kind == 'csa' else None
+    idx_h = idx.cpu().numpy() if kind == 'csa' else None
+    for i in sample:
+        t = T0 + i
+        if kind == 'csa':
+            ro, _, sel, scores = OM.csa_query(xq['q'][0, i], t, diq[0, i], xq['w'][0, i], caches['dik'][0],
+                                              caches['dk'][0], caches['dv'][0], caches['dwk'][0], caches['dwv'][0],
+                                              m, k, W)
+            assert_topk(idx_h[0, i], scores, OI.n_visible(t, m, N), k, f'layer {layer} query {i}')
+            if np.array_equal(np.sort(idx_h[0, i]), np.sort(sel)):
+                assert_close_rms(o[0, i], ro, TOL_BF16, f'o layer {layer} query {i}')
+            else:
+                o2 = v4.sparse_window_attn(q[:, i:i + 1].contiguous(), pos[:, i:i + 1].contiguous(), ek, ev, m, wk, wv,
+                                           W, dev(sel[None, None].astype(np.int32)))
+                assert_close_rms(o2.cpu().numpy()[0, 0], ro, TOL_BF16, f'o layer {layer} query {i} (oracle sel)')
+        else:
+            ro, _ = OM.hca_query(xq['q'][0, i], t, caches['dk'][0], caches['dv'][0], caches['dwk'][0],
+                                 caches['dwv'][0], m, W)
+            assert_close_rms(o[0, i], ro, TOL_BF16, f'o layer {layer} query {i}')
+
+
+@pytest.mark.parametrize('layer', [0, 1, 2, 3])
+def test_c4_chunked_prefill_layer(layer):
+    """8,192 new tokens on a 131,072-token context; layers CSA, HCA, CSA, HCA.
+
+    GPU: compression of the new chunk, then every new query (index + sparse attention, or
+    HCA attention). Oracle: 31 sampled queries per layer (first, block boundaries, last, random).
+    """
+    _c4_layer(layer)
