@@ -169,8 +169,9 @@ int check_index(const v4a_index_args *a) {
 
 // --------------------------------------------------- attention planning ----
 
-constexpr int KS_MIN_MX = 128;  // keys per split: the MFMA kernel loads 4 tiles of 32 together
-constexpr int KS_MIN_F32 = 32;
+constexpr int KS_MIN = 32;      // keys per split: one tile at least
+constexpr int KS_MAX = 2048;    // the FP8 kernel resolves a split's rows into LDS
+constexpr int WG_TARGET = 512;  // about two resident workgroups per compute unit
 
 struct AttnLayout {
     int n_split, keys_per_split;
@@ -189,13 +190,13 @@ AttnLayout attn_layout(const v4a_attn_args *a, bool sparse, int k, int64_t n_ove
         }
     }
     const int64_t cap = n_list + a->W;
-    const bool mx = a->win_k && a->win_k->fmt == V4A_KV_E4M3_BF16;
-    const int ks_min = mx ? KS_MIN_MX : KS_MIN_F32;
-    int64_t n_split = (cap + ks_min - 1) / ks_min;
-    const int64_t want = (512 + Q - 1) / Q;  // aim at about two workgroups per compute unit
-    n_split = std::max<int64_t>(1, std::min(n_split, want));
+    // enough splits to fill the device when the queries alone cannot, at least
+    // one tile per split, and no split longer than KS_MAX keys
+    int64_t n_split = std::min((cap + KS_MIN - 1) / KS_MIN, (WG_TARGET + Q - 1) / Q);
+    n_split = std::max<int64_t>(n_split, (cap + KS_MAX - 1) / KS_MAX);
+    n_split = std::max<int64_t>(1, std::min<int64_t>(n_split, 1024));
     int64_t ks = (cap + n_split - 1) / n_split;
-    ks = std::max<int64_t>(32, (ks + 31) / 32 * 32);
+    ks = std::max<int64_t>(KS_MIN, (ks + 31) / 32 * 32);
     n_split = std::max<int64_t>(1, (cap + ks - 1) / ks);
     L.n_split = (int)n_split;
     L.keys_per_split = (int)ks;

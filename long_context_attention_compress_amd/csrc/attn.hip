@@ -23,11 +23,15 @@
 //    two BF16 terms (hi + lo) so it keeps ~16 mantissa bits.
 //  * O^T += V^T P^T with dims as M: the lane's eight probabilities are already
 //    the B operand (the key order inside the 32-wide contraction is permuted
-//    to match), V is staged transposed in LDS, and the V row scale is folded
-//    into P for the E4M3 dims; P also goes in as two BF16 terms (hi + lo).
+//    to match); V is staged row-major in LDS and read transposed with
+//    ds_read_b64_tr_b16; the V row scale is folded into P for the E4M3 dims,
+//    and P goes in as two BF16 terms (hi + lo).
 //  * All 64 heads of a workgroup share each staged K/V tile.
-//  * The raw bytes of every tile of the split are loaded into registers before
-//    any is used, so one HBM round trip covers the whole split.
+//  * The split's store rows are resolved into LDS first (one coalesced pass
+//    over the selected ids); tile loads are branch-free and run two tiles
+//    ahead of the tile being computed.
+//  * The running max is raised lazily (only when a tile beats it by 2^8), so
+//    the 48 accumulator registers are rarely rescaled.
 
 #include "common.hpp"
 
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(AT) void attn_f32_kernel(AttnPlan p) {
         if (d >= Dn) {
             const int r = d - Dn, pr = r >> 1;
             double sn, cs;
-            sincos((double)ki.t * p.inv_freq[pr], &sn, &cs);
+            rope_sincos((double)ki.t * p.inv_freq[pr], &sn, &cs);
             const double x = qin[h * D + Dn + 2 * pr], y = qin[h * D + Dn + 2 * pr + 1];
             v = (float)((r & 1) ? x * sn + y * cs : x * cs - y * sn);
         }
@@ -216,61 +220,61 @@ __global__ __launch_bounds__(AT) void attn_f32_kernel(AttnPlan p) {
 
 constexpr int MD = 192;         // head dim
 constexpr int MDN = 128;        // E4M3 dims
-constexpr int KB_LD = MD + 8;   // bf16 elements per staged K row (padded)
-constexpr int VT_LD = TK + 8;   // bf16 elements per staged V^T row (padded)
-constexpr int PF = 4;           // tiles whose raw bytes are loaded together
+constexpr int KB_LD = MD + 8;   // bf16 elements per staged K or V row (padded)
+constexpr int MAX_KS = 2048;    // keys per split (their store rows are resolved into LDS first)
 
 struct MxSmem {
-    __bf16 kb[TK * KB_LD];
-    __bf16 vt[MD * VT_LD];
+    __bf16 kb[TK * KB_LD];      // K tile, row-major BF16
+    __bf16 vb[TK * KB_LD];      // V tile, row-major BF16 (read transposed by ds_read_b64_tr_b16)
     float ksc[TK];
     float vsc[TK];
     int kval[TK];
+    double rcos[ROPE_PAIRS];
+    double rsin[ROPE_PAIRS];
+    int32_t rows[MAX_KS];       // row of each key of the split; bit 30 marks a window row; -1: no key
 };
+
+constexpr int32_t WIN_BIT = 1 << 30;
 
 struct TileRegs {
     v4i k[2], v[2];
     float sc;
-    int row[2];
-    int win[2];
 };
 
-__device__ __forceinline__ void load_tile(const AttnPlan &p, int q, int b, const KeyInfo &ki, int64_t jt, int64_t j1,
+// Issue the loads of one 32-key tile. Branch-free: a slot without a key reads
+// row 0 of the window store (always present) and is zeroed afterwards, so the
+// compiler keeps every load of the tile in flight together.
+__device__ __forceinline__ void load_tile(const AttnPlan &p, int b, const MxSmem &sm, int rel, int n_rel,
                                           TileRegs &R) {
     const int tid = threadIdx.x;
     const int part = tid & 15;
+    const int64_t koff = part < 8 ? 16 * part : 16 * (part - 8);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 16 * h;
-        bool win = false;
-        const int64_t row = (jt + r < j1) ? key_row(p, q, ki, jt + r, &win) : -1;
-        R.row[h] = (int)(row >= 0);
-        R.win[h] = win;
-        v4i kx = {0, 0, 0, 0}, vx = {0, 0, 0, 0};
-        if (row >= 0) {
-            const KvView &K = win ? p.wk : p.ek;
-            const KvView &V = win ? p.wv : p.ev;
-            const char *kp = part < 8 ? K.nope + b * K.nope_bs + row * K.nope_rs + 16 * part
-                                      : K.rope + b * K.rope_bs + row * K.rope_rs + 16 * (part - 8);
-            const char *vp = part < 8 ? V.nope + b * V.nope_bs + row * V.nope_rs + 16 * part
-                                      : V.rope + b * V.rope_bs + row * V.rope_rs + 16 * (part - 8);
-            kx = __builtin_nontemporal_load((const v4i *)kp);
-            vx = __builtin_nontemporal_load((const v4i *)vp);
-        }
-        R.k[h] = kx;
-        R.v[h] = vx;
+        const int32_t code = rel + r < n_rel ? sm.rows[rel + r] : -1;
+        const bool ok = code >= 0;
+        const bool win = !ok || (code & WIN_BIT);
+        const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
+        const KvView &K = win ? p.wk : p.ek;
+        const KvView &V = win ? p.wv : p.ev;
+        const char *kb = part < 8 ? K.nope + b * K.nope_bs + row * K.nope_rs : K.rope + b * K.rope_bs + row * K.rope_rs;
+        const char *vb = part < 8 ? V.nope + b * V.nope_bs + row * V.nope_rs : V.rope + b * V.rope_bs + row * V.rope_rs;
+        const v4i kx = __builtin_nontemporal_load((const v4i *)(kb + koff));
+        const v4i vx = __builtin_nontemporal_load((const v4i *)(vb + koff));
+        const v4i z = {0, 0, 0, 0};
+        R.k[h] = ok ? kx : z;
+        R.v[h] = ok ? vx : z;
     }
     // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
-    R.sc = 0.f;
-    if (tid < 2 * TK) {
-        const int r = tid & (TK - 1);
-        bool win = false;
-        const int64_t row = (jt + r < j1) ? key_row(p, q, ki, jt + r, &win) : -1;
-        if (row >= 0) {
-            const KvView &S = (tid < TK) ? (win ? p.wk : p.ek) : (win ? p.wv : p.ev);
-            R.sc = *(const float *)(S.scale + b * S.scale_bs + row * S.scale_rs);
-        }
-    }
+    const int r = tid & (TK - 1);
+    const int32_t code = (tid < 2 * TK && rel + r < n_rel) ? sm.rows[rel + r] : -1;
+    const bool ok = code >= 0;
+    const bool win = !ok || (code & WIN_BIT);
+    const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
+    const KvView &S = (tid < TK) ? (win ? p.wk : p.ek) : (win ? p.wv : p.ev);
+    const float sc = *(const float *)(S.scale + b * S.scale_bs + row * S.scale_rs);
+    R.sc = ok ? sc : 0.f;
 }
 
 template <bool HI>
@@ -279,68 +283,85 @@ __device__ __forceinline__ unsigned fp8x2_to_bf16x2(unsigned w) {
     return __builtin_bit_cast(unsigned, v);
 }
 
-__device__ __forceinline__ void stage_tile(const TileRegs &R, MxSmem &sm) {
+// 16 E4M3 codes -> 16 BF16 values (exact), written as two 16-byte LDS stores
+__device__ __forceinline__ void store_codes(__bf16 *dst, const v4i &c) {
+    v4i lo, hi;
+    lo[0] = fp8x2_to_bf16x2<false>(c[0]);
+    lo[1] = fp8x2_to_bf16x2<true>(c[0]);
+    lo[2] = fp8x2_to_bf16x2<false>(c[1]);
+    lo[3] = fp8x2_to_bf16x2<true>(c[1]);
+    hi[0] = fp8x2_to_bf16x2<false>(c[2]);
+    hi[1] = fp8x2_to_bf16x2<true>(c[2]);
+    hi[2] = fp8x2_to_bf16x2<false>(c[3]);
+    hi[3] = fp8x2_to_bf16x2<true>(c[3]);
+    *(v4i *)dst = lo;
+    *(v4i *)(dst + 8) = hi;
+}
+
+__device__ __forceinline__ void stage_tile(const TileRegs &R, const int *valid_rows, MxSmem &sm, int rel, int n_rel) {
     const int tid = threadIdx.x;
     const int part = tid & 15;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 16 * h;
         if (part < 8) {
-            // 16 E4M3 codes -> 16 BF16 (exact)
-            v4i c = R.k[h];
-            v4i lo, hi;
-            lo[0] = fp8x2_to_bf16x2<false>(c[0]);
-            lo[1] = fp8x2_to_bf16x2<true>(c[0]);
-            lo[2] = fp8x2_to_bf16x2<false>(c[1]);
-            lo[3] = fp8x2_to_bf16x2<true>(c[1]);
-            hi[0] = fp8x2_to_bf16x2<false>(c[2]);
-            hi[1] = fp8x2_to_bf16x2<true>(c[2]);
-            hi[2] = fp8x2_to_bf16x2<false>(c[3]);
-            hi[3] = fp8x2_to_bf16x2<true>(c[3]);
-            *(v4i *)&sm.kb[r * KB_LD + 16 * part] = lo;
-            *(v4i *)&sm.kb[r * KB_LD + 16 * part + 8] = hi;
-            v4i cv = R.v[h];
-            unsigned u[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u[2 * i] = fp8x2_to_bf16x2<false>(cv[i]);
-                u[2 * i + 1] = fp8x2_to_bf16x2<true>(cv[i]);
-            }
-            unsigned short *vt = (unsigned short *)sm.vt;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                vt[(16 * part + 2 * i) * VT_LD + r] = (unsigned short)(u[i] & 0xFFFF);
-                vt[(16 * part + 2 * i + 1) * VT_LD + r] = (unsigned short)(u[i] >> 16);
-            }
+            store_codes(&sm.kb[r * KB_LD + 16 * part], R.k[h]);
+            store_codes(&sm.vb[r * KB_LD + 16 * part], R.v[h]);
         } else {
             *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * (part - 8)] = R.k[h];
-            v4i cv = R.v[h];
-            unsigned short *vt = (unsigned short *)sm.vt;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vt[(MDN + 8 * (part - 8) + 2 * i) * VT_LD + r] = (unsigned short)((unsigned)cv[i] & 0xFFFF);
-                vt[(MDN + 8 * (part - 8) + 2 * i + 1) * VT_LD + r] = (unsigned short)((unsigned)cv[i] >> 16);
-            }
+            *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * (part - 8)] = R.v[h];
         }
     }
     if (tid < TK) {
         sm.ksc[tid] = R.sc;
+        sm.kval[tid] = rel + tid < n_rel && sm.rows[rel + tid] >= 0;
     } else if (tid < 2 * TK) {
         sm.vsc[tid - TK] = R.sc;
     }
-    // validity: thread with part == 0 owns rows (tid>>4) and 16+(tid>>4)
-    if (part == 0) {
-        sm.kval[(tid >> 4)] = R.row[0];
-        sm.kval[16 + (tid >> 4)] = R.row[1];
-    }
+    (void)valid_rows;
 }
 
-__device__ __forceinline__ bf16x8 lds8(const __bf16 *p) { return *(const bf16x8 *)p; }
-__device__ __forceinline__ bf16x8 lds4x2(const __bf16 *a, const __bf16 *b) {
-    v2u x = *(const v2u *)a, y = *(const v2u *)b;
-    v4i r = {(int)x[0], (int)x[1], (int)y[0], (int)y[1]};
-    return __builtin_bit_cast(bf16x8, r);
+__device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *(const bf16x8 *)p; }
+
+// V^T operand of the P.V product: lane (group g, position j) gets, for dim
+// 16*dt + j, the keys of its contraction slots: 4g..4g+3 and 16+4g..16+4g+3.
+// Each ds_read_b64_tr_b16 transposes a 16x4 block within the 16-lane group:
+// source lane 4k+r reads key kappa(k), dims 16*dt + 4r .. +3.
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 vt_operand(const MxSmem &sm, int dt, int g, int j) {
+    const int k = j >> 2, r = j & 3;
+    const __bf16 *a = &sm.vb[(4 * g + k) * KB_LD + 16 * dt + 4 * r];
+    const __bf16 *c = &sm.vb[(16 + 4 * g + k) * KB_LD + 16 * dt + 4 * r];
+    v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)a);
+    v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)c);
+    v4i r4 = {(int)((unsigned short)x[0] | ((unsigned)(unsigned short)x[1] << 16)),
+              (int)((unsigned short)x[2] | ((unsigned)(unsigned short)x[3] << 16)),
+              (int)((unsigned short)y[0] | ((unsigned)(unsigned short)y[1] << 16)),
+              (int)((unsigned short)y[2] | ((unsigned)(unsigned short)y[3] << 16))};
+    return __builtin_bit_cast(bf16x8, r4);
 }
+
+__device__ __forceinline__ float swap16_max(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+    auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+// The running maximum is raised only when a tile's maximum exceeds it by more
+// than 2^RESCALE_SLACK (then the accumulators are rescaled); in between, the
+// probabilities may exceed 1 by at most that factor, which float32 absorbs.
+constexpr float RESCALE_SLACK = 8.0f;
 
 template <int NW>
 __global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
@@ -354,22 +375,34 @@ __global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
     const bool active = wave < NW;
     const int head = 16 * wave + col;
 
+    const int64_t n_keys = ki.n_list + ki.n_win;
+    const int64_t j0 = (int64_t)split * p.keys_per_split;
+    const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
+    const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
+    // resolve the split's keys to store rows once (coalesced id loads), and the RoPE table
+    for (int i = tid; i < n_rel; i += AT) {
+        bool win;
+        const int64_t row = key_row(p, q, ki, j0 + i, &win);
+        sm.rows[i] = row < 0 ? -1 : (int32_t)row | (win ? WIN_BIT : 0);
+    }
+    if (tid < ROPE_PAIRS) rope_sincos((double)ki.t * p.inv_freq[tid], &sm.rsin[tid], &sm.rcos[tid]);
+    __syncthreads();
+
     // query operands (B of S^T = K Q^T): head `col` of this wave, dims 32c + 8g .. +8
     bf16x8 qn[4], qrh[2], qrl[2];
     {
         const int hh = active ? head : 0;
         const __bf16 *qp = (const __bf16 *)p.q + ((size_t)q * H + hh) * MD;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qn[c] = lds8(qp + 32 * c + 8 * g);
+        for (int c = 0; c < 4; ++c) qn[c] = ld16(qp + 32 * c + 8 * g);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            bf16x8 raw = lds8(qp + MDN + 32 * c + 8 * g);
+            bf16x8 raw = ld16(qp + MDN + 32 * c + 8 * g);
             bf16x8 hi, lo;
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
                 const int pr = (32 * c + 8 * g + i) >> 1;
-                double sn, cs;
-                sincos((double)ki.t * p.inv_freq[pr], &sn, &cs);
+                const double sn = sm.rsin[pr], cs = sm.rcos[pr];
                 const double x = (double)(float)raw[i], y = (double)(float)raw[i + 1];
                 const float rx = (float)(x * cs - y * sn), ry = (float)(x * sn + y * cs);
                 hi[i] = (__bf16)rx;
@@ -386,96 +419,87 @@ __global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
     v4f O[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-    const int64_t n_keys = ki.n_list + ki.n_win;
-    const int64_t j0 = (int64_t)split * p.keys_per_split;
-    const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    for (int64_t jg = j0; jg < j1; jg += PF * TK) {
-        TileRegs R[PF];
+    // two-stage pipeline: tile i+2 is loaded while tile i is staged and computed
+    const int n_tiles = (n_rel + TK - 1) / TK;
+    TileRegs RA, RB;
+    if (n_tiles > 0) load_tile(p, b, sm, 0, n_rel, RA);
+    if (n_tiles > 1) load_tile(p, b, sm, TK, n_rel, RB);
+    for (int t = 0; t < n_tiles; ++t) {
+        __syncthreads();
+        if (t & 1) {
+            stage_tile(RB, nullptr, sm, t * TK, n_rel);
+            if (t + 2 < n_tiles) load_tile(p, b, sm, (t + 2) * TK, n_rel, RB);
+        } else {
+            stage_tile(RA, nullptr, sm, t * TK, n_rel);
+            if (t + 2 < n_tiles) load_tile(p, b, sm, (t + 2) * TK, n_rel, RA);
+        }
+        __syncthreads();
+        if (active) {
+            float s[2][4];
 #pragma unroll
-        for (int u = 0; u < PF; ++u)
-            if (jg + u * TK < j1) load_tile(p, q, b, ki, jg + u * TK, j1, R[u]);
+            for (int st = 0; st < 2; ++st) {
+                v4f an = zero, ar = zero;
+                const __bf16 *krow = &sm.kb[(16 * st + col) * KB_LD + 8 * g];
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-            if (jg + u * TK >= j1) break;
-            __syncthreads();
-            stage_tile(R[u], sm);
-            __syncthreads();
-            if (active) {
-                float s[2][4];
+                for (int c = 0; c < 4; ++c)
+                    an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld16(krow + 32 * c), qn[c], an, 0, 0, 0);
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    v4f an = zero, ar = zero;
-                    const __bf16 *krow = &sm.kb[(16 * st + col) * KB_LD + 8 * g];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds8(krow + 32 * c), qn[c], an, 0, 0, 0);
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        bf16x8 a = lds8(krow + MDN + 32 * c);
-                        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrh[c], ar, 0, 0, 0);
-                        ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrl[c], ar, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int key = 16 * st + 4 * g + j;
-                        s[st][j] = sm.kval[key] ? (an[j] * sm.ksc[key] + ar[j]) * sc2 : -__builtin_inff();
-                    }
+                for (int c = 0; c < 2; ++c) {
+                    bf16x8 a = ld16(krow + MDN + 32 * c);
+                    ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrh[c], ar, 0, 0, 0);
+                    ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrl[c], ar, 0, 0, 0);
                 }
-                float mx = s[0][0];
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+                for (int j = 0; j < 4; ++j) {
+                    const int key = 16 * st + 4 * g + j;
+                    s[st][j] = sm.kval[key] ? (an[j] * sm.ksc[key] + ar[j]) * sc2 : -__builtin_inff();
+                }
+            }
+            float mx = s[0][0];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, s[st][j]);
-                mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16, 64));
-                mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32, 64));
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, s[st][j]);
+            mx = swap32_max(swap16_max(mx));
+            // raise the running max (and rescale) only when this tile exceeds it by the slack
+            if (__builtin_amdgcn_ballot_w64(mx > mrun + RESCALE_SLACK)) {
                 const float mn = __builtin_fmaxf(mrun, mx);
-                float c = 1.f, psum = 0.f;
-                float pr[2][4];
-                if (mn != -__builtin_inff()) {
-                    c = exp2f(mrun - mn);
-#pragma unroll
-                    for (int st = 0; st < 2; ++st)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            pr[st][j] = exp2f(s[st][j] - mn);
-                            psum += pr[st][j];
-                        }
-                } else {
-#pragma unroll
-                    for (int st = 0; st < 2; ++st)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) pr[st][j] = 0.f;
-                }
-                psum += __shfl_xor(psum, 16, 64);
-                psum += __shfl_xor(psum, 32, 64);
-                lrun = lrun * c + psum;
-                mrun = mn;
+                const float c = mn == -__builtin_inff() ? 1.f : exp2f(mrun - mn);
+                lrun *= c;
 #pragma unroll
                 for (int i = 0; i < 12; ++i) O[i] *= c;
-                // P as two BF16 terms (hi + lo): one BF16 alone would cost 2^-9 of the
-                // largest output element, which outliers in V turn into a visible error.
-                bf16x8 pnh, pnl, pbh, pbl;
+                mrun = mn;
+            }
+            float pr[2][4], psum = 0.f;
 #pragma unroll
-                for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int key = 16 * st + 4 * g + j;
-                        const float xn = pr[st][j] * sm.vsc[key], xb = pr[st][j];
-                        pnh[4 * st + j] = (__bf16)xn;
-                        pnl[4 * st + j] = (__bf16)(xn - (float)pnh[4 * st + j]);
-                        pbh[4 * st + j] = (__bf16)xb;
-                        pbl[4 * st + j] = (__bf16)(xb - (float)pbh[4 * st + j]);
-                    }
-#pragma unroll
-                for (int dt = 0; dt < 12; ++dt) {
-                    const __bf16 *vr = &sm.vt[(16 * dt + col) * VT_LD];
-                    bf16x8 a = lds4x2(vr + 4 * g, vr + 16 + 4 * g);
-                    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnh : pbh, O[dt], 0, 0, 0);
-                    O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnl : pbl, O[dt], 0, 0, 0);
+                for (int j = 0; j < 4; ++j) {
+                    pr[st][j] = s[st][j] == -__builtin_inff() ? 0.f : exp2f(s[st][j] - mrun);
+                    psum += pr[st][j];
                 }
+            lrun += swap32_sum(swap16_sum(psum));
+            // P as two BF16 terms (hi + lo): one BF16 alone would cost 2^-9 of the
+            // largest output element, which outliers in V turn into a visible error.
+            bf16x8 pnh, pnl, pbh, pbl;
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int key = 16 * st + 4 * g + j;
+                    const float xn = pr[st][j] * sm.vsc[key], xb = pr[st][j];
+                    pnh[4 * st + j] = (__bf16)xn;
+                    pnl[4 * st + j] = (__bf16)(xn - (float)pnh[4 * st + j]);
+                    pbh[4 * st + j] = (__bf16)xb;
+                    pbl[4 * st + j] = (__bf16)(xb - (float)pbh[4 * st + j]);
+                }
+#pragma unroll
+            for (int dt = 0; dt < 12; ++dt) {
+                const bf16x8 a = vt_operand(sm, dt, g, col);
+                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnh : pbh, O[dt], 0, 0, 0);
+                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnl : pbl, O[dt], 0, 0, 0);
             }
         }
     }
@@ -513,32 +537,57 @@ __global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
 
 // -------------------------------------------------------------- combine ----
 
+constexpr int MAX_SPLIT = 1024;
+
+// Merge the splits of one (query, head): the per-split weights exp2(m_s - M) / L
+// are computed once into LDS, then each thread sums its output dim over the
+// splits with independent loads.
 template <int OUT_BF16>
-__global__ void attn_combine_kernel(AttnPlan p) {
-    const int q = blockIdx.x, h = blockIdx.y;
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnPlan p) {
+    __shared__ float wgt[MAX_SPLIT];
+    __shared__ float red[8];
+    const int q = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int D = p.D, H = p.H, S = p.n_split;
     const size_t base = (size_t)q * S * H;
-    float M = -__builtin_inff();
-    for (int s = 0; s < S; ++s) M = __builtin_fmaxf(M, p.part_ml[((base + (size_t)s * H) + h) * 2]);
-    float L = 0.f;
-    if (M != -__builtin_inff())
-        for (int s = 0; s < S; ++s) {
-            const size_t i = (base + (size_t)s * H) + h;
-            L += p.part_ml[i * 2 + 1] * exp2f(p.part_ml[i * 2] - M);
+    float mloc = -__builtin_inff();
+    for (int s = tid; s < S; s += 256) {
+        const float m = p.part_ml[((base + (size_t)s * H) + h) * 2];
+        wgt[s] = m;
+        mloc = __builtin_fmaxf(mloc, m);
+    }
+    mloc = wave_max(mloc);
+    if ((tid & 63) == 0) red[tid >> 6] = mloc;
+    __syncthreads();
+    const float M = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    float lloc = 0.f;
+    for (int s = tid; s < S; s += 256) {
+        const float w = M == -__builtin_inff() ? 0.f : exp2f(wgt[s] - M);
+        wgt[s] = w;
+        lloc += w * p.part_ml[((base + (size_t)s * H) + h) * 2 + 1];
+    }
+    lloc = wave_sum(lloc);
+    __syncthreads();
+    if ((tid & 63) == 0) red[4 + (tid >> 6)] = lloc;
+    __syncthreads();
+    const float L = (red[4] + red[5]) + (red[6] + red[7]);
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int d = tid; d < D; d += 256) {
+        const float *po = p.part_o + (base + h) * D + d;
+        const size_t stride = (size_t)H * D;
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        int s = 0;
+        for (; s + 4 <= S; s += 4) {
+            a0 += po[(size_t)(s + 0) * stride] * wgt[s + 0];
+            a1 += po[(size_t)(s + 1) * stride] * wgt[s + 1];
+            a2 += po[(size_t)(s + 2) * stride] * wgt[s + 2];
+            a3 += po[(size_t)(s + 3) * stride] * wgt[s + 3];
         }
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float o = 0.f;
-        if (L > 0.f) {
-            for (int s = 0; s < S; ++s) {
-                const size_t i = (base + (size_t)s * H) + h;
-                o += p.part_o[i * D + d] * exp2f(p.part_ml[i * 2] - M);
-            }
-            o /= L;
-        }
+        for (; s < S; ++s) a0 += po[(size_t)s * stride] * wgt[s];
+        const float o = ((a0 + a1) + (a2 + a3)) * inv;
         if (OUT_BF16) ((__bf16 *)p.o)[((size_t)q * H + h) * D + d] = (__bf16)o;
         else ((float *)p.o)[((size_t)q * H + h) * D + d] = o;
     }
-    if (threadIdx.x == 0 && p.lse)
+    if (tid == 0 && p.lse)
         p.lse[(size_t)q * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -__builtin_inff();
 }
 

@@ -112,6 +112,56 @@ __device__ __forceinline__ int mx_exponent(float amax) {
     return e < -127 ? -127 : e;
 }
 
+// ------------------------------------------------------------- RoPE angle ----
+// sin and cos of a float64 angle. RoPE angles reach 1e6 radians at a million
+// positions, where the library routine takes its slow large-argument path.
+// Here: Cody-Waite reduction by pi/2 with pi/2 split into three doubles (the
+// first two carry 28 significant bits, so n*P1 and n*P2 are exact for
+// |n| < 2^25), then Taylor polynomials on |r| <= pi/4 (terms to r^23, error
+// below 1e-27). Angles beyond 2^25 * pi/2 fall back to the library routine.
+__device__ __forceinline__ void rope_sincos(double x, double *sn, double *cs) {
+    const double ax = __builtin_fabs(x);
+    if (!(ax < 5.2e7)) {  // also catches NaN
+        sincos(x, sn, cs);
+        return;
+    }
+    const double P1 = 0x1.921fb54000000p+0, P2 = 0x1.10b4610000000p-30, P3 = 0x1.a62633145c06ep-58;
+    const double n = __builtin_rint(x * 0x1.45f306dc9c883p-1);  // x * 2/pi
+    const double r = ((x - n * P1) - n * P2) - n * P3;
+    const double r2 = r * r;
+    // sin r = r (1 - r^2/3! + r^4/5! - ...), cos r = 1 - r^2/2! + r^4/4! - ...
+    double ps = -1.0 / 25852016738884976640000.0;  // -1/23!
+    ps = __builtin_fma(ps, r2, 1.0 / 51090942171709440000.0);
+    ps = __builtin_fma(ps, r2, -1.0 / 121645100408832000.0);
+    ps = __builtin_fma(ps, r2, 1.0 / 355687428096000.0);
+    ps = __builtin_fma(ps, r2, -1.0 / 1307674368000.0);
+    ps = __builtin_fma(ps, r2, 1.0 / 6227020800.0);
+    ps = __builtin_fma(ps, r2, -1.0 / 39916800.0);
+    ps = __builtin_fma(ps, r2, 1.0 / 362880.0);
+    ps = __builtin_fma(ps, r2, -1.0 / 5040.0);
+    ps = __builtin_fma(ps, r2, 1.0 / 120.0);
+    ps = __builtin_fma(ps, r2, -1.0 / 6.0);
+    const double s = __builtin_fma(ps * r2, r, r);
+    double pc = 1.0 / 1124000727777607680000.0;     // 1/22!
+    pc = __builtin_fma(pc, r2, -1.0 / 2432902008176640000.0);
+    pc = __builtin_fma(pc, r2, 1.0 / 6402373705728000.0);
+    pc = __builtin_fma(pc, r2, -1.0 / 20922789888000.0);
+    pc = __builtin_fma(pc, r2, 1.0 / 87178291200.0);
+    pc = __builtin_fma(pc, r2, -1.0 / 479001600.0);
+    pc = __builtin_fma(pc, r2, 1.0 / 3628800.0);
+    pc = __builtin_fma(pc, r2, -1.0 / 40320.0);
+    pc = __builtin_fma(pc, r2, 1.0 / 720.0);
+    pc = __builtin_fma(pc, r2, -1.0 / 24.0);
+    pc = __builtin_fma(pc, r2, 0.5);
+    const double c = __builtin_fma(-pc, r2, 1.0);
+    switch (((long long)n) & 3) {
+        case 0: *sn = s; *cs = c; break;
+        case 1: *sn = c; *cs = -s; break;
+        case 2: *sn = -s; *cs = -c; break;
+        default: *sn = -c; *cs = s; break;
+    }
+}
+
 // --------------------------------------------------- order-preserving key ----
 // Larger float -> larger key; -0 == +0; NaN -> 0 (below every number).
 __device__ __forceinline__ uint32_t score_key(float s) {

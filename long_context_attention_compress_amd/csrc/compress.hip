@@ -112,7 +112,7 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
                     double y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
                     if (which == 0) {
                         double sn, cs;
-                        sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                        rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
                         double xr = x * cs - y * sn;
                         double yr = x * sn + y * cs;
                         x = xr;
