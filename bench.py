@@ -215,6 +215,19 @@ def run_step(calls, s, L, ev=None):
         ev[4].record()
 
 
+CALIB_BYTES = 256 << 20
+
+
+def calibration_copy(torch):
+    """One plain streaming kernel of known size (read 256 MiB, write 256 MiB: an
+    elementwise negation), so that hardware byte counters taken over this program
+    can be scaled against a kernel whose traffic is known exactly."""
+    src = torch.ones(CALIB_BYTES // 4, device='cuda')
+    dst = torch.neg(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def sleep_cycles_per_ms(torch):
     """Calibrate torch.cuda._sleep (a spin kernel) against HIP events."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -308,6 +321,7 @@ def main():
     print(f'[bench] building {L} layer caches (B={B}, context {T})', file=sys.stderr, flush=True)
     layers, inputs = build_layers(v4, synth, torch, L, a.seed)
     calls, outs = prepare_calls(v4, synth, torch, layers, inputs, a.seed)
+    calibration_copy(torch)
     print('[bench] warmup', file=sys.stderr, flush=True)
     for s in range(a.warmup):
         run_step(calls, s, L)
