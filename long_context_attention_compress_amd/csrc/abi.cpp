@@ -133,9 +133,11 @@ IndexLayout index_layout(const v4a_index_args *a) {
     const int64_t Q = (int64_t)a->B * a->Tq;
     const int64_t rows = a->keys->rows;
     L.chunk = 1024;
-    L.n_chunks = (int)((rows + L.chunk - 1) / L.chunk);
+    L.n_chunks = (int)std::max<int64_t>(1, (rows + L.chunk - 1) / L.chunk);
     L.s_local = 2 * ((a->k + L.n_chunks - 1) / L.n_chunks) + 8;
-    L.region_cap = std::min(L.chunk, std::max(2 * L.s_local + 64, 128));
+    // a multiple of 4 slots and at least 32: the merge reads a region's first
+    // 32 slots with 16-byte loads
+    L.region_cap = std::min(L.chunk, (std::max(2 * L.s_local + 64, 128) + 3) / 4 * 4);
     L.off_meta = 0;
     L.off_key = align_up(L.off_meta + (size_t)Q * L.n_chunks * 8, 256);
     L.off_idx = align_up(L.off_key + (size_t)Q * L.n_chunks * L.region_cap * 4, 256);

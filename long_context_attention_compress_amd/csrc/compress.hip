@@ -61,6 +61,32 @@ __device__ void store_kv_row(const KvView &s, int b, int64_t row, const float *n
     }
 }
 
+// Encode one pooled indexer value held by this lane (dimension d) into the
+// indexer store; every lane of the wave calls it (MX blocks are 32 lanes).
+__device__ __forceinline__ void store_ik_value(const IkView &s, int b, int64_t entry, int d, bool on, float x) {
+    const int lane = lane_id();
+    if (s.fmt == 0) {
+        if (on) ((float *)(s.f32 + b * s.f32_bs + entry * s.f32_rs))[d] = x;
+        return;
+    }
+    // MX block of 32 = one half of the wave
+    bool bad = !__builtin_isfinite(x) && on;
+    float a = on ? amax_acc(0.0f, x) : 0.0f;
+    a = half_max(a);
+    int nbad = __builtin_popcountll(__ballot(bad) & ((lane < 32) ? 0xFFFFFFFFull : 0xFFFFFFFF00000000ull));
+    uint32_t code = 0;
+    int E = 0;
+    if (nbad == 0) {
+        E = mx_exponent(a);
+        code = e2m1_encode(__builtin_ldexpf(x, -E));
+    }
+    uint32_t nb = __shfl_down(code, 1, 64);
+    if (on && (lane & 1) == 0)
+        ((uint8_t *)(s.e2m1 + b * s.e2m1_bs + entry * s.e2m1_rs))[d >> 1] = (uint8_t)(code | (nb << 4));
+    if (on && (lane & 31) == 0)
+        ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[d >> 5] = nbad ? 0xFF : (uint8_t)(E + 127);
+}
+
 template <int ACT>
 __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
     __shared__ double alpha[MAX_M];
@@ -139,35 +165,137 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
             double acc = 0.0;
             if (on)
                 for (int r = 0; r < m; ++r) acc += alpha[r] * load_act<ACT>(p.raw_ik, rowbase + (int64_t)r * dI + d);
-            float x = (float)acc;
-            if (s.fmt == 0) {
-                if (on) ((float *)(s.f32 + b * s.f32_bs + entry * s.f32_rs))[d] = x;
-                continue;
-            }
-            // MX block of 32 = one half of the wave
-            bool bad = !__builtin_isfinite(x) && on;
-            float a = on ? amax_acc(0.0f, x) : 0.0f;
-            a = half_max(a);
-            int nbad = __builtin_popcountll(__ballot(bad) & ((lane < 32) ? 0xFFFFFFFFull : 0xFFFFFFFF00000000ull));
-            uint32_t code = 0;
-            int E = 0;
-            if (nbad == 0) {
-                E = mx_exponent(a);
-                code = e2m1_encode(__builtin_ldexpf(x, -E));
-            }
-            uint32_t nb = __shfl_down(code, 1, 64);
-            if (on && (lane & 1) == 0)
-                ((uint8_t *)(s.e2m1 + b * s.e2m1_bs + entry * s.e2m1_rs))[d >> 1] = (uint8_t)(code | (nb << 4));
-            if (on && (lane & 31) == 0)
-                ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[d >> 5] = nbad ? 0xFF : (uint8_t)(E + 127);
+            store_ik_value(s, b, entry, d, on, (float)acc);
         }
+    }
+}
+
+// Blocks of at most SMALL_M tokens (the per-token window append, the CSA
+// block): every global load is issued before any arithmetic, so one memory
+// round trip precedes the encode, and each lane evaluates the gate softmax
+// itself. Same float64 arithmetic as the general kernel.
+constexpr int SMALL_M = 4;
+
+template <int ACT>
+__device__ __forceinline__ float load_val(const void *base, int64_t i) {
+    if (ACT == 0) return ((const float *)base)[i];
+    return bf16_decode(((const uint16_t *)base)[i]);
+}
+
+template <int ACT, int M>
+__global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
+    const int lane = lane_id();
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int64_t tok0 = (int64_t)j * M;
+    const int64_t entry = p.pos0 / M + j;
+    const bool do_kv = p.has_kv && (p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring);
+    const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
+    const int dI = p.dI;
+    const bool rl = lane < ROPE_PAIRS;
+    double z[M];
+    float kn[M][4], vn[M][4], kx[M], ky[M], vx[M], vy[M], ui[M][4];
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        const int64_t t = (int64_t)b * p.t_new + tok0 + r;
+        z[r] = (double)p.gate[t] + (double)p.pos_bias[r];
+        const int64_t row = t * D;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool on = do_kv && i < nit;
+            kn[r][i] = on ? load_val<ACT>(p.raw_k, row + lane + 64 * i) : 0.f;
+            vn[r][i] = on ? load_val<ACT>(p.raw_v, row + lane + 64 * i) : 0.f;
+        }
+        const bool ron = do_kv && rl;
+        kx[r] = ron ? load_val<ACT>(p.raw_k, row + Dn + 2 * lane) : 0.f;
+        ky[r] = ron ? load_val<ACT>(p.raw_k, row + Dn + 2 * lane + 1) : 0.f;
+        vx[r] = ron ? load_val<ACT>(p.raw_v, row + Dn + 2 * lane) : 0.f;
+        vy[r] = ron ? load_val<ACT>(p.raw_v, row + Dn + 2 * lane + 1) : 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool on = p.has_ik && lane + 64 * i < dI;
+            ui[r][i] = on ? load_val<ACT>(p.raw_ik, t * dI + lane + 64 * i) : 0.f;
+        }
+    }
+    // alpha_r = softmax_r(gate + pos_bias), float64
+    double zmax = z[0];
+#pragma unroll
+    for (int r = 1; r < M; ++r) zmax = z[r] > zmax ? z[r] : zmax;
+    double e[M], zsum = 0.0;
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+        e[r] = exp(z[r] - zmax);
+        zsum += e[r];
+    }
+    double alpha[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) alpha[r] = e[r] / zsum;
+
+    if (do_kv) {
+        float nk[4], nv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            double ak = 0.0, av = 0.0;
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                ak += alpha[r] * (double)kn[r][i];
+                av += alpha[r] * (double)vn[r][i];
+            }
+            nk[i] = (float)ak;
+            nv[i] = (float)av;
+        }
+        float rkx = 0.f, rky = 0.f, rvx = 0.f, rvy = 0.f;
+        if (rl) {
+            const double f = p.inv_freq[lane];
+            double akx = 0.0, aky = 0.0, avx = 0.0, avy = 0.0;
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                double sn, cs;
+                rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                const double x = kx[r], y = ky[r];
+                akx += alpha[r] * (x * cs - y * sn);
+                aky += alpha[r] * (x * sn + y * cs);
+                avx += alpha[r] * (double)vx[r];
+                avy += alpha[r] * (double)vy[r];
+            }
+            rkx = (float)akx;
+            rky = (float)aky;
+            rvx = (float)avx;
+            rvy = (float)avy;
+        }
+        store_kv_row(p.k, b, kv_row(p.k, entry), nk, nit, rkx, rky);
+        store_kv_row(p.v, b, kv_row(p.v, entry), nv, nit, rvx, rvy);
+    }
+    if (p.has_ik) {
+        const int nit_i = (dI + 63) / 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (i >= nit_i) break;
+            double acc = 0.0;
+#pragma unroll
+            for (int r = 0; r < M; ++r) acc += alpha[r] * (double)ui[r][i];
+            const int d = lane + 64 * i;
+            store_ik_value(p.ik, b, entry, d, d < dI, (float)acc);
+        }
+    }
+}
+
+template <int ACT>
+static void launch_small(const CompressPlan &p, dim3 grid, hipStream_t s) {
+    switch (p.m) {
+        case 1: hipLaunchKernelGGL((compress_small_kernel<ACT, 1>), grid, dim3(64), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((compress_small_kernel<ACT, 2>), grid, dim3(64), 0, s, p); break;
+        case 3: hipLaunchKernelGGL((compress_small_kernel<ACT, 3>), grid, dim3(64), 0, s, p); break;
+        default: hipLaunchKernelGGL((compress_small_kernel<ACT, 4>), grid, dim3(64), 0, s, p); break;
     }
 }
 
 hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
     dim3 grid(p.t_new / p.m, p.B);
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, grid, dim3(64), 0, s, p);
+    if (p.m <= SMALL_M) {
+        if (p.act == 0) launch_small<0>(p, grid, s);
+        else launch_small<1>(p, grid, s);
+    } else if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, grid, dim3(64), 0, s, p);
     else hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(64), 0, s, p);
     return hipGetLastError();
 }

@@ -31,7 +31,8 @@
 
 namespace v4a {
 
-constexpr int IT = 256;  // threads per workgroup (4 waves)
+constexpr int IT = 256;   // threads of a scoring workgroup (4 waves)
+constexpr int MT = 1024;  // threads of the merge workgroup (16 waves)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -39,7 +40,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 struct IdxSmem {
     uint32_t hist[256];
-    uint32_t scan[IT / 64 + 1];
+    uint32_t scan[MT / 64 + 1];
     int misc[8];
 };
 
@@ -64,7 +65,8 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
-// Inclusive prefix sum over the workgroup in thread order; *total gets the sum.
+// Inclusive prefix sum over the workgroup (NT threads) in thread order; *total gets the sum.
+template <int NT>
 __device__ uint32_t block_scan(uint32_t v, IdxSmem &sm, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const uint32_t x = wave_inclusive_scan(v);
@@ -74,7 +76,7 @@ __device__ uint32_t block_scan(uint32_t v, IdxSmem &sm, uint32_t *total) {
     __syncthreads();
     uint32_t before = 0, all = 0;
 #pragma unroll
-    for (int w = 0; w < IT / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         uint32_t t = sm.scan[w];
         before += (w < wave) ? t : 0u;
         all += t;
@@ -84,13 +86,15 @@ __device__ uint32_t block_scan(uint32_t v, IdxSmem &sm, uint32_t *total) {
 }
 
 // Largest bin b with sum(hist[b..255]) >= need. Returns b; *above = sum(hist[b+1..255]).
+template <int NT>
 __device__ int find_bin(IdxSmem &sm, uint32_t need, uint32_t *above) {
     const int tid = threadIdx.x;
+    const uint32_t h = tid < 256 ? sm.hist[255 - tid] : 0u;  // thread t: bin 255-t
     uint32_t total;
-    uint32_t suf = block_scan(sm.hist[255 - tid], sm, &total);  // thread t: bins 255-t .. 255
-    uint32_t excl = suf - sm.hist[255 - tid];
+    uint32_t suf = block_scan<NT>(h, sm, &total);
+    uint32_t excl = suf - h;
     __syncthreads();
-    if (suf >= need && excl < need) {
+    if (tid < 256 && suf >= need && excl < need) {
         sm.misc[0] = 255 - tid;
         sm.misc[1] = (int)excl;
     }
@@ -103,14 +107,6 @@ __device__ int find_bin(IdxSmem &sm, uint32_t need, uint32_t *above) {
 
 // ------------------------------------------------------------- scoring ----
 
-// max(0, x) as one VALU op (IEEE maxNum: a quiet-NaN x gives 0). The compiler's
-// fmaxf would first canonicalise x, doubling the epilogue's VALU work.
-__device__ __forceinline__ float relu1(float x) {
-    float r;
-    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));
-    return r;
-}
-
 // Sum over the four 16-lane rows holding the same key column, on the VALU
 // (gfx950 lane-swap instructions instead of LDS-routed shuffles).
 __device__ __forceinline__ float sum_rows(float s) {
@@ -120,9 +116,15 @@ __device__ __forceinline__ float sum_rows(float s) {
     return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
-template <int NT>
+// sum_h w_h max(0, d_h) over this lane's heads. The exact form pays a
+// canonicalisation per max (fmaxf semantics: NaN -> 0). The fast form uses
+// w_h max(0, d) = (w_h / 2)(d + |d|): one add with an abs modifier instead,
+// bitwise equal to the exact form whenever d + |d| cannot overflow, no d is
+// NaN and w_h / 2 is exact; the caller guarantees that from the scale bytes
+// (hw holds w / 2).
+template <int NT, bool FAST>
 __device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const v4i &kv, uint32_t sB,
-                                          const float (&wv)[4][4]) {
+                                          const float (&wv)[4][4], const float (&hw)[4][4]) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
     const v8i B = {kv[0], kv[1], kv[2], kv[3], 0, 0, 0, 0};
     v4f acc[4];
@@ -134,17 +136,21 @@ __device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const 
 #pragma unroll
     for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s = __builtin_fmaf(wv[i][j], relu1(acc[i][j]), s);
+        for (int j = 0; j < 4; ++j) {
+            if (FAST) s = __builtin_fmaf(hw[i][j], acc[i][j] + __builtin_fabsf(acc[i][j]), s);
+            else s = __builtin_fmaf(wv[i][j], __builtin_fmaxf(acc[i][j], 0.0f), s);
+        }
     return s;
 }
 
-constexpr int MX_BATCH = 4;  // key tiles per wave per batch; two batches are in flight
+constexpr int MX_BATCH = 4;  // key tiles per wave per batch (scoring kernel); two batches are in flight
 
 // Scores of entries [c0, c0+cnt) -> skey[0..cnt) (order-preserving keys).
-// Wave w takes tiles w, w+4, w+8, ...; each lane loads one 16-byte quarter of
-// one key row per tile, addressed as a uniform base plus a 32-bit offset, and
-// the next batch's loads are issued before the current batch is consumed.
-template <int NT>
+// With NW waves, wave w takes tiles w, w+NW, w+2NW, ...; each lane loads one
+// 16-byte quarter of one key row per tile, addressed as a uniform base plus a
+// 32-bit offset, and the next batch's loads are issued before the current
+// batch is consumed.
+template <int NT, int NW, int BATCH, bool FASTOK>
 __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int cnt, uint32_t *skey) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -152,8 +158,9 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
     const uint8_t *iqs = p.iq_scale + (size_t)q * p.H * 4;
     const float *w = p.w + (size_t)q * p.H;
     v8i A[4];
-    uint32_t sA = 0;
-    float wv[4][4];
+    uint32_t sA = 0, qmax = 0, qnan = 0;
+    float wv[4][4], hw[4][4], wmax = 0.f;
+    bool wsub = false;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         v4i v = {0, 0, 0, 0};
@@ -164,31 +171,52 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
         }
         A[i] = (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
         sA |= sc << (8 * i);
+        qmax = sc > qmax ? sc : qmax;
+        qnan |= sc == 0xFFu;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wv[i][j] = (i < NT) ? w[16 * i + 4 * grp + j] : 0.f;
+        for (int j = 0; j < 4; ++j) {
+            wv[i][j] = (i < NT) ? w[16 * i + 4 * grp + j] : 0.f;
+            hw[i][j] = 0.5f * wv[i][j];
+            const float a = __builtin_fabsf(wv[i][j]);
+            wmax = (a > wmax || a != a) ? a : wmax;
+            wsub |= a != 0.f && a < 0x1p-125f;
+        }
     }
+    // The fast form is exact for a tile when every key scale byte stays below
+    // `lim`: |d| < 2^(12.2 + ea + eb) for 128 E2M1 products with block
+    // exponents ea, eb, and the 64-head sum of |w| 2|d| stays below 2^127 if
+    // ea + eb + 20.2 + wexp < 127. A NaN query scale, a subnormal or
+    // non-finite weight sends every tile to the exact form.
+    qmax = wave_max(qmax);
+    wmax = wave_amax(wmax);
+    const bool all_exact = __ballot(qnan != 0 || wsub) != 0;
+    const int wexp = (int)((__float_as_uint(wmax) >> 23) & 0xFFu) - 127;
+    int lim = 361 - wexp - (int)qmax;
+    if (all_exact || lim < 0) lim = 0;
     const char *kbase = p.keys.e2m1 + (int64_t)b * p.keys.e2m1_bs + c0 * p.keys.e2m1_rs;
     const char *sbase = p.keys.e8m0 + (int64_t)b * p.keys.e8m0_bs + c0 * p.keys.e8m0_rs;
     const uint32_t krs = (uint32_t)p.keys.e2m1_rs, srs = (uint32_t)p.keys.e8m0_rs;
     const int ntiles = (cnt + 15) >> 4;
-    constexpr int STRIDE = 4 * MX_BATCH;  // tiles per batch over the 4 waves
-    v4i ka[MX_BATCH], kb[MX_BATCH];
-    uint32_t sa[MX_BATCH], sb[MX_BATCH];
-    auto issue = [&](v4i (&kv)[MX_BATCH], uint32_t (&sv)[MX_BATCH], int t0) {
+    constexpr int STRIDE = NW * BATCH;  // tiles per batch over the NW waves
+    v4i ka[BATCH], kb[BATCH];
+    uint32_t sa[BATCH], sb[BATCH];
+    auto issue = [&](v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], int t0) {
 #pragma unroll
-        for (int u = 0; u < MX_BATCH; ++u) {
-            int r = (t0 + 4 * u) * 16 + col;
+        for (int u = 0; u < BATCH; ++u) {
+            int r = (t0 + NW * u) * 16 + col;
             r = r < cnt ? r : cnt - 1;  // tail lanes reload the last valid row; masked below
             kv[u] = __builtin_nontemporal_load((const v4i *)(kbase + (uint32_t)r * krs + 16 * grp));
             sv[u] = (uint8_t)__builtin_nontemporal_load(sbase + (uint32_t)r * srs + grp);
         }
     };
-    auto consume = [&](const v4i (&kv)[MX_BATCH], const uint32_t (&sv)[MX_BATCH], int t0) {
+    auto consume = [&](const v4i (&kv)[BATCH], const uint32_t (&sv)[BATCH], int t0) {
 #pragma unroll
-        for (int u = 0; u < MX_BATCH; ++u) {
-            const int tile = t0 + 4 * u;
+        for (int u = 0; u < BATCH; ++u) {
+            const int tile = t0 + NW * u;
             if (tile >= ntiles) break;
-            const float s = sum_rows(head_sum<NT>(A, sA, kv[u], sv[u], wv));
+            float s;
+            if (FASTOK && __ballot((int)sv[u] >= lim) == 0) s = sum_rows(head_sum<NT, true>(A, sA, kv[u], sv[u], wv, hw));
+            else s = sum_rows(head_sum<NT, false>(A, sA, kv[u], sv[u], wv, hw));
             const int r = tile * 16 + col;
             if (grp == 0 && r < cnt) skey[r] = score_key(s);
         }
@@ -207,11 +235,12 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
 constexpr int F32_MAX_H = 16;
 
 // float32 keys: one entry per thread, dot products in float64.
+template <int NTH>
 __device__ void score_chunk_f32(const IndexPlan &p, int q, int b, int64_t c0, int cnt, uint32_t *skey,
                                 const float *sq) {
     const int H = p.H, dI = p.dI;
     const float *w = p.w + (size_t)q * H;
-    for (int r = threadIdx.x; r < cnt; r += IT) {
+    for (int r = threadIdx.x; r < cnt; r += NTH) {
         const float *key = (const float *)(p.keys.f32 + (int64_t)b * p.keys.f32_bs + (c0 + r) * p.keys.f32_rs);
         double acc[F32_MAX_H];
 #pragma unroll
@@ -237,11 +266,13 @@ __device__ void score_chunk_f32(const IndexPlan &p, int q, int b, int64_t c0, in
     }
 }
 
-template <int MODE>  // 0: f32 keys, 1..4: MXFP4 with MODE head tiles
+// MODE 0: f32 keys, 1..4: MXFP4 with MODE head tiles; NTH threads; BATCH MX tiles per wave and
+// batch; FASTOK: tiles may take the fast ReLU form
+template <int MODE, int NTH, int BATCH = MX_BATCH, bool FASTOK = true>
 __device__ __forceinline__ void score_chunk(const IndexPlan &p, int q, int b, int64_t c0, int cnt, uint32_t *skey,
                                             const float *sq) {
-    if (MODE == 0) score_chunk_f32(p, q, b, c0, cnt, skey, sq);
-    else score_chunk_mx<MODE>(p, q, b, c0, cnt, skey);
+    if (MODE == 0) score_chunk_f32<NTH>(p, q, b, c0, cnt, skey, sq);
+    else score_chunk_mx<MODE, NTH / 64, BATCH, FASTOK>(p, q, b, c0, cnt, skey);
 }
 
 // ---------------------------------------------------- chunk candidates ----
@@ -258,14 +289,14 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
         for (int i = tid; i < cnt; i += IT) atomicAdd(&sm.hist[skey[i] >> 24], 1u);
         __syncthreads();
         uint32_t above1;
-        const int b1 = find_bin(sm, (uint32_t)s_want, &above1);
+        const int b1 = find_bin<IT>(sm, (uint32_t)s_want, &above1);
         for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
         __syncthreads();
         for (int i = tid; i < cnt; i += IT)
             if ((int)(skey[i] >> 24) == b1) atomicAdd(&sm.hist[(skey[i] >> 16) & 255u], 1u);
         __syncthreads();
         uint32_t above2;
-        const int b2 = find_bin(sm, (uint32_t)s_want - above1, &above2);
+        const int b2 = find_bin<IT>(sm, (uint32_t)s_want - above1, &above2);
         thr = ((uint32_t)b1 << 24) | ((uint32_t)b2 << 16);
     }
     // compaction in index order: thread t owns entries [t*per, t*per + per)
@@ -274,7 +305,7 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
     uint32_t mine = 0;
     for (int i = lo; i < lo + per && i < cnt; ++i) mine += skey[i] >= thr;
     uint32_t total;
-    uint32_t off = block_scan(mine, sm, &total) - mine;
+    uint32_t off = block_scan<IT>(mine, sm, &total) - mine;
     uint32_t *meta = p.meta + rid * 2;
     if (total > (uint32_t)p.region_cap) {
         if (tid == 0) {
@@ -300,27 +331,28 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
 
 // ------------------------------------------------------------- merge ----
 
-constexpr int REG_CAND = 32;  // candidates a merge thread holds in registers
+constexpr int REG_CAND = 8;  // candidates a merge thread holds in registers
+constexpr int GROUP = 4;     // merge threads sharing one chunk's region (32 slots)
 
-template <int MODE>
+template <int MODE, int NT>
 __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, int kk, uint32_t *skey,
                                const float *sq, IdxSmem &sm) {
     // Radix select over every visible entry, rescoring chunk by chunk.
     const int tid = threadIdx.x;
     uint32_t prefix = 0, mask = 0, need = (uint32_t)kk;
     for (int d = 3; d >= 0; --d) {
-        for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
+        for (int i = tid; i < 256; i += NT) sm.hist[i] = 0;
         __syncthreads();
         for (int64_t c0 = 0; c0 < nvis; c0 += p.chunk) {
             const int cnt = (int)((nvis - c0) < p.chunk ? (nvis - c0) : p.chunk);
-            score_chunk<MODE>(p, q, b, c0, cnt, skey, sq);
+            if (threadIdx.x < IT) score_chunk<MODE, IT, 1, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
             __syncthreads();
-            for (int i = tid; i < cnt; i += IT)
+            for (int i = tid; i < cnt; i += NT)
                 if ((skey[i] & mask) == prefix) atomicAdd(&sm.hist[(skey[i] >> (8 * d)) & 255u], 1u);
             __syncthreads();
         }
         uint32_t above;
-        const int bin = find_bin(sm, need, &above);
+        const int bin = find_bin<NT>(sm, need, &above);
         need -= above;
         prefix |= (uint32_t)bin << (8 * d);
         mask |= 255u << (8 * d);
@@ -329,16 +361,16 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
     float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
     uint32_t written = 0, ties = 0;
-    const int per = (p.chunk + IT - 1) / IT;
+    const int per = (p.chunk + NT - 1) / NT;
     for (int64_t c0 = 0; c0 < nvis; c0 += p.chunk) {
         const int cnt = (int)((nvis - c0) < p.chunk ? (nvis - c0) : p.chunk);
-        score_chunk<MODE>(p, q, b, c0, cnt, skey, sq);
+        if (threadIdx.x < IT) score_chunk<MODE, IT, 1, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
         __syncthreads();
         const int lo = threadIdx.x * per;
         uint32_t nt = 0;
         for (int i = lo; i < lo + per && i < cnt; ++i) nt += skey[i] == prefix;
         uint32_t tot_t;
-        uint32_t tie_before = ties + block_scan(nt, sm, &tot_t) - nt;
+        uint32_t tie_before = ties + block_scan<NT>(nt, sm, &tot_t) - nt;
         uint32_t ns = 0;
         {
             uint32_t tb = tie_before;
@@ -348,7 +380,7 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
             }
         }
         uint32_t tot_s;
-        uint32_t pos = written + block_scan(ns, sm, &tot_s) - ns;
+        uint32_t pos = written + block_scan<NT>(ns, sm, &tot_s) - ns;
         {
             uint32_t tb = tie_before;
             for (int i = lo; i < lo + per && i < cnt; ++i) {
@@ -365,7 +397,7 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
         ties += tot_t;
         __syncthreads();
     }
-    for (int i = kk + tid; i < p.k; i += IT) {
+    for (int i = kk + tid; i < p.k; i += NT) {
         oidx[i] = -1;
         if (osc) osc[i] = 0.f;
     }
@@ -399,7 +431,7 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
         }
         return;
     }
-    score_chunk<MODE>(p, q, b, c0, cnt, skey, sq);
+    score_chunk<MODE, IT>(p, q, b, c0, cnt, skey, sq);
     __syncthreads();
     // every full chunk keeps enough that the union holds at least kk entries
     const int64_t n_active = (nvis + p.chunk - 1) / p.chunk;
@@ -411,72 +443,210 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
     chunk_emit(p, q, chunk, c0, cnt, s_want, skey, sm);
 }
 
-// One workgroup per query. The chunks' candidates are taken in chunk order
-// (ascending entry ids) and split into equal contiguous runs, one per thread,
-// held in registers; a 4 x 8-bit radix select finds the k-th key.
-template <int MODE>
-__global__ __launch_bounds__(IT) void index_merge_kernel(IndexPlan p) {
-    extern __shared__ uint32_t dyn[];
-    __shared__ IdxSmem sm;
-    const int q = blockIdx.x, tid = threadIdx.x;
-    const int b = q / p.Tq;
-    uint32_t *pre = dyn;                                  // [n_chunks + 1] candidate offsets
-    uint32_t *skey = dyn + p.n_chunks + 1;                // [chunk] (exact fallback)
-    float *sq = (float *)(skey + p.chunk);                // f32 mode query
-    if (MODE == 0) {
-        const float *iq = (const float *)p.iq + (size_t)q * p.H * p.dI;
-        for (int i = tid; i < p.H * p.dI; i += IT) sq[i] = iq[i];
+// ------------------------------------------------------ merge select ----
+
+constexpr int MBITS = 11;                 // radix digit of the merge select
+constexpr int MBINS = 1 << MBITS;
+constexpr int RESOLVE_MAX = 64;           // a boundary bin this small is ranked by one wave
+constexpr int BPT = MBINS / MT;         // histogram bins per merge thread
+static_assert(BPT == 2, "each merge thread scans two bins");
+
+// Per-key loops are kept free of branches: a key that does not count goes
+// to a dummy slot of its lane (the arrays carry 64 extra slots).
+struct __attribute__((aligned(16))) MergeSmem {
+    uint32_t hist[MBINS + 64];
+    uint32_t part[2][MT / 64];  // wave totals of block scans (two buffers, used in turn)
+    uint32_t red[3][MT / 64];
+    uint32_t list[RESOLVE_MAX + 64] __attribute__((aligned(16)));
+    uint32_t misc[4];
+    uint32_t stage_key[MBINS + 64];  // selected keys, staged for coalesced output
+};
+
+// Inclusive prefix sum over the workgroup. Consecutive calls must alternate
+// `buf`; the barrier of one call then protects the other buffer.
+__device__ __forceinline__ uint32_t scan_buf(uint32_t v, MergeSmem &sm, int buf, uint32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t x = wave_inclusive_scan(v);
+    if (lane == 63) sm.part[buf][wave] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < MT / 64; ++w) {
+        const uint32_t t = sm.part[buf][w];
+        before += (w < wave) ? t : 0u;
+        all += t;
     }
-    const int64_t nvis = visible_entries(p, q);
-    const int kk = (int)(nvis < p.k ? nvis : p.k);
+    *total = all;
+    return x + before;
+}
+
+// Highest bin whose suffix count reaches `need`: its index, the count above
+// it, its own count and the count over all bins. Thread t covers bins
+// [MBINS - BPT(t+1), MBINS - BPT t) and zeroes them for the next pass.
+__device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf, uint32_t *bin, uint32_t *above,
+                                           uint32_t *in_bin, uint32_t *total) {
+    const int b0 = MBINS - BPT * (threadIdx.x + 1);
+    const uint2 hv = *(const uint2 *)&sm.hist[b0];
+    const uint32_t h[BPT] = {hv.x, hv.y};
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) local += h[j];
+    const uint32_t incl = scan_buf(local, sm, buf, total);
+    uint32_t acc = incl - local;
+    if (acc < need && incl >= need) {
+#pragma unroll
+        for (int j = BPT - 1; j >= 0; --j) {
+            if (acc + h[j] >= need) {
+                sm.misc[0] = (uint32_t)(b0 + j);
+                sm.misc[1] = acc;
+                sm.misc[2] = h[j];
+                break;
+            }
+            acc += h[j];
+        }
+    }
+    *(uint2 *)&sm.hist[b0] = make_uint2(0, 0);
+    __syncthreads();
+    *bin = sm.misc[0];
+    *above = sm.misc[1];
+    *in_bin = sm.misc[2];
+}
+
+// Max over the wave on the VALU: row rotations, then the lane-swap
+// instructions across rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    uint32_t y;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
+    x = y > x ? y : x;
+    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = a[0] > a[1] ? a[0] : a[1];
+    auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return c[0] > c[1] ? c[0] : c[1];
+}
+
+// Marks the key registers as rewritten (no instruction is emitted), so that
+// per-key tests are not hoisted out of the select loop into 32 live masks.
+__device__ __forceinline__ void fence_keys(uint32_t (&k)[REG_CAND]) {
+#pragma unroll
+    for (int i = 0; i < REG_CAND; ++i) asm volatile("" : "+v"(k[i]));
+}
+
+// One workgroup per query. Each thread holds a contiguous run of the chunks'
+// candidates (in ascending id order) in registers: a quarter of its chunk's
+// region when every chunk fits in 32 slots, else an equal share of the
+// flattened list.
+//
+// Every chunk emitted all of its entries at or above its lower bound, so with
+// T_lo = the largest lower bound, the candidates at or above T_lo are exactly
+// the entries at or above T_lo. If at least k of them exist, the k-th key
+// lies there and the candidates decide the selection exactly; otherwise the
+// exact fallback runs. The k-th key is found by radix passes of MBITS-bit
+// digits over [T_lo, max key], starting at the highest bit where the two
+// differ; once the boundary bin holds at most RESOLVE_MAX keys they are
+// gathered and ranked directly.
+//
+// Registers hold key + 1 (keys never reach 2^32 - 1: NaN maps to 0), so an
+// empty slot is 0 and falls below every bound without a validity mask.
+//
+// merge_select is the candidate select; false when the exact fallback has to
+// decide instead.
+__device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, uint32_t *pre, IdxSmem &sm,
+                                             MergeSmem &ms) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
     float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
-    if (kk == 0) {
-        for (int i = tid; i < p.k; i += IT) {
-            oidx[i] = -1;
-            if (osc) osc[i] = 0.f;
-        }
-        return;
-    }
     const uint32_t *meta = p.meta + (size_t)q * p.n_chunks * 2;
-    // exclusive prefix of candidate counts over chunks
-    int bad = 0;
-    uint32_t carry = 0;
-    for (int c0 = 0; c0 < p.n_chunks; c0 += IT) {
-        const int c = c0 + tid;
-        uint32_t n = c < p.n_chunks ? meta[2 * c] : 0u;
-        if (n == 0xFFFFFFFFu) {
-            bad = 1;
-            n = 0;
-        }
-        uint32_t tot;
-        const uint32_t inc = block_scan(n, sm, &tot);
-        if (c < p.n_chunks) pre[c] = carry + inc - n;
-        carry += tot;
-        __syncthreads();
-    }
-    if (tid == 0) pre[p.n_chunks] = carry;
-    const uint32_t total = carry;
-    const uint32_t per = (total + IT - 1) / IT;
-    __syncthreads();
-    if (__syncthreads_or(bad) || per > REG_CAND) {
-        exact_fallback<MODE>(p, q, b, nvis, kk, skey, sq, sm);
-        return;
-    }
+
     uint32_t keys[REG_CAND];
     int32_t ids[REG_CAND];
-    int mine;
-    if (p.n_chunks <= IT && __syncthreads_and(tid >= p.n_chunks || pre[tid + 1] - pre[tid] <= REG_CAND)) {
-        // one chunk per thread: its whole region, in order
-        mine = tid < p.n_chunks ? (int)(pre[tid + 1] - pre[tid]) : 0;
-        const size_t base = ((size_t)q * p.n_chunks + tid) * p.region_cap;
+    int mine = 0;
+    uint32_t t_lo = 1;  // largest chunk lower bound (+1) seen by this thread
+    int over = 0, big = 1;
+    if (p.n_chunks * GROUP <= MT) {
+        // region mode: the region load is issued together with the count
+        const int c = tid / GROUP, sub = tid % GROUP;
+        uint32_t cnt = 0;
+        if (c < p.n_chunks) {
+            const uint2 mt = *(const uint2 *)(meta + 2 * c);
+            cnt = mt.x;
+            t_lo = mt.y + 1u;
+            const size_t base = ((size_t)q * p.n_chunks + c) * p.region_cap + sub * REG_CAND;
+            const uint4 *rk = (const uint4 *)(p.reg_key + base);
+            const uint4 *ri = (const uint4 *)(p.reg_idx + base);
 #pragma unroll
-        for (int i = 0; i < REG_CAND; ++i) {
-            keys[i] = i < mine ? p.reg_key[base + i] : 0u;
-            ids[i] = i < mine ? p.reg_idx[base + i] : -1;
+            for (int v = 0; v < REG_CAND / 4; ++v) {
+                const uint4 kx = rk[v], ix = ri[v];
+                keys[4 * v + 0] = kx.x; keys[4 * v + 1] = kx.y; keys[4 * v + 2] = kx.z; keys[4 * v + 3] = kx.w;
+                ids[4 * v + 0] = (int32_t)ix.x; ids[4 * v + 1] = (int32_t)ix.y;
+                ids[4 * v + 2] = (int32_t)ix.z; ids[4 * v + 3] = (int32_t)ix.w;
+            }
         }
-    } else {
-        // equal contiguous runs [lo, hi) of the flattened candidate list
+        over = cnt == 0xFFFFFFFFu;
+        big = !over && cnt > (uint32_t)(GROUP * REG_CAND);
+        const int rest = over ? 0 : (int)cnt - sub * REG_CAND;
+        mine = rest < 0 ? 0 : (rest > REG_CAND ? REG_CAND : rest);
+#pragma unroll
+        for (int i = 0; i < REG_CAND; ++i) keys[i] = i < mine ? keys[i] + 1u : 0u;
+    }
+    // range of the candidates and the flags, in one workgroup round
+    uint32_t kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < REG_CAND; ++i) kmax = keys[i] > kmax ? keys[i] : kmax;
+    kmax = wave_max_u32(kmax);
+    t_lo = wave_max_u32(t_lo);
+    const bool w_over = __ballot(over) != 0, w_big = __ballot(big) != 0;
+    if (lane == 0) {
+        ms.red[0][wave] = kmax;
+        ms.red[1][wave] = t_lo;
+        ms.red[2][wave] = (w_over ? 1u : 0u) | (w_big ? 2u : 0u);
+    }
+    __syncthreads();
+    uint32_t flags = 0;
+#pragma unroll
+    for (int w = 0; w < MT / 64; ++w) {
+        kmax = ms.red[0][w] > kmax ? ms.red[0][w] : kmax;
+        t_lo = ms.red[1][w] > t_lo ? ms.red[1][w] : t_lo;
+        flags |= ms.red[2][w];
+    }
+    if (flags & 1u) {
+        return false;
+    }
+    if (flags & 2u) {
+        // general mode: exclusive prefix of candidate counts, then equal runs
+        int bad = 0;
+        uint32_t carry = 0, tl = 1;
+        for (int c0 = 0; c0 < p.n_chunks; c0 += MT) {
+            const int c = c0 + tid;
+            uint32_t n = 0;
+            if (c < p.n_chunks) {
+                n = meta[2 * c];
+                const uint32_t th = meta[2 * c + 1] + 1u;
+                tl = th > tl ? th : tl;
+            }
+            if (n == 0xFFFFFFFFu) {
+                bad = 1;
+                n = 0;
+            }
+            uint32_t tot;
+            const uint32_t inc = block_scan<MT>(n, sm, &tot);
+            if (c < p.n_chunks) pre[c] = carry + inc - n;
+            carry += tot;
+            __syncthreads();
+        }
+        if (tid == 0) pre[p.n_chunks] = carry;
+        const uint32_t total = carry;
+        const uint32_t per = (total + MT - 1) / MT;
+        __syncthreads();
+        if (__syncthreads_or(bad) || per > REG_CAND) {
+            return false;
+        }
         const uint32_t lo = min(total, tid * per), hi = min(total, lo + per);
         int c = 0;
         {
@@ -488,6 +658,7 @@ __global__ __launch_bounds__(IT) void index_merge_kernel(IndexPlan p) {
             }
             c = l;
         }
+        uint32_t km = 0u;
 #pragma unroll
         for (int i = 0; i < REG_CAND; ++i) {
             keys[i] = 0u;
@@ -496,83 +667,216 @@ __global__ __launch_bounds__(IT) void index_merge_kernel(IndexPlan p) {
             if (f < hi) {
                 while (pre[c + 1] <= f) ++c;
                 const size_t slot = ((size_t)q * p.n_chunks + c) * p.region_cap + (f - pre[c]);
-                keys[i] = p.reg_key[slot];
+                keys[i] = p.reg_key[slot] + 1u;
                 ids[i] = p.reg_idx[slot];
+                km = keys[i] > km ? keys[i] : km;
             }
         }
         mine = (int)(hi - lo);
-    }
-    // radix select of the kk-th largest key
-    uint32_t prefix = 0, mask = 0, need = (uint32_t)kk;
-    for (int d = 3; d >= 0; --d) {
-        for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
+        km = wave_max_u32(km);
+        tl = wave_max_u32(tl);
+        if (lane == 0) {
+            ms.red[0][wave] = km;
+            ms.red[1][wave] = tl;
+        }
         __syncthreads();
-        const int sh = 8 * d;
-        // runs of equal bins are counted in a register first: the candidates
-        // cluster in few bins, and same-address LDS atomics serialise
-        uint32_t run_bin = 0xFFFFFFFFu, run = 0;
+        kmax = 0u;
+        t_lo = 1u;
+#pragma unroll
+        for (int w = 0; w < MT / 64; ++w) {
+            kmax = ms.red[0][w] > kmax ? ms.red[0][w] : kmax;
+            t_lo = ms.red[1][w] > t_lo ? ms.red[1][w] : t_lo;
+        }
+    }
+    if (kmax < t_lo) return false;  // no candidate at or above T_lo
+    // candidates below T_lo never decide anything: empty their slots
+#pragma unroll
+    for (int i = 0; i < REG_CAND; ++i) keys[i] = keys[i] >= t_lo ? keys[i] : 0u;
+
+    // k-th key (kth) and how many keys equal to it are taken (need_ties)
+    uint32_t need = (uint32_t)kk, kth = kmax, need_ties = need;
+    uint32_t hi_bits = kmax;  // bits at and above `top` are settled
+    const uint32_t diff = kmax ^ t_lo;
+    int top = diff ? 32 - __builtin_clz(diff) : 0;
+    int buf = 0;
+    bool first = true;
+    for (;;) {
+        if (top == 0) {
+            // every remaining key equals hi_bits; on the first pass count them
+            if (first) {
+                uint32_t n = 0;
+#pragma unroll
+                for (int i = 0; i < REG_CAND; ++i) n += keys[i] == kmax;
+                uint32_t tot;
+                scan_buf(n, ms, buf, &tot);
+                if (tot < need) {
+                    return false;
+                }
+                buf ^= 1;
+            }
+            kth = hi_bits;
+            need_ties = need;
+            break;
+        }
+        fence_keys(keys);
+        const int s = top > MBITS ? top - MBITS : 0;
+        const uint32_t mhi = top >= 32 ? 0u : (0xFFFFFFFFu << top);
+        const uint32_t dmask = (1u << (top - s)) - 1u;
+        if (!first) __syncthreads();  // the bins were zeroed by their owners
 #pragma unroll
         for (int i = 0; i < REG_CAND; ++i) {
-            if (i < mine && (keys[i] & mask) == prefix) {
-                const uint32_t bin = (keys[i] >> sh) & 255u;
-                if (bin != run_bin) {
-                    if (run) atomicAdd(&sm.hist[run_bin], run);
-                    run_bin = bin;
-                    run = 0;
-                }
-                ++run;
-            }
+            const bool in = (keys[i] & mhi) == (hi_bits & mhi) && keys[i] != 0u;
+            atomicAdd(&ms.hist[in ? (keys[i] >> s) & dmask : MBINS + lane], 1u);
         }
-        if (run) atomicAdd(&sm.hist[run_bin], run);
         __syncthreads();
-        uint32_t above;
-        const int bin = find_bin(sm, need, &above);
+        uint32_t bin, above, in_bin, total;
+        merge_find(ms, need, buf, &bin, &above, &in_bin, &total);
+        buf ^= 1;
+        if (first && total < need) {  // the k-th key lies below T_lo
+            return false;
+        }
+        first = false;
         need -= above;
-        prefix |= (uint32_t)bin << sh;
-        mask |= 255u << sh;
+        hi_bits = (hi_bits & mhi) | (bin << s);
+        top = s;
+        if (top == 0) {
+            kth = hi_bits;
+            need_ties = need;
+            break;
+        }
+        if (in_bin <= (uint32_t)RESOLVE_MAX) {
+            // gather the bin into LDS (slots by a workgroup prefix sum) ...
+            fence_keys(keys);
+            const uint32_t m2 = 0xFFFFFFFFu << top;
+            uint32_t n = 0;
+#pragma unroll
+            for (int i = 0; i < REG_CAND; ++i) n += (keys[i] & m2) == hi_bits && keys[i] != 0u;
+            uint32_t tot;
+            uint32_t slot = scan_buf(n, ms, buf, &tot) - n;
+            buf ^= 1;
+            fence_keys(keys);
+#pragma unroll
+            for (int i = 0; i < REG_CAND; ++i) {
+                const bool in = (keys[i] & m2) == hi_bits && keys[i] != 0u;
+                ms.list[in ? slot : RESOLVE_MAX + lane] = keys[i];
+                slot += in;
+            }
+            __syncthreads();
+            // ... and rank it: PARTS threads share an element, each comparing
+            // it with RESOLVE_MAX / PARTS list entries
+            constexpr int PARTS = MT / RESOLVE_MAX;
+            const int e = tid / PARTS, part = tid % PARTS;
+            const uint32_t mk = ms.list[e];
+            uint32_t gt = 0, ge = 0;
+#pragma unroll
+            for (int j = 0; j < RESOLVE_MAX / PARTS; ++j) {
+                const int o = part * (RESOLVE_MAX / PARTS) + j;
+                const uint32_t ok = ms.list[o];
+                const bool in = (uint32_t)o < in_bin;
+                gt += in && ok > mk;
+                ge += in && ok >= mk;
+            }
+#pragma unroll
+            for (int off = 1; off < PARTS; off <<= 1) {
+                gt += __shfl_xor(gt, off, 64);
+                ge += __shfl_xor(ge, off, 64);
+            }
+            // every element equal to the k-th key writes the same pair
+            if (part == 0 && (uint32_t)e < in_bin && gt < need && need <= ge) {
+                ms.misc[0] = mk;
+                ms.misc[1] = need - gt;
+            }
+            __syncthreads();
+            kth = ms.misc[0];
+            need_ties = ms.misc[1];
+            break;
+        }
     }
-    const uint32_t kth = prefix;
-    // a chunk whose emitted lower bound lies above the k-th key may have withheld winners
-    int sat = 0;
-    for (int cc = tid; cc < p.n_chunks; cc += IT) sat |= meta[2 * cc + 1] > kth;
-    if (__syncthreads_or(sat)) {
-        exact_fallback<MODE>(p, q, b, nvis, kk, skey, sq, sm);
-        return;
-    }
-    // keys > kth, and the first `need` keys == kth in id order
-    uint32_t nt = 0, ngt = 0;
+
+    fence_keys(keys);
+    // keys > kth, and the first need_ties keys == kth in id order; one scan of
+    // (greater << 16 | equal) gives both offsets (each total is below 2^16)
+    uint32_t ngt = 0, neq = 0;
 #pragma unroll
     for (int i = 0; i < REG_CAND; ++i) {
-        nt += (i < mine) && keys[i] == kth;
-        ngt += (i < mine) && keys[i] > kth;
+        ngt += keys[i] > kth;
+        neq += keys[i] == kth;
     }
+    const uint32_t packed = (ngt << 16) | neq;
     uint32_t tot;
-    uint32_t tb = block_scan(nt, sm, &tot) - nt;
-    const uint32_t ntake = ngt + (tb < need ? min(nt, need - tb) : 0u);
-    uint32_t pos = block_scan(ntake, sm, &tot) - ntake;
+    const uint32_t ex = scan_buf(packed, ms, buf, &tot) - packed;
+    fence_keys(keys);
+    uint32_t tb = ex & 0xFFFFu;
+    uint32_t pos = (ex >> 16) + (tb < need_ties ? tb : need_ties);
+    // up to MBINS selections are staged in LDS (ids in the free histogram)
+    // and written out in order by consecutive lanes
+    const bool stage = kk <= MBINS;
+    uint32_t *st_id = ms.hist;
+    if (stage) {
 #pragma unroll
-    for (int i = 0; i < REG_CAND; ++i) {
-        if (i < mine) {
+        for (int i = 0; i < REG_CAND; ++i) {
+            const bool eq = keys[i] == kth;
+            const bool take = keys[i] > kth || (eq && tb < need_ties);
+            tb += eq;
+            const uint32_t a = take ? pos : MBINS + lane;
+            st_id[a] = (uint32_t)ids[i];
+            ms.stage_key[a] = keys[i];
+            pos += take;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < REG_CAND; ++i) {
             bool take = keys[i] > kth;
-            if (keys[i] == kth) take = (tb++ < need);
+            if (keys[i] == kth) take = (tb++ < need_ties);
             if (take) {
                 oidx[pos] = ids[i];
-                if (osc) osc[pos] = key_score(keys[i]);
+                if (osc) osc[pos] = key_score(keys[i] - 1u);
                 ++pos;
             }
         }
     }
-    for (int i = kk + tid; i < p.k; i += IT) {
+    if (stage) {
+        __syncthreads();
+        for (int i = tid; i < kk; i += MT) {
+            oidx[i] = (int32_t)st_id[i];
+            if (osc) osc[i] = key_score(ms.stage_key[i] - 1u);
+        }
+    }
+    return true;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(MT) void index_merge_kernel(IndexPlan p) {
+    extern __shared__ uint32_t dyn[];
+    __shared__ IdxSmem sm;
+    __shared__ MergeSmem ms;
+    const int q = blockIdx.x, tid = threadIdx.x;
+    const int b = q / p.Tq;
+    uint32_t *pre = dyn;                                  // [n_chunks + 1] candidate offsets
+    uint32_t *skey = dyn + p.n_chunks + 1;                // [chunk] (exact fallback)
+    float *sq = (float *)(skey + p.chunk);                // f32 mode query
+    *(uint2 *)&ms.hist[BPT * tid] = make_uint2(0, 0);
+    if (MODE == 0) {
+        const float *iq = (const float *)p.iq + (size_t)q * p.H * p.dI;
+        for (int i = tid; i < p.H * p.dI; i += MT) sq[i] = iq[i];
+    }
+    const int64_t nvis = visible_entries(p, q);
+    const int kk = (int)(nvis < p.k ? nvis : p.k);
+    int32_t *oidx = p.out_idx + (size_t)q * p.k;
+    float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
+    for (int i = kk + tid; i < p.k; i += MT) {
         oidx[i] = -1;
         if (osc) osc[i] = 0.f;
     }
+    if (kk == 0) return;
+    if (!merge_select(p, q, kk, pre, sm, ms)) exact_fallback<MODE, MT>(p, q, b, nvis, kk, skey, sq, sm);
 }
 
 template <int MODE>
 static void launch_mode(const IndexPlan &p, hipStream_t s) {
     const size_t q_lds = MODE == 0 ? (size_t)p.H * p.dI * 4 : 0;
     hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, p.Q), dim3(IT), (size_t)p.chunk * 4 + q_lds, s, p);
-    hipLaunchKernelGGL(index_merge_kernel<MODE>, dim3(p.Q), dim3(IT),
+    hipLaunchKernelGGL(index_merge_kernel<MODE>, dim3(p.Q), dim3(MT),
                        (size_t)(p.n_chunks + 1 + p.chunk) * 4 + q_lds, s, p);
 }
 
