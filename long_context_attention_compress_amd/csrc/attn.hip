@@ -226,9 +226,9 @@ constexpr int MAX_KS = 2048;    // keys per split (their store rows are resolved
 struct MxSmem {
     __bf16 kb[TK * KB_LD];      // K tile, row-major BF16
     __bf16 vb[TK * KB_LD];      // V tile, row-major BF16 (read transposed by ds_read_b64_tr_b16)
-    float ksc[TK];
-    float vsc[TK];
-    int kval[TK];
+    float ksc[TK] __attribute__((aligned(16)));  // K row scale of each key (0 for an empty slot)
+    float kbias[TK] __attribute__((aligned(16)));  // 0, or -inf for an empty slot
+    float vsc[TK] __attribute__((aligned(16)));
     double rcos[ROPE_PAIRS];
     double rsin[ROPE_PAIRS];
     int32_t rows[MAX_KS];       // row of each key of the split; bit 30 marks a window row; -1: no key
@@ -236,19 +236,48 @@ struct MxSmem {
 
 constexpr int32_t WIN_BIT = 1 << 30;
 
+// A tile in flight: the raw loads and which of them hold a key. Slots without
+// a key are zeroed only when the tile is staged, so that issuing the next
+// tile's loads never waits for this one's data.
 struct TileRegs {
     v4i k[2], v[2];
     float sc;
+    bool ok[2], sok;
 };
+
+// One batch element's planes of one store, with their row strides. Built
+// once per workgroup from the (uniform) plan, so that choosing between the
+// entry and the window store per lane is a register select and never a load
+// of the plan's fields through a per-lane address.
+struct Planes {
+    const char *nope, *rope, *scale;
+    int64_t nope_rs, rope_rs, scale_rs;
+};
+__device__ __forceinline__ Planes planes_of(const KvView &s, int b) {
+    Planes r;
+    r.nope = s.nope + b * s.nope_bs;
+    r.rope = s.rope + b * s.rope_bs;
+    r.scale = s.scale + b * s.scale_bs;
+    r.nope_rs = s.nope_rs;
+    r.rope_rs = s.rope_rs;
+    r.scale_rs = s.scale_rs;
+    return r;
+}
+struct TileSrc {
+    Planes ek, ev, wk, wv;
+};
+
+template <typename T>
+__device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
 
 // Issue the loads of one 32-key tile. Branch-free: a slot without a key reads
 // row 0 of the window store (always present) and is zeroed afterwards, so the
 // compiler keeps every load of the tile in flight together.
-__device__ __forceinline__ void load_tile(const AttnPlan &p, int b, const MxSmem &sm, int rel, int n_rel,
-                                          TileRegs &R) {
+__device__ __forceinline__ void load_tile(const TileSrc &S, const MxSmem &sm, int rel, int n_rel, TileRegs &R) {
     const int tid = threadIdx.x;
     const int part = tid & 15;
     const int64_t koff = part < 8 ? 16 * part : 16 * (part - 8);
+    const bool nope = part < 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 16 * h;
@@ -256,15 +285,13 @@ __device__ __forceinline__ void load_tile(const AttnPlan &p, int b, const MxSmem
         const bool ok = code >= 0;
         const bool win = !ok || (code & WIN_BIT);
         const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
-        const KvView &K = win ? p.wk : p.ek;
-        const KvView &V = win ? p.wv : p.ev;
-        const char *kb = part < 8 ? K.nope + b * K.nope_bs + row * K.nope_rs : K.rope + b * K.rope_bs + row * K.rope_rs;
-        const char *vb = part < 8 ? V.nope + b * V.nope_bs + row * V.nope_rs : V.rope + b * V.rope_bs + row * V.rope_rs;
-        const v4i kx = __builtin_nontemporal_load((const v4i *)(kb + koff));
-        const v4i vx = __builtin_nontemporal_load((const v4i *)(vb + koff));
-        const v4i z = {0, 0, 0, 0};
-        R.k[h] = ok ? kx : z;
-        R.v[h] = ok ? vx : z;
+        const char *kb = pick(win, pick(nope, S.wk.nope, S.wk.rope), pick(nope, S.ek.nope, S.ek.rope));
+        const int64_t krs = pick(win, pick(nope, S.wk.nope_rs, S.wk.rope_rs), pick(nope, S.ek.nope_rs, S.ek.rope_rs));
+        const char *vb = pick(win, pick(nope, S.wv.nope, S.wv.rope), pick(nope, S.ev.nope, S.ev.rope));
+        const int64_t vrs = pick(win, pick(nope, S.wv.nope_rs, S.wv.rope_rs), pick(nope, S.ev.nope_rs, S.ev.rope_rs));
+        R.k[h] = __builtin_nontemporal_load((const v4i *)(kb + row * krs + koff));
+        R.v[h] = __builtin_nontemporal_load((const v4i *)(vb + row * vrs + koff));
+        R.ok[h] = ok;
     }
     // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
     const int r = tid & (TK - 1);
@@ -272,9 +299,11 @@ __device__ __forceinline__ void load_tile(const AttnPlan &p, int b, const MxSmem
     const bool ok = code >= 0;
     const bool win = !ok || (code & WIN_BIT);
     const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
-    const KvView &S = (tid < TK) ? (win ? p.wk : p.ek) : (win ? p.wv : p.ev);
-    const float sc = *(const float *)(S.scale + b * S.scale_bs + row * S.scale_rs);
-    R.sc = ok ? sc : 0.f;
+    const bool isk = tid < TK;
+    const char *sb = pick(isk, pick(win, S.wk.scale, S.ek.scale), pick(win, S.wv.scale, S.ev.scale));
+    const int64_t srs = pick(isk, pick(win, S.wk.scale_rs, S.ek.scale_rs), pick(win, S.wv.scale_rs, S.ev.scale_rs));
+    R.sc = *(const float *)(sb + row * srs);
+    R.sok = ok;
 }
 
 template <bool HI>
@@ -301,22 +330,25 @@ __device__ __forceinline__ void store_codes(__bf16 *dst, const v4i &c) {
 __device__ __forceinline__ void stage_tile(const TileRegs &R, const int *valid_rows, MxSmem &sm, int rel, int n_rel) {
     const int tid = threadIdx.x;
     const int part = tid & 15;
+    const v4i z = {0, 0, 0, 0};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 16 * h;
+        const v4i kx = R.ok[h] ? R.k[h] : z, vx = R.ok[h] ? R.v[h] : z;
         if (part < 8) {
-            store_codes(&sm.kb[r * KB_LD + 16 * part], R.k[h]);
-            store_codes(&sm.vb[r * KB_LD + 16 * part], R.v[h]);
+            store_codes(&sm.kb[r * KB_LD + 16 * part], kx);
+            store_codes(&sm.vb[r * KB_LD + 16 * part], vx);
         } else {
-            *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * (part - 8)] = R.k[h];
-            *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * (part - 8)] = R.v[h];
+            *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * (part - 8)] = kx;
+            *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * (part - 8)] = vx;
         }
     }
+    const float sc = R.sok ? R.sc : 0.f;
     if (tid < TK) {
-        sm.ksc[tid] = R.sc;
-        sm.kval[tid] = rel + tid < n_rel && sm.rows[rel + tid] >= 0;
+        sm.ksc[tid] = sc;
+        sm.kbias[tid] = (rel + tid < n_rel && sm.rows[rel + tid] >= 0) ? 0.f : -__builtin_inff();
     } else if (tid < 2 * TK) {
-        sm.vsc[tid - TK] = R.sc;
+        sm.vsc[tid - TK] = sc;
     }
     (void)valid_rows;
 }
@@ -364,55 +396,75 @@ __device__ __forceinline__ float swap32_sum(float x) {
 constexpr float RESCALE_SLACK = 8.0f;
 
 template <int NW>
-__global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
+__global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
     __shared__ MxSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, g = lane >> 4;
     const int q = blockIdx.y, split = blockIdx.x;
     const int b = q / p.Tq;
-    const KeyInfo ki = key_info(p, q);
     const int H = p.H;
     const bool active = wave < NW;
     const int head = 16 * wave + col;
 
-    const int64_t n_keys = ki.n_list + ki.n_win;
+    // The query and (sparse) this split's selected ids do not depend on the
+    // query position: their loads are issued before the position arrives.
+    const __bf16 *qp = (const __bf16 *)p.q + ((size_t)q * H + (active ? head : 0)) * MD;
+    bf16x8 qn[4], qraw[2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qn[c] = ld16(qp + 32 * c + 8 * g);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) qraw[c] = ld16(qp + MDN + 32 * c + 8 * g);
+    constexpr int IDS = MAX_KS / AT;
     const int64_t j0 = (int64_t)split * p.keys_per_split;
+    int32_t ids[IDS];
+#pragma unroll
+    for (int u = 0; u < IDS; ++u) {
+        const int i = tid + AT * u;
+        ids[u] = (p.sparse && i < p.keys_per_split && j0 + i < p.k) ? p.idx[(size_t)q * p.k + j0 + i] : -1;
+    }
+    const KeyInfo ki = key_info(p, q);
+    const int64_t n_keys = ki.n_list + ki.n_win;
     const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
     const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
-    // resolve the split's keys to store rows once (coalesced id loads), and the RoPE table
-    for (int i = tid; i < n_rel; i += AT) {
-        bool win;
-        const int64_t row = key_row(p, q, ki, j0 + i, &win);
-        sm.rows[i] = row < 0 ? -1 : (int32_t)row | (win ? WIN_BIT : 0);
+    // resolve the split's keys to store rows once, and the RoPE table
+#pragma unroll
+    for (int u = 0; u < IDS; ++u) {
+        const int i = tid + AT * u;
+        if (i < n_rel) {
+            const int64_t j = j0 + i;
+            int64_t row;
+            bool win = false;
+            if (j < ki.n_list) {
+                const int64_t e = p.sparse ? (int64_t)ids[u] : j;
+                row = (e >= 0 && e < p.ek.rows) ? e : -1;
+            } else {
+                row = key_row(p, q, ki, j, &win);
+            }
+            sm.rows[i] = row < 0 ? -1 : (int32_t)row | (win ? WIN_BIT : 0);
+        }
     }
     if (tid < ROPE_PAIRS) rope_sincos((double)ki.t * p.inv_freq[tid], &sm.rsin[tid], &sm.rcos[tid]);
     __syncthreads();
 
     // query operands (B of S^T = K Q^T): head `col` of this wave, dims 32c + 8g .. +8
-    bf16x8 qn[4], qrh[2], qrl[2];
-    {
-        const int hh = active ? head : 0;
-        const __bf16 *qp = (const __bf16 *)p.q + ((size_t)q * H + hh) * MD;
+    bf16x8 qrh[2], qrl[2];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) qn[c] = ld16(qp + 32 * c + 8 * g);
+    for (int c = 0; c < 2; ++c) {
+        const bf16x8 raw = qraw[c];
+        bf16x8 hi, lo;
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            bf16x8 raw = ld16(qp + MDN + 32 * c + 8 * g);
-            bf16x8 hi, lo;
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                const int pr = (32 * c + 8 * g + i) >> 1;
-                const double sn = sm.rsin[pr], cs = sm.rcos[pr];
-                const double x = (double)(float)raw[i], y = (double)(float)raw[i + 1];
-                const float rx = (float)(x * cs - y * sn), ry = (float)(x * sn + y * cs);
-                hi[i] = (__bf16)rx;
-                hi[i + 1] = (__bf16)ry;
-                lo[i] = (__bf16)(rx - (float)hi[i]);
-                lo[i + 1] = (__bf16)(ry - (float)hi[i + 1]);
-            }
-            qrh[c] = hi;
-            qrl[c] = lo;
+        for (int i = 0; i < 8; i += 2) {
+            const int pr = (32 * c + 8 * g + i) >> 1;
+            const double sn = sm.rsin[pr], cs = sm.rcos[pr];
+            const double x = (double)(float)raw[i], y = (double)(float)raw[i + 1];
+            const float rx = (float)(x * cs - y * sn), ry = (float)(x * sn + y * cs);
+            hi[i] = (__bf16)rx;
+            hi[i + 1] = (__bf16)ry;
+            lo[i] = (__bf16)(rx - (float)hi[i]);
+            lo[i + 1] = (__bf16)(ry - (float)hi[i + 1]);
         }
+        qrh[c] = hi;
+        qrl[c] = lo;
     }
     const float sc2 = p.sm_scale * 1.4426950408889634f;
     float mrun = -__builtin_inff(), lrun = 0.f;
@@ -421,87 +473,108 @@ __global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
     for (int i = 0; i < 12; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-    // two-stage pipeline: tile i+2 is loaded while tile i is staged and computed
+    // two-stage pipeline: tile t+2 is loaded while tile t is staged and computed
     const int n_tiles = (n_rel + TK - 1) / TK;
-    TileRegs RA, RB;
-    if (n_tiles > 0) load_tile(p, b, sm, 0, n_rel, RA);
-    if (n_tiles > 1) load_tile(p, b, sm, TK, n_rel, RB);
-    for (int t = 0; t < n_tiles; ++t) {
-        __syncthreads();
-        if (t & 1) {
-            stage_tile(RB, nullptr, sm, t * TK, n_rel);
-            if (t + 2 < n_tiles) load_tile(p, b, sm, (t + 2) * TK, n_rel, RB);
-        } else {
-            stage_tile(RA, nullptr, sm, t * TK, n_rel);
-            if (t + 2 < n_tiles) load_tile(p, b, sm, (t + 2) * TK, n_rel, RA);
+    TileSrc src;
+    src.wk = planes_of(p.wk, b);
+    src.wv = planes_of(p.wv, b);
+    src.ek = p.has_ent ? planes_of(p.ek, b) : src.wk;
+    src.ev = p.has_ent ? planes_of(p.ev, b) : src.wv;
+    // Every tile load is issued unconditionally (a tile past the end reads
+    // window row 0 and is never staged), and the loop is unrolled by two, so
+    // the wait before staging tile t only covers tile t's loads and tile t+1's
+    // stay in flight.
+    auto compute = [&]() {
+        if (!active) return;
+        // per-key scales of this lane's eight keys (4g..4g+3 and 16+4g..), read as vectors
+        v4f ks[2], kb[2], vs[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            ks[st] = *(const v4f *)&sm.ksc[16 * st + 4 * g];
+            kb[st] = *(const v4f *)&sm.kbias[16 * st + 4 * g];
+            vs[st] = *(const v4f *)&sm.vsc[16 * st + 4 * g];
         }
-        __syncthreads();
-        if (active) {
-            float s[2][4];
+        // the two key halves as independent MFMA chains
+        v4f an[2] = {zero, zero}, ar[2] = {zero, zero};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+                an[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    ld16(&sm.kb[(16 * st + col) * KB_LD + 8 * g + 32 * c]), qn[c], an[st], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                v4f an = zero, ar = zero;
-                const __bf16 *krow = &sm.kb[(16 * st + col) * KB_LD + 8 * g];
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    an = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ld16(krow + 32 * c), qn[c], an, 0, 0, 0);
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    bf16x8 a = ld16(krow + MDN + 32 * c);
-                    ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrh[c], ar, 0, 0, 0);
-                    ar = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrl[c], ar, 0, 0, 0);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = 16 * st + 4 * g + j;
-                    s[st][j] = sm.kval[key] ? (an[j] * sm.ksc[key] + ar[j]) * sc2 : -__builtin_inff();
-                }
+                const bf16x8 a = ld16(&sm.kb[(16 * st + col) * KB_LD + 8 * g + MDN + 32 * c]);
+                ar[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrh[c], ar[st], 0, 0, 0);
+                ar[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrl[c], ar[st], 0, 0, 0);
             }
-            float mx = s[0][0];
+        // an empty slot has a zero K row and bias -inf
+        float s[2][4];
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, s[st][j]);
-            mx = swap32_max(swap16_max(mx));
-            // raise the running max (and rescale) only when this tile exceeds it by the slack
-            if (__builtin_amdgcn_ballot_w64(mx > mrun + RESCALE_SLACK)) {
-                const float mn = __builtin_fmaxf(mrun, mx);
-                const float c = mn == -__builtin_inff() ? 1.f : exp2f(mrun - mn);
-                lrun *= c;
+            for (int j = 0; j < 4; ++j) s[st][j] = (an[st][j] * ks[st][j] + ar[st][j]) * sc2 + kb[st][j];
+        float mx = s[0][0];
 #pragma unroll
-                for (int i = 0; i < 12; ++i) O[i] *= c;
-                mrun = mn;
-            }
-            float pr[2][4], psum = 0.f;
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int j = 0; j < 4; ++j) mx = __builtin_fmaxf(mx, s[st][j]);
+        mx = swap32_max(swap16_max(mx));
+        // raise the running max (and rescale) only when this tile exceeds it by the slack
+        if (__builtin_amdgcn_ballot_w64(mx > mrun + RESCALE_SLACK)) {
+            const float mn = __builtin_fmaxf(mrun, mx);
+            const float c = mn == -__builtin_inff() ? 1.f : exp2f(mrun - mn);
+            lrun *= c;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    pr[st][j] = s[st][j] == -__builtin_inff() ? 0.f : exp2f(s[st][j] - mrun);
-                    psum += pr[st][j];
-                }
-            lrun += swap32_sum(swap16_sum(psum));
-            // P as two BF16 terms (hi + lo): one BF16 alone would cost 2^-9 of the
-            // largest output element, which outliers in V turn into a visible error.
-            bf16x8 pnh, pnl, pbh, pbl;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int key = 16 * st + 4 * g + j;
-                    const float xn = pr[st][j] * sm.vsc[key], xb = pr[st][j];
-                    pnh[4 * st + j] = (__bf16)xn;
-                    pnl[4 * st + j] = (__bf16)(xn - (float)pnh[4 * st + j]);
-                    pbh[4 * st + j] = (__bf16)xb;
-                    pbl[4 * st + j] = (__bf16)(xb - (float)pbh[4 * st + j]);
-                }
-#pragma unroll
-            for (int dt = 0; dt < 12; ++dt) {
-                const bf16x8 a = vt_operand(sm, dt, g, col);
-                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnh : pbh, O[dt], 0, 0, 0);
-                O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnl : pbl, O[dt], 0, 0, 0);
-            }
+            for (int i = 0; i < 12; ++i) O[i] *= c;
+            mrun = mn;
         }
+        float pr[2][4], psum = 0.f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pr[st][j] = s[st][j] == -__builtin_inff() ? 0.f : exp2f(s[st][j] - mrun);
+                psum += pr[st][j];
+            }
+        lrun += swap32_sum(swap16_sum(psum));
+        // P as two BF16 terms (hi + lo): one BF16 alone would cost 2^-9 of the
+        // largest output element, which outliers in V turn into a visible error.
+        bf16x8 pnh, pnl, pbh, pbl;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float xn = pr[st][j] * vs[st][j], xb = pr[st][j];
+                pnh[4 * st + j] = (__bf16)xn;
+                pnl[4 * st + j] = (__bf16)(xn - (float)pnh[4 * st + j]);
+                pbh[4 * st + j] = (__bf16)xb;
+                pbl[4 * st + j] = (__bf16)(xb - (float)pbh[4 * st + j]);
+            }
+#pragma unroll
+        for (int dt = 0; dt < 12; ++dt) {
+            const bf16x8 a = vt_operand(sm, dt, g, col);
+            O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnh : pbh, O[dt], 0, 0, 0);
+            O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnl : pbl, O[dt], 0, 0, 0);
+        }
+    };
+    TileRegs RA, RB;
+    load_tile(src, sm, 0, n_rel, RA);
+    load_tile(src, sm, TK, n_rel, RB);
+    for (int t = 0; t < n_tiles; t += 2) {
+        __syncthreads();
+        stage_tile(RA, nullptr, sm, t * TK, n_rel);
+        load_tile(src, sm, (t + 2) * TK, n_rel, RA);
+        __syncthreads();
+        compute();
+        if (t + 1 >= n_tiles) break;
+        __syncthreads();
+        stage_tile(RB, nullptr, sm, (t + 1) * TK, n_rel);
+        load_tile(src, sm, (t + 3) * TK, n_rel, RB);
+        __syncthreads();
+        compute();
     }
     if (!active) return;
     // epilogue: lane holds O^T[16dt + 4g + j][head]
@@ -538,52 +611,89 @@ __global__ __launch_bounds__(AT) void attn_mx_kernel(AttnPlan p) {
 // -------------------------------------------------------------- combine ----
 
 constexpr int MAX_SPLIT = 1024;
+constexpr int CMB_G = 4;                 // threads sharing one output dim
+constexpr int CMB_T = CMB_G * 192;       // combine workgroup (dims up to 192)
+constexpr int CMB_CHUNK = 32;            // splits a combine thread loads at once
 
-// Merge the splits of one (query, head): the per-split weights exp2(m_s - M) / L
-// are computed once into LDS, then each thread sums its output dim over the
-// splits with independent loads.
+// Merge the splits of one (query, head). CMB_G threads share output dim d:
+// thread group gi takes splits gi, gi + CMB_G, ...; every partial output a
+// thread needs (up to CMB_CHUNK) is loaded before the split weights are known,
+// so one memory round trip covers the partials and the (max, sum) pairs. The
+// groups' sums are added in a fixed order (deterministic).
 template <int OUT_BF16>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnPlan p) {
+__global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
     __shared__ float wgt[MAX_SPLIT];
-    __shared__ float red[8];
+    __shared__ float red[2][CMB_T / 64];
+    __shared__ float part[CMB_G - 1][192];
     const int q = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int D = p.D, H = p.H, S = p.n_split;
+    const int d = tid % 192, gi = tid / 192;
     const size_t base = (size_t)q * S * H;
+    const size_t stride = (size_t)H * D;
+    const bool own = d < D;
+    const float *po = p.part_o + (base + h) * D + (own ? d : 0);
+    float v[CMB_CHUNK];
+#pragma unroll
+    for (int i = 0; i < CMB_CHUNK; ++i) {
+        const int sp = gi + CMB_G * i;
+        v[i] = (own && sp < S) ? po[(size_t)sp * stride] : 0.f;
+    }
+    float2 ml[2];
     float mloc = -__builtin_inff();
-    for (int s = tid; s < S; s += 256) {
-        const float m = p.part_ml[((base + (size_t)s * H) + h) * 2];
-        wgt[s] = m;
-        mloc = __builtin_fmaxf(mloc, m);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int sp = tid + CMB_T * k;
+        ml[k] = sp < S ? *(const float2 *)&p.part_ml[((base + (size_t)sp * H) + h) * 2]
+                       : make_float2(-__builtin_inff(), 0.f);
+        mloc = __builtin_fmaxf(mloc, ml[k].x);
     }
     mloc = wave_max(mloc);
-    if ((tid & 63) == 0) red[tid >> 6] = mloc;
+    if (lane == 0) red[0][wave] = mloc;
     __syncthreads();
-    const float M = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+    float M = red[0][0];
+#pragma unroll
+    for (int w = 1; w < CMB_T / 64; ++w) M = __builtin_fmaxf(M, red[0][w]);
     float lloc = 0.f;
-    for (int s = tid; s < S; s += 256) {
-        const float w = M == -__builtin_inff() ? 0.f : exp2f(wgt[s] - M);
-        wgt[s] = w;
-        lloc += w * p.part_ml[((base + (size_t)s * H) + h) * 2 + 1];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int sp = tid + CMB_T * k;
+        if (sp < S) {
+            const float w = M == -__builtin_inff() ? 0.f : exp2f(ml[k].x - M);
+            wgt[sp] = w;
+            lloc += w * ml[k].y;
+        }
     }
     lloc = wave_sum(lloc);
+    if (lane == 0) red[1][wave] = lloc;
     __syncthreads();
-    if ((tid & 63) == 0) red[4 + (tid >> 6)] = lloc;
-    __syncthreads();
-    const float L = (red[4] + red[5]) + (red[6] + red[7]);
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int d = tid; d < D; d += 256) {
-        const float *po = p.part_o + (base + h) * D + d;
-        const size_t stride = (size_t)H * D;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        int s = 0;
-        for (; s + 4 <= S; s += 4) {
-            a0 += po[(size_t)(s + 0) * stride] * wgt[s + 0];
-            a1 += po[(size_t)(s + 1) * stride] * wgt[s + 1];
-            a2 += po[(size_t)(s + 2) * stride] * wgt[s + 2];
-            a3 += po[(size_t)(s + 3) * stride] * wgt[s + 3];
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < CMB_T / 64; ++w) L += red[1][w];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < CMB_CHUNK; ++i) {
+        const int sp = gi + CMB_G * i;
+        if (sp < S) acc += v[i] * wgt[sp];
+    }
+    for (int s0 = CMB_G * CMB_CHUNK; s0 < S; s0 += CMB_G * CMB_CHUNK) {  // more than 128 splits
+#pragma unroll
+        for (int i = 0; i < CMB_CHUNK; ++i) {
+            const int sp = s0 + gi + CMB_G * i;
+            v[i] = (own && sp < S) ? po[(size_t)sp * stride] : 0.f;
         }
-        for (; s < S; ++s) a0 += po[(size_t)s * stride] * wgt[s];
-        const float o = ((a0 + a1) + (a2 + a3)) * inv;
+#pragma unroll
+        for (int i = 0; i < CMB_CHUNK; ++i) {
+            const int sp = s0 + gi + CMB_G * i;
+            if (sp < S) acc += v[i] * wgt[sp];
+        }
+    }
+    if (gi > 0) part[gi - 1][d] = acc;
+    __syncthreads();
+    if (gi == 0 && own) {
+#pragma unroll
+        for (int k = 0; k < CMB_G - 1; ++k) acc += part[k][d];
+        const float o = L > 0.f ? acc / L : 0.f;
         if (OUT_BF16) ((__bf16 *)p.o)[((size_t)q * H + h) * D + d] = (__bf16)o;
         else ((float *)p.o)[((size_t)q * H + h) * D + d] = o;
     }
@@ -606,8 +716,8 @@ hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
-    if (p.o_bf16) hipLaunchKernelGGL(attn_combine_kernel<1>, dim3(p.Q, p.H), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(attn_combine_kernel<0>, dim3(p.Q, p.H), dim3(256), 0, s, p);
+    if (p.o_bf16) hipLaunchKernelGGL(attn_combine_kernel<1>, dim3(p.Q, p.H), dim3(CMB_T), 0, s, p);
+    else hipLaunchKernelGGL(attn_combine_kernel<0>, dim3(p.Q, p.H), dim3(CMB_T), 0, s, p);
     return hipGetLastError();
 }
 

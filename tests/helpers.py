@@ -81,6 +81,7 @@ def assert_close_rms(got, ref, tol, what=''):
     err = np.abs(got - ref).max()
     assert np.all(np.isfinite(got)), f'{what}: non-finite output'
     assert err <= tol * rms, f'{what}: max err {err:.3e} > {tol} x RMS {rms:.3e} (ratio {err / rms:.3e})'
+    print(f'[close] {what}: max err / RMS = {err / rms:.3e} (tolerance {tol})', flush=True)
     return err / rms
 
 
