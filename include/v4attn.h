@@ -202,8 +202,10 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream);
  *          order as the store) with iq_scale [B][Tq][H_I][dim/32] E8M0;
  *          F32 keys: [B][Tq][H_I][dim] float32 (iq_scale unused).
  *  w       [B][Tq][H_I] float32 head weights.
- * Supported: F32 keys with dim % 4 == 0, dim <= 256, H_I <= 64; MXFP4 keys
- * with dim == 128 and H_I in {16, 32, 48, 64}. 1 <= k <= 4096.
+ * Supported: F32 keys with dim % 4 == 0, dim <= 256, H_I <= 16; MXFP4 keys
+ * with dim == 128 and H_I in {16, 32, 48, 64}, iq 16-byte aligned and the
+ * keys' e8m0 plane (pointer and strides) 4-byte aligned: each key's four
+ * exponents are read as one 32-bit word. 1 <= k <= 4096.
  * ---------------------------------------------------------------------- */
 typedef struct {
     int32_t B;

@@ -132,7 +132,7 @@ IndexLayout index_layout(const v4a_index_args *a) {
     IndexLayout L;
     const int64_t Q = (int64_t)a->B * a->Tq;
     const int64_t rows = a->keys->rows;
-    L.chunk = 1024;
+    L.chunk = IDX_CHUNK;
     L.n_chunks = (int)std::max<int64_t>(1, (rows + L.chunk - 1) / L.chunk);
     L.s_local = 2 * ((a->k + L.n_chunks - 1) / L.n_chunks) + 8;
     // a multiple of 4 slots and at least 32: the merge reads a region's first
@@ -156,6 +156,8 @@ int check_index(const v4a_index_args *a) {
         if (a->H_I <= 0 || a->H_I > 64 || a->H_I % 16) return fail(V4A_EFORMAT, "MXFP4 indexer needs H_I in {16,32,48,64}");
         if (!a->iq_scale) return fail(V4A_ENULL, "iq_scale is NULL");
         if (!aligned(a->iq, 16)) return fail(V4A_EALIGN, "iq must be 16-byte aligned");
+        if (!aligned(a->keys->e8m0.ptr, 4) || a->keys->e8m0.row_stride % 4 || a->keys->e8m0.batch_stride % 4)
+            return fail(V4A_EALIGN, "MXFP4 indexer keys: e8m0 pointer and strides must be 4-byte aligned");
     } else if (a->keys->fmt == V4A_IK_F32) {
         if (a->H_I <= 0 || a->H_I > 16) return fail(V4A_EFORMAT, "F32 indexer needs H_I in 1..16");
         if (!aligned(a->iq, 4)) return fail(V4A_EALIGN, "iq must be 4-byte aligned");

@@ -107,24 +107,52 @@ __device__ int find_bin(IdxSmem &sm, uint32_t need, uint32_t *above) {
 
 // ------------------------------------------------------------- scoring ----
 
-// Sum over the four 16-lane rows holding the same key column, on the VALU
-// (gfx950 lane-swap instructions instead of LDS-routed shuffles).
-__device__ __forceinline__ float sum_rows(float s) {
-    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    s = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+// Reduce-scatter over the four 16-lane rows: row g of the result holds, in
+// each column, the sum over all four rows of x[g] (on the VALU, with the
+// gfx950 lane-swap instructions). A 32-lane swap adds rows g and g + 2 of
+// x[0] / x[2] and of x[1] / x[3]; a 16-lane swap then adds rows 2j and 2j + 1.
+__device__ __forceinline__ float swap_add32(float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_add16(float a, float b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float scatter_rows(const float (&x)[4]) {
+    const float x02 = swap_add32(x[0], x[2]);  // rows 0, 1: x[0]; rows 2, 3: x[2] (two rows summed)
+    const float x13 = swap_add32(x[1], x[3]);
+    return swap_add16(x02, x13);               // row g: x[g] summed over the four rows
 }
 
-// sum_h w_h max(0, d_h) over this lane's heads. The exact form pays a
-// canonicalisation per max (fmaxf semantics: NaN -> 0). The fast form uses
-// w_h max(0, d) = (w_h / 2)(d + |d|): one add with an abs modifier instead,
-// bitwise equal to the exact form whenever d + |d| cannot overflow, no d is
-// NaN and w_h / 2 is exact; the caller guarantees that from the scale bytes
-// (hw holds w / 2).
+// Max over the wave on the VALU: row rotations, then the lane-swap
+// instructions across rows.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    uint32_t y;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
+    x = y > x ? y : x;
+    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = a[0] > a[1] ? a[0] : a[1];
+    auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return c[0] > c[1] ? c[0] : c[1];
+}
+
+// sum_h w_h max(0, d_h) over this lane's heads, as an fma chain. The exact
+// form takes max(0, d) with fmaxf semantics (a NaN d counts as 0), which the
+// compiler implements with a canonicalisation per value. The fast form takes
+// the max of the bit patterns as signed integers: one instruction, equal to
+// the exact form for every d that is not NaN (a negative value or -0 gives
+// +0, and +0 or -0 added to a chain that starts at +0 leaves it unchanged);
+// the caller sends a tile to it only when the scale bytes rule out a NaN d.
 template <int NT, bool FAST>
 __device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const v4i &kv, uint32_t sB,
-                                          const float (&wv)[4][4], const float (&hw)[4][4]) {
+                                          const float (&wv)[4][4]) {
     const v4f z = {0.f, 0.f, 0.f, 0.f};
     const v8i B = {kv[0], kv[1], kv[2], kv[3], 0, 0, 0, 0};
     v4f acc[4];
@@ -137,98 +165,167 @@ __device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const 
     for (int i = 0; i < NT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if (FAST) s = __builtin_fmaf(hw[i][j], acc[i][j] + __builtin_fabsf(acc[i][j]), s);
-            else s = __builtin_fmaf(wv[i][j], __builtin_fmaxf(acc[i][j], 0.0f), s);
+            const float r = FAST ? __int_as_float(__builtin_elementwise_max(__float_as_int(acc[i][j]), 0))
+                                 : __builtin_fmaxf(acc[i][j], 0.0f);
+            s = __builtin_fmaf(wv[i][j], r, s);
         }
     return s;
 }
 
-constexpr int MX_BATCH = 4;  // key tiles per wave per batch (scoring kernel); two batches are in flight
-
-// Scores of entries [c0, c0+cnt) -> skey[0..cnt) (order-preserving keys).
-// With NW waves, wave w takes tiles w, w+NW, w+2NW, ...; each lane loads one
-// 16-byte quarter of one key row per tile, addressed as a uniform base plus a
-// 32-bit offset, and the next batch's loads are issued before the current
-// batch is consumed.
-template <int NT, int NW, int BATCH, bool FASTOK>
+// Scores of entries [c0, c0+cnt) -> skey[0..IDX_CHUNK) (order-preserving
+// keys; slots at or past cnt hold the score of an all-zero key and are never
+// read). Wave w takes tiles w, w+NW, w+2NW, ... of 16 keys; a batch is four
+// of them, one per 16-lane row, and two batches are in flight. Each lane
+// loads one 16-byte quarter of one key row per tile through a buffer
+// resource that ends at the chunk's last row, so loads past the end return
+// zeros with no address clamping and no branch. After the per-lane head sums
+// of a batch, one reduce-scatter over the rows leaves lane (row g, column c)
+// with the score of key c of the batch's tile g: one score key and one LDS
+// store per lane per batch.
+template <int NT, bool FASTOK>
 __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int cnt, uint32_t *skey) {
+    constexpr int NW = IT / 64, BATCH = 4;
+    constexpr int STRIDE = NW * BATCH;               // tiles per batch over the NW waves
+    constexpr int NB = IDX_CHUNK / (16 * STRIDE);    // batches per wave
+    static_assert(NB * 16 * STRIDE == IDX_CHUNK && NB % 2 == 0, "a chunk is an even number of batches");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
+
+    // Issue order: the query's raw operands, then key batches 0 and 1; the
+    // query is first used after both batches are issued. The memory clobbers
+    // pin that order in the IR, the scheduling barriers in the machine
+    // scheduler, and the register fences keep every use of the query values
+    // (even their unpacking) behind the key loads.
     const uint8_t *iq = (const uint8_t *)p.iq + (size_t)q * p.H * 64;
     const uint8_t *iqs = p.iq_scale + (size_t)q * p.H * 4;
     const float *w = p.w + (size_t)q * p.H;
-    v8i A[4];
-    uint32_t sA = 0, qmax = 0, qnan = 0;
-    float wv[4][4], hw[4][4], wmax = 0.f;
-    bool wsub = false;
+    v4i qv[4];
+    uint32_t qsc[4];
+    float wv[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        v4i v = {0, 0, 0, 0};
-        uint32_t sc = 0;
+        qv[i] = (v4i){0, 0, 0, 0};
+        qsc[i] = 0;
         if (i < NT) {
-            v = *(const v4i *)(iq + (16 * i + col) * 64 + 16 * grp);
-            sc = iqs[(16 * i + col) * 4 + grp];
+            qv[i] = *(const v4i *)(iq + (16 * i + col) * 64 + 16 * grp);
+            qsc[i] = iqs[(16 * i + col) * 4 + grp];
         }
-        A[i] = (v8i){v[0], v[1], v[2], v[3], 0, 0, 0, 0};
-        sA |= sc << (8 * i);
-        qmax = sc > qmax ? sc : qmax;
-        qnan |= sc == 0xFFu;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            wv[i][j] = (i < NT) ? w[16 * i + 4 * grp + j] : 0.f;
-            hw[i][j] = 0.5f * wv[i][j];
-            const float a = __builtin_fabsf(wv[i][j]);
-            wmax = (a > wmax || a != a) ? a : wmax;
-            wsub |= a != 0.f && a < 0x1p-125f;
-        }
+        for (int j = 0; j < 4; ++j) wv[i][j] = (i < NT) ? w[16 * i + 4 * grp + j] : 0.f;
     }
-    // The fast form is exact for a tile when every key scale byte stays below
-    // `lim`: |d| < 2^(12.2 + ea + eb) for 128 E2M1 products with block
-    // exponents ea, eb, and the 64-head sum of |w| 2|d| stays below 2^127 if
-    // ea + eb + 20.2 + wexp < 127. A NaN query scale, a subnormal or
-    // non-finite weight sends every tile to the exact form.
-    qmax = wave_max(qmax);
-    wmax = wave_amax(wmax);
-    const bool all_exact = __ballot(qnan != 0 || wsub) != 0;
-    const int wexp = (int)((__float_as_uint(wmax) >> 23) & 0xFFu) - 127;
-    int lim = 361 - wexp - (int)qmax;
-    if (all_exact || lim < 0) lim = 0;
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     const char *kbase = p.keys.e2m1 + (int64_t)b * p.keys.e2m1_bs + c0 * p.keys.e2m1_rs;
     const char *sbase = p.keys.e8m0 + (int64_t)b * p.keys.e8m0_bs + c0 * p.keys.e8m0_rs;
     const uint32_t krs = (uint32_t)p.keys.e2m1_rs, srs = (uint32_t)p.keys.e8m0_rs;
-    const int ntiles = (cnt + 15) >> 4;
-    constexpr int STRIDE = NW * BATCH;  // tiles per batch over the NW waves
+    // byte ranges of the chunk's rows: the last row ends at (cnt - 1) * stride + row bytes
+    const uint32_t kbytes = (uint32_t)(cnt - 1) * krs + 64u, sbytes = (uint32_t)(cnt - 1) * srs + 4u;
+    const uint32_t kvo = (uint32_t)(wave * 16 + col) * krs + 16u * grp;  // this lane's quarter in tile `wave`
+    const uint32_t svo = (uint32_t)(wave * 16 + col) * srs;              // the row's four exponents (one word)
     v4i ka[BATCH], kb[BATCH];
     uint32_t sa[BATCH], sb[BATCH];
-    auto issue = [&](v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], int t0) {
+    auto issue = [&](v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], int bi) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            int r = (t0 + NW * u) * 16 + col;
-            r = r < cnt ? r : cnt - 1;  // tail lanes reload the last valid row; masked below
-            kv[u] = __builtin_nontemporal_load((const v4i *)(kbase + (uint32_t)r * krs + 16 * grp));
-            sv[u] = (uint8_t)__builtin_nontemporal_load(sbase + (uint32_t)r * srs + grp);
+            // the tile's offset is uniform: it moves the resource base (scalar work only)
+            const uint32_t t16 = (uint32_t)(STRIDE * bi + NW * u) * 16u;
+            const uint32_t ko = t16 * krs, so = t16 * srs;
+            const int nk = (int)kbytes - (int)ko, ns = (int)sbytes - (int)so;  // bytes left (max on the SALU)
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(kbase + ko), (short)0, __builtin_elementwise_max(nk, 0), 0x00020000);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(sbase + so), (short)0, __builtin_elementwise_max(ns, 0), 0x00020000);
+            kv[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, kvo, 0, 2);  // nontemporal
+            sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, svo, 0, 2);
         }
     };
-    auto consume = [&](const v4i (&kv)[BATCH], const uint32_t (&sv)[BATCH], int t0) {
+    issue(ka, sa, 0);
+    __builtin_amdgcn_sched_barrier(0);  // batch 0 (keys and exponents) wholly ahead of batch 1
+    issue(kb, sb, 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        asm volatile("" : "+v"(qv[i]), "+v"(qsc[i]));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) asm volatile("" : "+v"(wv[i][j]));
+    }
+
+    v8i A[4];
+    uint32_t sA = 0, qmax = 0, qnan = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        A[i] = (v8i){qv[i][0], qv[i][1], qv[i][2], qv[i][3], 0, 0, 0, 0};
+        sA |= qsc[i] << (8 * i);
+        qmax = qsc[i] > qmax ? qsc[i] : qmax;
+        qnan |= qsc[i] == 0xFFu;
+    }
+    // A tile takes the fast form when no d can be NaN: no scale byte is 0xFF
+    // (NaN) and nothing overflows. Each of the 128 products is at most
+    // 6 * 6 * 2^(ea - 127) * 2^(eb - 127) for block exponent bytes ea, eb, so
+    // |d| and every partial sum stay below 2^(12.2 + ea + eb - 254), finite
+    // while ea + eb <= 369. Hence: every key byte of the tile below
+    // lim = min(370 - max query byte, 255); a NaN query scale sends every tile
+    // to the exact form.
+    qmax = wave_max_u32(qmax);
+    const bool q_nan = __ballot(qnan != 0) != 0;
+    int lim = 370 - (int)qmax;
+    lim = lim > 255 ? 255 : lim;
+    if (q_nan || !FASTOK) lim = 0;
+
+    auto unpack = [&](uint32_t (&sv)[BATCH]) {
+        // the fence keeps every use of the batch (even the byte extraction) behind the previous issue
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
-            const int tile = t0 + NW * u;
-            if (tile >= ntiles) break;
-            float s;
-            if (FASTOK && __ballot((int)sv[u] >= lim) == 0) s = sum_rows(head_sum<NT, true>(A, sA, kv[u], sv[u], wv, hw));
-            else s = sum_rows(head_sum<NT, false>(A, sA, kv[u], sv[u], wv, hw));
-            const int r = tile * 16 + col;
-            if (grp == 0 && r < cnt) skey[r] = score_key(s);
+            asm volatile("" : "+v"(sv[u]));
+            sv[u] = (sv[u] >> (8 * grp)) & 0xFFu;  // this lane's K block: exponent byte grp
         }
     };
-    int t = wave;
-    issue(ka, sa, t);
-    for (; t < ntiles; t += 2 * STRIDE) {
-        if (t + STRIDE < ntiles) issue(kb, sb, t + STRIDE);
-        consume(ka, sa, t);
-        if (t + STRIDE >= ntiles) break;
-        if (t + 2 * STRIDE < ntiles) issue(ka, sa, t + 2 * STRIDE);
-        consume(kb, sb, t + STRIDE);
+    auto finish = [&](const float (&part)[BATCH], int bi) {
+        const float s = scatter_rows(part);
+        skey[(STRIDE * bi + wave + NW * grp) * 16 + col] = score_key(s);
+    };
+    // fast pass: every tile in the fast form; a batch with a key byte at or
+    // above lim only marks the wave for the exact pass below
+    bool redo = !FASTOK || q_nan;
+    auto consume = [&](const v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], int bi) {
+        unpack(sv);
+        const uint32_t smax = __builtin_elementwise_max(__builtin_elementwise_max(sv[0], sv[1]),
+                                                        __builtin_elementwise_max(sv[2], sv[3]));
+        redo |= __ballot((int)smax >= lim) != 0;
+        float part[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) part[u] = head_sum<NT, true>(A, sA, kv[u], sv[u], wv);
+        finish(part, bi);
+    };
+    if (FASTOK) {
+        // two batches in flight: batch bi + 2 is issued as soon as bi is consumed
+        // (scheduling barriers around each issue keep the next batch's work from
+        // being hoisted above it, which would wait for that batch's data first)
+#pragma unroll
+        for (int bi = 0; bi < NB; bi += 2) {
+            consume(ka, sa, bi);
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 2 < NB) issue(ka, sa, bi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(kb, sb, bi + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 3 < NB) issue(kb, sb, bi + 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // exact pass (rare: extreme exponents, NaN scales, or the merge's exact
+    // select): the wave rescores its own tiles one batch at a time, in a
+    // separate loop so that its registers never add to the fast pass's
+    if (redo) {
+        for (int bi = 0; bi < NB; ++bi) {
+            issue(ka, sa, bi);
+            unpack(sa);
+            float part[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) part[u] = head_sum<NT, false>(A, sA, ka[u], sa[u], wv);
+            finish(part, bi);
+        }
     }
 }
 
@@ -266,13 +363,13 @@ __device__ void score_chunk_f32(const IndexPlan &p, int q, int b, int64_t c0, in
     }
 }
 
-// MODE 0: f32 keys, 1..4: MXFP4 with MODE head tiles; NTH threads; BATCH MX tiles per wave and
-// batch; FASTOK: tiles may take the fast ReLU form
-template <int MODE, int NTH, int BATCH = MX_BATCH, bool FASTOK = true>
+// MODE 0: f32 keys, 1..4: MXFP4 with MODE head tiles (IT threads); NTH
+// threads for the f32 form; FASTOK: tiles may take the fast ReLU form
+template <int MODE, int NTH, bool FASTOK = true>
 __device__ __forceinline__ void score_chunk(const IndexPlan &p, int q, int b, int64_t c0, int cnt, uint32_t *skey,
                                             const float *sq) {
     if (MODE == 0) score_chunk_f32<NTH>(p, q, b, c0, cnt, skey, sq);
-    else score_chunk_mx<MODE, NTH / 64, BATCH, FASTOK>(p, q, b, c0, cnt, skey);
+    else score_chunk_mx<MODE, FASTOK>(p, q, b, c0, cnt, skey);
 }
 
 // ---------------------------------------------------- chunk candidates ----
@@ -345,7 +442,7 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
         __syncthreads();
         for (int64_t c0 = 0; c0 < nvis; c0 += p.chunk) {
             const int cnt = (int)((nvis - c0) < p.chunk ? (nvis - c0) : p.chunk);
-            if (threadIdx.x < IT) score_chunk<MODE, IT, 1, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
+            if (threadIdx.x < IT) score_chunk<MODE, IT, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
             __syncthreads();
             for (int i = tid; i < cnt; i += NT)
                 if ((skey[i] & mask) == prefix) atomicAdd(&sm.hist[(skey[i] >> (8 * d)) & 255u], 1u);
@@ -364,7 +461,7 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
     const int per = (p.chunk + NT - 1) / NT;
     for (int64_t c0 = 0; c0 < nvis; c0 += p.chunk) {
         const int cnt = (int)((nvis - c0) < p.chunk ? (nvis - c0) : p.chunk);
-        if (threadIdx.x < IT) score_chunk<MODE, IT, 1, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
+        if (threadIdx.x < IT) score_chunk<MODE, IT, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
         __syncthreads();
         const int lo = threadIdx.x * per;
         uint32_t nt = 0;
@@ -512,23 +609,6 @@ __device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf
     *in_bin = sm.misc[2];
 }
 
-// Max over the wave on the VALU: row rotations, then the lane-swap
-// instructions across rows.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    uint32_t y;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
-    x = y > x ? y : x;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
-    x = y > x ? y : x;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
-    x = y > x ? y : x;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
-    x = y > x ? y : x;
-    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = a[0] > a[1] ? a[0] : a[1];
-    auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return c[0] > c[1] ? c[0] : c[1];
-}
 
 // Marks the key registers as rewritten (no instruction is emitted), so that
 // per-key tests are not hoisted out of the select loop into 32 live masks.

@@ -43,9 +43,13 @@ struct CompressPlan {
     double inv_freq[ROPE_PAIRS];
 };
 
+// Entries scored by one indexer workgroup. A compile-time constant: the
+// scoring loop over a chunk is fully unrolled.
+constexpr int IDX_CHUNK = 1024;
+
 struct IndexPlan {
     int Q, Tq, H, dI, k, m;
-    int chunk;       // entries scored per workgroup
+    int chunk;       // entries scored per workgroup (IDX_CHUNK)
     int n_chunks;    // workgroups per query
     int s_local;     // candidates a chunk keeps at least (its local top-s)
     int region_cap;  // candidate slots per chunk in the workspace
