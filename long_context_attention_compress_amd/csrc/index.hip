@@ -374,35 +374,133 @@ __device__ __forceinline__ void score_chunk(const IndexPlan &p, int q, int b, in
 
 // ---------------------------------------------------- chunk candidates ----
 
-// Keep the chunk's entries whose key's top 16 bits reach the s-th largest.
-__device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
-                           const uint32_t *skey, IdxSmem &sm) {
-    const int tid = threadIdx.x;
-    const size_t rid = (size_t)q * p.n_chunks + chunk;
-    uint32_t thr = 0;  // emit keys >= thr
-    if (cnt > s_want) {
-        for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < cnt; i += IT) atomicAdd(&sm.hist[skey[i] >> 24], 1u);
-        __syncthreads();
-        uint32_t above1;
-        const int b1 = find_bin<IT>(sm, (uint32_t)s_want, &above1);
-        for (int i = tid; i < 256; i += IT) sm.hist[i] = 0;
-        __syncthreads();
-        for (int i = tid; i < cnt; i += IT)
-            if ((int)(skey[i] >> 24) == b1) atomicAdd(&sm.hist[(skey[i] >> 16) & 255u], 1u);
-        __syncthreads();
-        uint32_t above2;
-        const int b2 = find_bin<IT>(sm, (uint32_t)s_want - above1, &above2);
-        thr = ((uint32_t)b1 << 24) | ((uint32_t)b2 << 16);
+// Keep the chunk's entries at or above a threshold that at least s of them
+// reach. The threshold is the lower edge of a radix bin: 11-bit digits taken
+// from the highest bit in which the chunk's keys differ, so the bins follow
+// the keys' actual range; the bin holding the s-th largest key is refined by
+// further digits only while the entries at or above its edge are more than a
+// merge thread group takes in registers (EMIT_SOFT). Entries are written in
+// index order with the threshold as the region's lower bound.
+constexpr int EBITS = 11;
+constexpr int EBINS = 1 << EBITS;
+constexpr int EMIT_SOFT = 32;  // = GROUP * REG_CAND of the merge (static_assert there)
+struct EmitSmem {
+    uint32_t hist[EBINS] __attribute__((aligned(16)));
+    uint32_t red[2][IT / 64];
+    uint32_t scan[IT / 64];
+    uint32_t res[4];
+};
+
+// Exclusive prefix sum over the IT threads in thread order; *total gets the sum.
+__device__ __forceinline__ uint32_t emit_scan(uint32_t v, EmitSmem &em, uint32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t x = wave_inclusive_scan(v);
+    if (lane == 63) em.scan[wave] = x;
+    __syncthreads();
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < IT / 64; ++w) {
+        const uint32_t t = em.scan[w];
+        before += (w < wave) ? t : 0u;
+        all += t;
     }
-    // compaction in index order: thread t owns entries [t*per, t*per + per)
-    const int per = (p.chunk + IT - 1) / IT;
-    const int lo = tid * per;
+    *total = all;
+    return x - v + before;
+}
+
+__device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
+                           const uint32_t *skey, EmitSmem &em) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t rid = (size_t)q * p.n_chunks + chunk;
+    constexpr int PER = IDX_CHUNK / IT;  // entries per thread, in index order
+    static_assert(PER == 4, "one 16-byte LDS read per thread");
+    const uint4 k4 = *(const uint4 *)&skey[PER * tid];
+    const uint32_t key[PER] = {k4.x, k4.y, k4.z, k4.w};
+    bool valid[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) valid[j] = PER * tid + j < cnt;
+    uint32_t thr = 0;  // emit valid keys >= thr
+    if (cnt > s_want) {
+        // range of the valid keys; the histogram is cleared in the same round
+        uint32_t mx = 0u, nmn = 0u;  // max and ~min
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+            if (valid[j]) {
+                mx = key[j] > mx ? key[j] : mx;
+                nmn = ~key[j] > nmn ? ~key[j] : nmn;
+            }
+        mx = wave_max_u32(mx);
+        nmn = wave_max_u32(nmn);
+        *(uint4 *)&em.hist[8 * tid] = make_uint4(0, 0, 0, 0);
+        *(uint4 *)&em.hist[8 * tid + 4] = make_uint4(0, 0, 0, 0);
+        if (lane == 0) {
+            em.red[0][wave] = mx;
+            em.red[1][wave] = nmn;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < IT / 64; ++w) {
+            mx = em.red[0][w] > mx ? em.red[0][w] : mx;
+            nmn = em.red[1][w] > nmn ? em.red[1][w] : nmn;
+        }
+        const uint32_t diff = mx ^ ~nmn;
+        if (diff == 0u) {
+            thr = mx;  // every valid key equal: all of them reach it
+        } else {
+            int top = 31 - __builtin_clz(diff);  // highest differing bit; bits above it are common
+            uint32_t prefix = (uint32_t)(((uint64_t)mx >> (top + 1)) << (top + 1));
+            uint32_t need = (uint32_t)s_want, above_all = 0;
+            while (true) {
+                const int sh = top + 1 - EBITS > 0 ? top + 1 - EBITS : 0;
+                const uint32_t dmask = (2u << (top - sh)) - 1u;
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (valid[j] && ((uint64_t)key[j] >> (top + 1)) == ((uint64_t)prefix >> (top + 1)))
+                        atomicAdd(&em.hist[(key[j] >> sh) & dmask], 1u);
+                __syncthreads();
+                // thread t owns bins EBINS-8(t+1) .. EBINS-8t-1, highest first
+                const uint4 h1 = *(const uint4 *)&em.hist[EBINS - 8 * tid - 4];
+                const uint4 h0 = *(const uint4 *)&em.hist[EBINS - 8 * tid - 8];
+                const uint32_t h[8] = {h1.w, h1.z, h1.y, h1.x, h0.w, h0.z, h0.y, h0.x};
+                uint32_t local = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) local += h[i];
+                uint32_t tot;
+                const uint32_t before = emit_scan(local, em, &tot);
+                if (before < need && need <= before + local) {
+                    uint32_t c = before;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        if (c < need && need <= c + h[i]) {
+                            em.res[0] = EBINS - 1 - 8 * tid - i;
+                            em.res[1] = c;     // keys in higher bins
+                            em.res[2] = h[i];  // keys in the bin
+                        }
+                        c += h[i];
+                    }
+                }
+                __syncthreads();
+                const uint32_t bin = em.res[0], above = em.res[1], pop = em.res[2];
+                prefix |= bin << sh;
+                above_all += above;
+                need -= above;
+                if (above_all + pop <= (uint32_t)EMIT_SOFT || sh == 0) break;
+                // refine inside the bin: clear it for the next digit
+                __syncthreads();  // every thread has read res and its bins
+                *(uint4 *)&em.hist[8 * tid] = make_uint4(0, 0, 0, 0);
+                *(uint4 *)&em.hist[8 * tid + 4] = make_uint4(0, 0, 0, 0);
+                __syncthreads();
+                top = sh - 1;
+            }
+            thr = prefix;
+        }
+    }
+    // compaction in index order
     uint32_t mine = 0;
-    for (int i = lo; i < lo + per && i < cnt; ++i) mine += skey[i] >= thr;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) mine += (valid[j] && key[j] >= thr) ? 1u : 0u;
     uint32_t total;
-    uint32_t off = block_scan<IT>(mine, sm, &total) - mine;
+    uint32_t off = emit_scan(mine, em, &total);
     uint32_t *meta = p.meta + rid * 2;
     if (total > (uint32_t)p.region_cap) {
         if (tid == 0) {
@@ -413,10 +511,11 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
     }
     uint32_t *rk = p.reg_key + rid * p.region_cap;
     int32_t *ri = p.reg_idx + rid * p.region_cap;
-    for (int i = lo; i < lo + per && i < cnt; ++i) {
-        if (skey[i] >= thr) {
-            rk[off] = skey[i];
-            ri[off] = (int32_t)(c0 + i);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (valid[j] && key[j] >= thr) {
+            rk[off] = key[j];
+            ri[off] = (int32_t)(c0 + PER * tid + j);
             ++off;
         }
     }
@@ -430,6 +529,7 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
 
 constexpr int REG_CAND = 8;  // candidates a merge thread holds in registers
 constexpr int GROUP = 4;     // merge threads sharing one chunk's region (32 slots)
+static_assert(GROUP * REG_CAND == EMIT_SOFT, "a chunk emits at most what one thread group holds");
 
 template <int MODE, int NT>
 __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, int kk, uint32_t *skey,
@@ -504,8 +604,8 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
 
 template <int MODE>
 __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
-    extern __shared__ uint32_t dyn[];
-    __shared__ IdxSmem sm;
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    __shared__ EmitSmem em;
     uint32_t *skey = dyn;                                 // [chunk]
     float *sq = (float *)(dyn + p.chunk);                 // f32 mode: query [H][dI]
     const int chunk = blockIdx.x, q = blockIdx.y;
@@ -537,7 +637,7 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
     const int64_t spread = (kk + div - 1) / div;
     if (spread > s_want) s_want = (int)spread;
     if (s_want > cnt) s_want = cnt;
-    chunk_emit(p, q, chunk, c0, cnt, s_want, skey, sm);
+    chunk_emit(p, q, chunk, c0, cnt, s_want, skey, em);
 }
 
 // ------------------------------------------------------ merge select ----

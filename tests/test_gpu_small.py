@@ -155,6 +155,29 @@ def test_index_mxfp4_clustered_winners_and_ties():
     _check_index(c, idx, score, c['dkeys'], c['diq'])
 
 
+def test_index_mxfp4_exponent_extremes():
+    """Exponent bytes that send tiles to the exact pass of the scorer: keys scaled by
+    2^84 with a query head scaled by 2^34 (no overflow, but the bound on |q.k| no
+    longer rules it out), NaN key exponents (0xFF) and, in batch 1, a NaN query
+    exponent (every tile exact)."""
+    rows = 6000
+    q_pos = np.array([[rows * 4 - 1], [rows * 4 - 1]], np.int64)
+    c = _index_case_mx(5, 2, rows, q_pos, 256)
+    sc, isc = c['sc'].copy(), c['isc'].copy()
+    sc[:, ::97] += 84                     # rows 0, 97, ...: x 2^84
+    sc[:, 5::211, 2] = 0xFF               # NaN in one 32-dim block
+    isc[0, 0, 3] += 34                    # batch 0: head 3 x 2^34
+    isc[1, 0, 7, 1] = 0xFF                # batch 1: NaN query block -> every tile exact
+    c['sc'], c['isc'] = sc, isc
+    dkeys, diq = F.mxfp4_dequantize(c['packed'], sc), F.mxfp4_dequantize(c['ip'], isc)
+    for b in range(2):
+        s = OI.index_scores(diq[b, 0], c['w'][b, 0], dkeys[b])
+        assert np.all(np.isfinite(s.astype(np.float32))), 'the case must not overflow float32'
+    print('index mxfp4 exponent extremes', flush=True)
+    idx, score = _run_index(c)
+    _check_index(c, idx, score, dkeys, diq)
+
+
 def test_index_mxfp4_repeat_is_bitwise_identical():
     q_pos = np.array([[12000 * 4 - 1]], np.int64)
     c = _index_case_mx(3, 1, 12000, q_pos, 256)
