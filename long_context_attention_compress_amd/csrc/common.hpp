@@ -56,6 +56,34 @@ __device__ __forceinline__ float wave_amax(float v) {
     return v;
 }
 
+// Unsigned max over a 16-lane row, a 32-lane half and the wave, on the VALU:
+// DPP row rotations, then the gfx950 lane-swap instructions across rows.
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t x) {
+    uint32_t y;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
+    x = y > x ? y : x;
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
+    return y > x ? y : x;
+}
+__device__ __forceinline__ uint32_t half_max_u32(uint32_t x) {
+    x = row_max_u32(x);
+    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return a[0] > a[1] ? a[0] : a[1];
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+    x = half_max_u32(x);
+    auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return c[0] > c[1] ? c[0] : c[1];
+}
+// Magnitude maxima (inputs are |x| or a NaN with the sign cleared; as bits
+// they order like the magnitudes, a NaN above infinity, so a NaN propagates).
+__device__ __forceinline__ float wave_amax_bits(float a) { return __uint_as_float(wave_max_u32(__float_as_uint(a))); }
+__device__ __forceinline__ float half_amax_bits(float a) { return __uint_as_float(half_max_u32(__float_as_uint(a))); }
+
 // ------------------------------------------------------------------ BF16 ----
 __device__ __forceinline__ uint16_t bf16_encode(float x) {
     uint32_t u = __float_as_uint(x);

@@ -48,7 +48,7 @@ __device__ void store_kv_row(const KvView &s, int b, int64_t row, const float *n
     for (int g = 0; g < n_nope_it / 2; ++g) {  // groups of 128 dims = two lane iterations
         float a = amax_acc(0.0f, nope[2 * g]);
         a = amax_acc(a, nope[2 * g + 1]);
-        a = wave_amax(a);
+        a = wave_amax_bits(a);
         float sc = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
         if (__builtin_isnan(a)) sc = a;
         codes[128 * g + lane] = e4m3_encode(__fdiv_rn(nope[2 * g], sc));
@@ -72,7 +72,7 @@ __device__ __forceinline__ void store_ik_value(const IkView &s, int b, int64_t e
     // MX block of 32 = one half of the wave
     bool bad = !__builtin_isfinite(x) && on;
     float a = on ? amax_acc(0.0f, x) : 0.0f;
-    a = half_max(a);
+    a = half_amax_bits(a);
     int nbad = __builtin_popcountll(__ballot(bad) & ((lane < 32) ? 0xFFFFFFFFull : 0xFFFFFFFF00000000ull));
     uint32_t code = 0;
     int E = 0;
@@ -176,10 +176,15 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
 // itself. Same float64 arithmetic as the general kernel.
 constexpr int SMALL_M = 4;
 
+// Raw bits of one activation (float32 or BF16) and its float32 value.
 template <int ACT>
-__device__ __forceinline__ float load_val(const void *base, int64_t i) {
-    if (ACT == 0) return ((const float *)base)[i];
-    return bf16_decode(((const uint16_t *)base)[i]);
+__device__ __forceinline__ uint32_t load_bits(const char *base, int64_t i) {
+    if (ACT == 0) return ((const uint32_t *)base)[i];
+    return ((const uint16_t *)base)[i];
+}
+template <int ACT>
+__device__ __forceinline__ float bits_val(uint32_t x) {
+    return ACT == 0 ? __uint_as_float(x) : __uint_as_float(x << 16);
 }
 
 template <int ACT, int M>
@@ -192,30 +197,46 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
     const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
     const int dI = p.dI;
     const bool rl = lane < ROPE_PAIRS;
-    double z[M];
-    float kn[M][4], vn[M][4], kx[M], ky[M], vx[M], vy[M], ui[M][4];
+    // Every load is unconditional, so all of them are in flight together: an
+    // absent source reads element 0 of the gate instead, and an element past
+    // the row reads the row's first; the values are masked after the loads.
+    const char *gsrc = (const char *)p.gate;
+    const char *ksrc = do_kv ? (const char *)p.raw_k : gsrc;
+    const char *vsrc = do_kv ? (const char *)p.raw_v : gsrc;
+    const char *isrc = p.has_ik ? (const char *)p.raw_ik : gsrc;
+    double f = p.inv_freq[rl ? lane : 0];
+    float gz[M], gb[M];
+    uint32_t kn[M][4], vn[M][4], kx[M], ky[M], vx[M], vy[M], ui[M][4];
 #pragma unroll
     for (int r = 0; r < M; ++r) {
         const int64_t t = (int64_t)b * p.t_new + tok0 + r;
-        z[r] = (double)p.gate[t] + (double)p.pos_bias[r];
-        const int64_t row = t * D;
+        gz[r] = p.gate[t];
+        gb[r] = p.pos_bias[r];
+        const int64_t row = do_kv ? t * D : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool on = do_kv && i < nit;
-            kn[r][i] = on ? load_val<ACT>(p.raw_k, row + lane + 64 * i) : 0.f;
-            vn[r][i] = on ? load_val<ACT>(p.raw_v, row + lane + 64 * i) : 0.f;
+            const int64_t x = i < nit ? row + lane + 64 * i : row;
+            kn[r][i] = load_bits<ACT>(ksrc, x);
+            vn[r][i] = load_bits<ACT>(vsrc, x);
         }
-        const bool ron = do_kv && rl;
-        kx[r] = ron ? load_val<ACT>(p.raw_k, row + Dn + 2 * lane) : 0.f;
-        ky[r] = ron ? load_val<ACT>(p.raw_k, row + Dn + 2 * lane + 1) : 0.f;
-        vx[r] = ron ? load_val<ACT>(p.raw_v, row + Dn + 2 * lane) : 0.f;
-        vy[r] = ron ? load_val<ACT>(p.raw_v, row + Dn + 2 * lane + 1) : 0.f;
+        const int64_t xr = rl ? row + Dn + 2 * lane : row;
+        kx[r] = load_bits<ACT>(ksrc, xr);
+        ky[r] = load_bits<ACT>(ksrc, xr + (rl ? 1 : 0));
+        vx[r] = load_bits<ACT>(vsrc, xr);
+        vy[r] = load_bits<ACT>(vsrc, xr + (rl ? 1 : 0));
+        const int64_t irow = p.has_ik ? t * dI : 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool on = p.has_ik && lane + 64 * i < dI;
-            ui[r][i] = on ? load_val<ACT>(p.raw_ik, t * dI + lane + 64 * i) : 0.f;
+            ui[r][i] = load_bits<ACT>(isrc, on ? irow + lane + 64 * i : irow);
         }
     }
+    // no load is sunk into the branches that use it (the register fence also
+    // pins the rotation frequency, a kernel-argument load, up here)
+    asm volatile("" : "+v"(f) :: "memory");
+    double z[M];
+#pragma unroll
+    for (int r = 0; r < M; ++r) z[r] = (double)gz[r] + (double)gb[r];
     // alpha_r = softmax_r(gate + pos_bias), float64
     double zmax = z[0];
 #pragma unroll
@@ -237,25 +258,24 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
             double ak = 0.0, av = 0.0;
 #pragma unroll
             for (int r = 0; r < M; ++r) {
-                ak += alpha[r] * (double)kn[r][i];
-                av += alpha[r] * (double)vn[r][i];
+                ak += alpha[r] * (double)bits_val<ACT>(kn[r][i]);
+                av += alpha[r] * (double)bits_val<ACT>(vn[r][i]);
             }
             nk[i] = (float)ak;
             nv[i] = (float)av;
         }
         float rkx = 0.f, rky = 0.f, rvx = 0.f, rvy = 0.f;
         if (rl) {
-            const double f = p.inv_freq[lane];
             double akx = 0.0, aky = 0.0, avx = 0.0, avy = 0.0;
 #pragma unroll
             for (int r = 0; r < M; ++r) {
                 double sn, cs;
                 rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
-                const double x = kx[r], y = ky[r];
+                const double x = bits_val<ACT>(kx[r]), y = bits_val<ACT>(ky[r]);
                 akx += alpha[r] * (x * cs - y * sn);
                 aky += alpha[r] * (x * sn + y * cs);
-                avx += alpha[r] * (double)vx[r];
-                avy += alpha[r] * (double)vy[r];
+                avx += alpha[r] * (double)bits_val<ACT>(vx[r]);
+                avy += alpha[r] * (double)bits_val<ACT>(vy[r]);
             }
             rkx = (float)akx;
             rky = (float)aky;
@@ -272,7 +292,7 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
             if (i >= nit_i) break;
             double acc = 0.0;
 #pragma unroll
-            for (int r = 0; r < M; ++r) acc += alpha[r] * (double)ui[r][i];
+            for (int r = 0; r < M; ++r) acc += alpha[r] * (double)bits_val<ACT>(lane + 64 * i < dI ? ui[r][i] : 0u);
             const int d = lane + 64 * i;
             store_ik_value(p.ik, b, entry, d, d < dI, (float)acc);
         }

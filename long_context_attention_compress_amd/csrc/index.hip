@@ -125,23 +125,6 @@ __device__ __forceinline__ float scatter_rows(const float (&x)[4]) {
     return swap_add16(x02, x13);               // row g: x[g] summed over the four rows
 }
 
-// Max over the wave on the VALU: row rotations, then the lane-swap
-// instructions across rows.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
-    uint32_t y;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
-    x = y > x ? y : x;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
-    x = y > x ? y : x;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
-    x = y > x ? y : x;
-    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
-    x = y > x ? y : x;
-    auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    x = a[0] > a[1] ? a[0] : a[1];
-    auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return c[0] > c[1] ? c[0] : c[1];
-}
 
 // sum_h w_h max(0, d_h) over this lane's heads, as an fma chain. The exact
 // form takes max(0, d) with fmaxf semantics (a NaN d counts as 0), which the
