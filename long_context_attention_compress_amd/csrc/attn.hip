@@ -525,7 +525,7 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
         // raise the running max (and rescale) only when this tile exceeds it by the slack
         if (__builtin_amdgcn_ballot_w64(mx > mrun + RESCALE_SLACK)) {
             const float mn = __builtin_fmaxf(mrun, mx);
-            const float c = mn == -__builtin_inff() ? 1.f : exp2f(mrun - mn);
+            const float c = mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(mrun - mn);
             lrun *= c;
 #pragma unroll
             for (int i = 0; i < 12; ++i) O[i] *= c;
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                pr[st][j] = s[st][j] == -__builtin_inff() ? 0.f : exp2f(s[st][j] - mrun);
+                pr[st][j] = s[st][j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(s[st][j] - mrun);
                 psum += pr[st][j];
             }
         lrun += swap32_sum(swap16_sum(psum));
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
     for (int k = 0; k < 2; ++k) {
         const int sp = tid + CMB_T * k;
         if (sp < S) {
-            const float w = M == -__builtin_inff() ? 0.f : exp2f(ml[k].x - M);
+            const float w = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
             wgt[sp] = w;
             lloc += w * ml[k].y;
         }
