@@ -176,9 +176,11 @@ int check_index(const v4a_index_args *a) {
 constexpr int KS_MIN = 32;      // keys per split: one tile at least
 constexpr int KS_MAX = 2048;    // the FP8 kernel resolves a split's rows into LDS
 constexpr int WG_TARGET = 512;  // about two resident workgroups per compute unit
+constexpr int WG_TARGET_NS2 = 256;  // two-stream workgroups: one per compute unit
+constexpr int64_t NS2_MIN_KEYS = 4096;  // key lists at least this long take two streams
 
 struct AttnLayout {
-    int n_split, keys_per_split;
+    int n_split, keys_per_split, n_streams;
     size_t off_ml, total;
 };
 
@@ -194,9 +196,14 @@ AttnLayout attn_layout(const v4a_attn_args *a, bool sparse, int k, int64_t n_ove
         }
     }
     const int64_t cap = n_list + a->W;
+    // Long key lists (FP8 path) run two key streams per workgroup, one
+    // workgroup per compute unit; short ones one stream, about two per unit.
+    const bool fp8 = a->win_k && a->win_k->fmt == V4A_KV_E4M3_BF16;
+    L.n_streams = (fp8 && cap >= NS2_MIN_KEYS) ? 2 : 1;
+    const int64_t target = L.n_streams == 2 ? WG_TARGET_NS2 : WG_TARGET;
     // enough splits to fill the device when the queries alone cannot, at least
-    // one tile per split, and no split longer than KS_MAX keys
-    int64_t n_split = std::min((cap + KS_MIN - 1) / KS_MIN, (WG_TARGET + Q - 1) / Q);
+    // one tile per stream, and no split longer than KS_MAX keys
+    int64_t n_split = std::min((cap + KS_MIN * L.n_streams - 1) / (KS_MIN * L.n_streams), (target + Q - 1) / Q);
     n_split = std::max<int64_t>(n_split, (cap + KS_MAX - 1) / KS_MAX);
     n_split = std::max<int64_t>(1, std::min<int64_t>(n_split, 1024));
     int64_t ks = (cap + n_split - 1) / n_split;
@@ -268,6 +275,7 @@ int check_attn(const v4a_attn_args *a, AttnPlan *P) {
 int run_attn(AttnPlan &P, const AttnLayout &L, void *ws, size_t ws_bytes, hipStream_t s) {
     P.n_split = L.n_split;
     P.keys_per_split = L.keys_per_split;
+    P.n_streams = L.n_streams;
     if (L.total > 0) {
         if (!ws) return fail(V4A_EWORKSPACE, "a workspace of %zu bytes is required", L.total);
         if (ws_bytes < L.total) return fail(V4A_EWORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);

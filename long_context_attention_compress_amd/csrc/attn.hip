@@ -223,15 +223,25 @@ constexpr int MDN = 128;        // E4M3 dims
 constexpr int KB_LD = MD + 8;   // bf16 elements per staged K or V row (padded)
 constexpr int MAX_KS = 2048;    // keys per split (their store rows are resolved into LDS first)
 
-struct MxSmem {
-    __bf16 kb[TK * KB_LD];      // K tile, row-major BF16
-    __bf16 vb[TK * KB_LD];      // V tile, row-major BF16 (read transposed by ds_read_b64_tr_b16)
-    float ksc[TK] __attribute__((aligned(16)));  // K row scale of each key (0 for an empty slot)
+// One staged tile: K and V row-major BF16 (V read transposed by
+// ds_read_b64_tr_b16), per-key scales and the empty-slot bias.
+struct TileBuf {
+    __bf16 kb[TK * KB_LD];
+    __bf16 vb[TK * KB_LD];
+    float ksc[TK] __attribute__((aligned(16)));    // K row scale of each key (0 for an empty slot)
     float kbias[TK] __attribute__((aligned(16)));  // 0, or -inf for an empty slot
     float vsc[TK] __attribute__((aligned(16)));
+};
+
+// NS key streams per workgroup, each with its own tile buffer; at the end the
+// streams' partial results meet in the (then free) tile buffers.
+template <int NS>
+struct MxSmem {
+    TileBuf tb[NS];
     double rcos[ROPE_PAIRS];
     double rsin[ROPE_PAIRS];
     int32_t rows[MAX_KS];       // row of each key of the split; bit 30 marks a window row; -1: no key
+    float xml[NS > 1 ? 2 * AT : 1];
 };
 
 constexpr int32_t WIN_BIT = 1 << 30;
@@ -273,15 +283,15 @@ __device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
 // Issue the loads of one 32-key tile. Branch-free: a slot without a key reads
 // row 0 of the window store (always present) and is zeroed afterwards, so the
 // compiler keeps every load of the tile in flight together.
-__device__ __forceinline__ void load_tile(const TileSrc &S, const MxSmem &sm, int rel, int n_rel, TileRegs &R) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void load_tile(const TileSrc &S, const int32_t *rows, int rel, int n_rel, TileRegs &R,
+                                          int tid) {
     const int part = tid & 15;
     const int64_t koff = part < 8 ? 16 * part : 16 * (part - 8);
     const bool nope = part < 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 16 * h;
-        const int32_t code = rel + r < n_rel ? sm.rows[rel + r] : -1;
+        const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
         const bool ok = code >= 0;
         const bool win = !ok || (code & WIN_BIT);
         const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
@@ -295,7 +305,7 @@ __device__ __forceinline__ void load_tile(const TileSrc &S, const MxSmem &sm, in
     }
     // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
     const int r = tid & (TK - 1);
-    const int32_t code = (tid < 2 * TK && rel + r < n_rel) ? sm.rows[rel + r] : -1;
+    const int32_t code = (tid < 2 * TK && rel + r < n_rel) ? rows[rel + r] : -1;
     const bool ok = code >= 0;
     const bool win = !ok || (code & WIN_BIT);
     const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
@@ -327,8 +337,8 @@ __device__ __forceinline__ void store_codes(__bf16 *dst, const v4i &c) {
     *(v4i *)(dst + 8) = hi;
 }
 
-__device__ __forceinline__ void stage_tile(const TileRegs &R, const int *valid_rows, MxSmem &sm, int rel, int n_rel) {
-    const int tid = threadIdx.x;
+__device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *rows, TileBuf &sm, int rel, int n_rel,
+                                           int tid) {
     const int part = tid & 15;
     const v4i z = {0, 0, 0, 0};
 #pragma unroll
@@ -346,11 +356,10 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int *valid_r
     const float sc = R.sok ? R.sc : 0.f;
     if (tid < TK) {
         sm.ksc[tid] = sc;
-        sm.kbias[tid] = (rel + tid < n_rel && sm.rows[rel + tid] >= 0) ? 0.f : -__builtin_inff();
+        sm.kbias[tid] = (rel + tid < n_rel && rows[rel + tid] >= 0) ? 0.f : -__builtin_inff();
     } else if (tid < 2 * TK) {
         sm.vsc[tid - TK] = sc;
     }
-    (void)valid_rows;
 }
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *(const bf16x8 *)p; }
@@ -360,7 +369,7 @@ __device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *(const bf16x8 
 // Each ds_read_b64_tr_b16 transposes a 16x4 block within the 16-lane group:
 // source lane 4k+r reads key kappa(k), dims 16*dt + 4r .. +3.
 typedef short v4s __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x8 vt_operand(const MxSmem &sm, int dt, int g, int j) {
+__device__ __forceinline__ bf16x8 vt_operand(const TileBuf &sm, int dt, int g, int j) {
     const int k = j >> 2, r = j & 3;
     const __bf16 *a = &sm.vb[(4 * g + k) * KB_LD + 16 * dt + 4 * r];
     const __bf16 *c = &sm.vb[(16 + 4 * g + k) * KB_LD + 16 * dt + 4 * r];
@@ -395,10 +404,15 @@ __device__ __forceinline__ float swap32_sum(float x) {
 // probabilities may exceed 1 by at most that factor, which float32 absorbs.
 constexpr float RESCALE_SLACK = 8.0f;
 
-template <int NW>
-__global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
-    __shared__ MxSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// NS key streams: the workgroup has NS x 256 threads; stream s takes tiles
+// s, s + NS, ... of the split with its own four waves (16 heads each) and
+// tile buffer, so NS tiles are in flight per head group. The streams' online
+// softmax states are merged at the end.
+template <int NW, int NS>
+__global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
+    __shared__ MxSmem<NS> sm;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int stream = tid / AT, tids = tid % AT, wave = tids >> 6;
     const int col = lane & 15, g = lane >> 4;
     const int q = blockIdx.y, split = blockIdx.x;
     const int b = q / p.Tq;
@@ -414,12 +428,12 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
     for (int c = 0; c < 4; ++c) qn[c] = ld16(qp + 32 * c + 8 * g);
 #pragma unroll
     for (int c = 0; c < 2; ++c) qraw[c] = ld16(qp + MDN + 32 * c + 8 * g);
-    constexpr int IDS = MAX_KS / AT;
+    constexpr int IDS = MAX_KS / (AT * NS);
     const int64_t j0 = (int64_t)split * p.keys_per_split;
     int32_t ids[IDS];
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
-        const int i = tid + AT * u;
+        const int i = tid + AT * NS * u;
         ids[u] = (p.sparse && i < p.keys_per_split && j0 + i < p.k) ? p.idx[(size_t)q * p.k + j0 + i] : -1;
     }
     const KeyInfo ki = key_info(p, q);
@@ -429,7 +443,7 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
     // resolve the split's keys to store rows once, and the RoPE table
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
-        const int i = tid + AT * u;
+        const int i = tid + AT * NS * u;
         if (i < n_rel) {
             const int64_t j = j0 + i;
             int64_t row;
@@ -484,15 +498,16 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
     // window row 0 and is never staged), and the loop is unrolled by two, so
     // the wait before staging tile t only covers tile t's loads and tile t+1's
     // stay in flight.
+    TileBuf &tb = sm.tb[stream];
     auto compute = [&]() {
         if (!active) return;
         // per-key scales of this lane's eight keys (4g..4g+3 and 16+4g..), read as vectors
         v4f ks[2], kb[2], vs[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            ks[st] = *(const v4f *)&sm.ksc[16 * st + 4 * g];
-            kb[st] = *(const v4f *)&sm.kbias[16 * st + 4 * g];
-            vs[st] = *(const v4f *)&sm.vsc[16 * st + 4 * g];
+            ks[st] = *(const v4f *)&tb.ksc[16 * st + 4 * g];
+            kb[st] = *(const v4f *)&tb.kbias[16 * st + 4 * g];
+            vs[st] = *(const v4f *)&tb.vsc[16 * st + 4 * g];
         }
         // the two key halves as independent MFMA chains
         v4f an[2] = {zero, zero}, ar[2] = {zero, zero};
@@ -501,12 +516,12 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
 #pragma unroll
             for (int st = 0; st < 2; ++st)
                 an[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    ld16(&sm.kb[(16 * st + col) * KB_LD + 8 * g + 32 * c]), qn[c], an[st], 0, 0, 0);
+                    ld16(&tb.kb[(16 * st + col) * KB_LD + 8 * g + 32 * c]), qn[c], an[st], 0, 0, 0);
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const bf16x8 a = ld16(&sm.kb[(16 * st + col) * KB_LD + 8 * g + MDN + 32 * c]);
+                const bf16x8 a = ld16(&tb.kb[(16 * st + col) * KB_LD + 8 * g + MDN + 32 * c]);
                 ar[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrh[c], ar[st], 0, 0, 0);
                 ar[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrl[c], ar[st], 0, 0, 0);
             }
@@ -555,26 +570,59 @@ __global__ __launch_bounds__(AT, 2) void attn_mx_kernel(AttnPlan p) {
             }
 #pragma unroll
         for (int dt = 0; dt < 12; ++dt) {
-            const bf16x8 a = vt_operand(sm, dt, g, col);
+            const bf16x8 a = vt_operand(tb, dt, g, col);
             O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnh : pbh, O[dt], 0, 0, 0);
             O[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, dt < 8 ? pnl : pbl, O[dt], 0, 0, 0);
         }
     };
+    // stream s: tiles s + NS i; every stream runs the same number of rounds
+    // (a round past its last tile stages an empty tile and skips the compute)
+    const int n_rounds = (n_tiles + NS - 1) / NS;
     TileRegs RA, RB;
-    load_tile(src, sm, 0, n_rel, RA);
-    load_tile(src, sm, TK, n_rel, RB);
-    for (int t = 0; t < n_tiles; t += 2) {
+    load_tile(src, sm.rows, TK * stream, n_rel, RA, tids);
+    load_tile(src, sm.rows, TK * (stream + NS), n_rel, RB, tids);
+    for (int i = 0; i < n_rounds; i += 2) {
+        const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         __syncthreads();
-        stage_tile(RA, nullptr, sm, t * TK, n_rel);
-        load_tile(src, sm, (t + 2) * TK, n_rel, RA);
+        stage_tile(RA, sm.rows, tb, ta * TK, n_rel, tids);
+        load_tile(src, sm.rows, (ta + 2 * NS) * TK, n_rel, RA, tids);
         __syncthreads();
-        compute();
-        if (t + 1 >= n_tiles) break;
+        if (ta < n_tiles) compute();
+        if (i + 1 >= n_rounds) break;
         __syncthreads();
-        stage_tile(RB, nullptr, sm, (t + 1) * TK, n_rel);
-        load_tile(src, sm, (t + 3) * TK, n_rel, RB);
+        stage_tile(RB, sm.rows, tb, tb_ * TK, n_rel, tids);
+        load_tile(src, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
         __syncthreads();
-        compute();
+        if (tb_ < n_tiles) compute();
+    }
+    if (NS > 1) {
+        // the other streams hand their (max, sum, O) to stream 0 through the tile buffers
+        __syncthreads();
+        float *xo = (float *)&sm.tb[0];
+        static_assert(sizeof(TileBuf) * NS >= sizeof(float) * AT * 48 * (NS - 1), "exchange fits the tile buffers");
+        if (stream > 0 && active) {
+            const int base = (stream - 1) * AT * 48;
+#pragma unroll
+            for (int dt = 0; dt < 12; ++dt) *(v4f *)&xo[base + (dt * AT + tids) * 4] = O[dt];
+            sm.xml[2 * tids] = mrun;
+            sm.xml[2 * tids + 1] = lrun;
+        }
+        __syncthreads();
+        if (stream > 0) return;
+        if (active) {
+#pragma unroll
+            for (int os = 1; os < NS; ++os) {
+                const int base = (os - 1) * AT * 48;
+                const float m1 = sm.xml[2 * tids], l1 = sm.xml[2 * tids + 1];
+                const float mn = __builtin_fmaxf(mrun, m1);
+                const float c0 = mrun == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+                const float c1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+#pragma unroll
+                for (int dt = 0; dt < 12; ++dt) O[dt] = O[dt] * c0 + *(const v4f *)&xo[base + (dt * AT + tids) * 4] * c1;
+                lrun = lrun * c0 + l1 * c1;
+                mrun = mn;
+            }
+        }
     }
     if (!active) return;
     // epilogue: lane holds O^T[16dt + 4g + j][head]
@@ -707,11 +755,20 @@ hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
         size_t lds = (size_t)(p.H * p.D + 2 * TK * p.D + p.H * TK + 3 * p.H) * 4;
         hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(AT), lds, s, p);
     } else {
-        switch (p.H / 16) {
-            case 1: hipLaunchKernelGGL(attn_mx_kernel<1>, grid, dim3(AT), 0, s, p); break;
-            case 2: hipLaunchKernelGGL(attn_mx_kernel<2>, grid, dim3(AT), 0, s, p); break;
-            case 3: hipLaunchKernelGGL(attn_mx_kernel<3>, grid, dim3(AT), 0, s, p); break;
-            default: hipLaunchKernelGGL(attn_mx_kernel<4>, grid, dim3(AT), 0, s, p); break;
+        if (p.n_streams == 2) {
+            switch (p.H / 16) {
+                case 1: hipLaunchKernelGGL((attn_mx_kernel<1, 2>), grid, dim3(2 * AT), 0, s, p); break;
+                case 2: hipLaunchKernelGGL((attn_mx_kernel<2, 2>), grid, dim3(2 * AT), 0, s, p); break;
+                case 3: hipLaunchKernelGGL((attn_mx_kernel<3, 2>), grid, dim3(2 * AT), 0, s, p); break;
+                default: hipLaunchKernelGGL((attn_mx_kernel<4, 2>), grid, dim3(2 * AT), 0, s, p); break;
+            }
+        } else {
+            switch (p.H / 16) {
+                case 1: hipLaunchKernelGGL((attn_mx_kernel<1, 1>), grid, dim3(AT), 0, s, p); break;
+                case 2: hipLaunchKernelGGL((attn_mx_kernel<2, 1>), grid, dim3(AT), 0, s, p); break;
+                case 3: hipLaunchKernelGGL((attn_mx_kernel<3, 1>), grid, dim3(AT), 0, s, p); break;
+                default: hipLaunchKernelGGL((attn_mx_kernel<4, 1>), grid, dim3(AT), 0, s, p); break;
+            }
         }
     }
     hipError_t e = hipGetLastError();

@@ -73,6 +73,7 @@ struct AttnPlan {
     int has_ent;
     int n_split;       // workgroups per query
     int keys_per_split;
+    int n_streams;     // FP8 path: key streams per workgroup (1 or 2)
     const int64_t *q_pos;
     const void *q;
     KvView ek, ev, wk, wv;

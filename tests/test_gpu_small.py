@@ -293,6 +293,26 @@ def test_attn_dense(fmt, override):
             assert_close_rms(o[b, i], ro, tol, f'o b{b} i{i}')
 
 
+def test_attn_dense_two_streams():
+    """A key list long enough (>= 4096 with the window) for the two-stream
+    workgroups, with queries that see all entries, part of them, and almost
+    none (ragged and empty tiles in both streams)."""
+    B, Tq, rows, m = 1, 3, 6000, 4
+    H, D = 64, 192
+    q_pos = np.array([[rows * m - 1, 9001, 130]], np.int64)
+    c = _attn_case(13, B, Tq, H, D, rows, q_pos, 'fp8')
+    ek, ev, wk, wv = _stores(c)
+    print('attn dense two streams', flush=True)
+    o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'])
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    for i in range(Tq):
+        t = int(q_pos[0, i])
+        n = min((t + 1) // m, rows)
+        ro, _ = _oracle_attn(c, 0, i, np.arange(n))
+        assert_close_rms(o[0, i], ro, TOL_BF16, f'o i{i} t{t}')
+
+
 @pytest.mark.parametrize('t_last', [128, 1000])
 def test_attn_window_only_ring(t_last):
     # one query per batch element at the ring's newest position, plus early positions
