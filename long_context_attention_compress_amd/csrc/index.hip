@@ -625,11 +625,12 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
 
 // ------------------------------------------------------ merge select ----
 
-constexpr int MBITS = 11;                 // radix digit of the merge select
+constexpr int MBITS = 12;                 // radix digit of the merge select
 constexpr int MBINS = 1 << MBITS;
-constexpr int RESOLVE_MAX = 64;           // a boundary bin this small is ranked by one wave
-constexpr int BPT = MBINS / MT;         // histogram bins per merge thread
-static_assert(BPT == 2, "each merge thread scans two bins");
+constexpr int RESOLVE_MAX = 128;          // a boundary bin this small is gathered and ranked directly
+constexpr int BPT = MBINS / MT;           // histogram bins per merge thread
+static_assert(BPT == 4, "each merge thread scans four bins (one 16-byte word)");
+constexpr int STAGE_MAX = 2048;           // selections staged in LDS for coalesced output
 
 // Per-key loops are kept free of branches: a key that does not count goes
 // to a dummy slot of its lane (the arrays carry 64 extra slots).
@@ -639,7 +640,7 @@ struct __attribute__((aligned(16))) MergeSmem {
     uint32_t red[3][MT / 64];
     uint32_t list[RESOLVE_MAX + 64] __attribute__((aligned(16)));
     uint32_t misc[4];
-    uint32_t stage_key[MBINS + 64];  // selected keys, staged for coalesced output
+    uint32_t stage_key[STAGE_MAX + 64];  // selected keys, staged for coalesced output
 };
 
 // Inclusive prefix sum over the workgroup. Consecutive calls must alternate
@@ -666,8 +667,8 @@ __device__ __forceinline__ uint32_t scan_buf(uint32_t v, MergeSmem &sm, int buf,
 __device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf, uint32_t *bin, uint32_t *above,
                                            uint32_t *in_bin, uint32_t *total) {
     const int b0 = MBINS - BPT * (threadIdx.x + 1);
-    const uint2 hv = *(const uint2 *)&sm.hist[b0];
-    const uint32_t h[BPT] = {hv.x, hv.y};
+    const uint4 h0 = *(const uint4 *)&sm.hist[b0];
+    const uint32_t h[BPT] = {h0.x, h0.y, h0.z, h0.w};
     uint32_t local = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) local += h[j];
@@ -685,7 +686,7 @@ __device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf
             acc += h[j];
         }
     }
-    *(uint2 *)&sm.hist[b0] = make_uint2(0, 0);
+    *(uint4 *)&sm.hist[b0] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     *bin = sm.misc[0];
     *above = sm.misc[1];
@@ -971,9 +972,9 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
     fence_keys(keys);
     uint32_t tb = ex & 0xFFFFu;
     uint32_t pos = (ex >> 16) + (tb < need_ties ? tb : need_ties);
-    // up to MBINS selections are staged in LDS (ids in the free histogram)
+    // up to STAGE_MAX selections are staged in LDS (ids in the free histogram)
     // and written out in order by consecutive lanes
-    const bool stage = kk <= MBINS;
+    const bool stage = kk <= STAGE_MAX;
     uint32_t *st_id = ms.hist;
     if (stage) {
 #pragma unroll
@@ -981,7 +982,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
             const bool eq = keys[i] == kth;
             const bool take = keys[i] > kth || (eq && tb < need_ties);
             tb += eq;
-            const uint32_t a = take ? pos : MBINS + lane;
+            const uint32_t a = take ? pos : STAGE_MAX + lane;
             st_id[a] = (uint32_t)ids[i];
             ms.stage_key[a] = keys[i];
             pos += take;
@@ -1018,7 +1019,7 @@ __global__ __launch_bounds__(MT) void index_merge_kernel(IndexPlan p) {
     uint32_t *pre = dyn;                                  // [n_chunks + 1] candidate offsets
     uint32_t *skey = dyn + p.n_chunks + 1;                // [chunk] (exact fallback)
     float *sq = (float *)(skey + p.chunk);                // f32 mode query
-    *(uint2 *)&ms.hist[BPT * tid] = make_uint2(0, 0);
+    *(uint4 *)&ms.hist[BPT * tid] = make_uint4(0, 0, 0, 0);
     if (MODE == 0) {
         const float *iq = (const float *)p.iq + (size_t)q * p.H * p.dI;
         for (int i = tid; i < p.H * p.dI; i += MT) sq[i] = iq[i];
