@@ -52,9 +52,9 @@ struct KeyInfo {
     int64_t t;
 };
 
-__device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int q) {
+__device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int64_t t) {
     KeyInfo ki;
-    ki.t = p.q_pos[q];
+    ki.t = t;
     if (ki.t < 0) {
         ki.n_list = 0;
         ki.n_win = 0;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(AT) void attn_f32_kernel(AttnPlan p) {
     const int tid = threadIdx.x;
     const int q = blockIdx.y, split = blockIdx.x;
     const int b = q / p.Tq;
-    const KeyInfo ki = key_info(p, q);
+    const KeyInfo ki = key_info(p, p.q_pos[q]);
     const float *qin = (const float *)p.q + (size_t)q * H * D;
     const int Dn = D - ROPE_DIM;
     for (int i = tid; i < H * D; i += AT) {
@@ -419,6 +419,9 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const int H = p.H;
     const bool active = wave < NW;
     const int head = 16 * wave + col;
+    // the position (a pointer, then the value: the longest scalar chain of the
+    // prologue) is asked for first
+    const int64_t t_pos = p.q_pos[q];
 
     // The query and (sparse) this split's selected ids do not depend on the
     // query position: their loads are issued before the position arrives.
@@ -430,13 +433,18 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     for (int c = 0; c < 2; ++c) qraw[c] = ld16(qp + MDN + 32 * c + 8 * g);
     constexpr int IDS = MAX_KS / (AT * NS);
     const int64_t j0 = (int64_t)split * p.keys_per_split;
+    // Id loads without per-lane branches (which would wait for each load in
+    // turn): clamped positions, a dense call reading a valid dummy address; the
+    // values are masked where they are used.
+    const int32_t *ip = p.sparse ? p.idx + (size_t)q * p.k : (const int32_t *)p.q_pos;
+    const int64_t jmax = p.sparse ? p.k - 1 : 0;
     int32_t ids[IDS];
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
-        const int i = tid + AT * NS * u;
-        ids[u] = (p.sparse && i < p.keys_per_split && j0 + i < p.k) ? p.idx[(size_t)q * p.k + j0 + i] : -1;
+        const int64_t j = j0 + tid + AT * NS * u;
+        ids[u] = ip[j < jmax ? j : jmax];
     }
-    const KeyInfo ki = key_info(p, q);
+    const KeyInfo ki = key_info(p, t_pos);
     const int64_t n_keys = ki.n_list + ki.n_win;
     const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
     const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
             int64_t row;
             bool win = false;
             if (j < ki.n_list) {
-                const int64_t e = p.sparse ? (int64_t)ids[u] : j;
+                const int64_t e = p.sparse ? (j < p.k ? (int64_t)ids[u] : -1) : j;
                 row = (e >= 0 && e < p.ek.rows) ? e : -1;
             } else {
                 row = key_row(p, q, ki, j, &win);
