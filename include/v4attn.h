@@ -243,6 +243,17 @@ int lightning_index_topk(const v4a_index_args *a, void *workspace, size_t worksp
  *  sm_scale  logit scale; 0 means 1/sqrt(dim).
  *  o         [B][Tq][H_q][dim] in o_fmt.
  *  lse       [B][Tq][H_q] float32 or NULL.
+ *  append_k/v  optional fused window append (decode): the query tokens' raw
+ *          K and V rows [B][Tq][dim] bfloat16, 4-byte aligned. Each is first
+ *          written into win_k/win_v at its query position t, with the bytes
+ *          that csa_compress with m = 1 at pos0 = t writes (the pooling of
+ *          one token is the identity; K is rotated at t), and the attention
+ *          then sees it as the window row of t. Needs E4M3_BF16 stores,
+ *          Tq == 1 and W >= 1 (else EFORMAT / EINVAL); both NULL: no append.
+ *          A position past a linear window store's rows writes nothing.
+ *          [chaosnode.de, "DeepSeek-V4: 1 Million Token Context endlich
+ *          nutzbar", section "Hybrid Attention: CSA und HCA"]: the window
+ *          of the last 128 raw tokens includes the current one.
  * Supported: all stores F32 with q and o float32, dim 128, H_q * dim <= 4096;
  * or all stores E4M3_BF16 with dim == 192, q bfloat16, o float32 or bfloat16,
  * and H_q in {16, 32, 48, 64}. (A bfloat16 output carries its own rounding of
@@ -267,6 +278,8 @@ typedef struct {
     int32_t o_fmt;
     void *o;
     float *lse;
+    const void *append_k;
+    const void *append_v;
 } v4a_attn_args;
 
 /* CSA: keys are the entries listed in topk_idx[b][i][0..k) (ids < 0 or not

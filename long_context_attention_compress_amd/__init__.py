@@ -232,7 +232,7 @@ def lightning_index_topk(q_pos, iq, w, keys, k, m, iq_scale=None, out_idx=None, 
     return call if prepare else out_idx
 
 
-def _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse):
+def _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse, append_k, append_v):
     _need(q, 'q')
     _need(q_pos, 'q_pos', torch.int64)
     B, Tq, H, D = q.shape
@@ -248,32 +248,42 @@ def _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, 
     a.sm_scale, a.rope_base = sm_scale, rope_base
     a.o_fmt, a.o = _act(_need(o, 'o')), _ptr(o)
     a.lse = _ptr(lse) if lse is not None else None
+    if append_k is not None or append_v is not None:
+        a.append_k = _ptr(_need(append_k, 'append_k', torch.bfloat16))
+        a.append_v = _ptr(_need(append_v, 'append_v', torch.bfloat16))
     return a, o
 
 
 def sparse_window_attn(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, idx, sm_scale=0.0,
-                       rope_base=10000.0, o=None, lse=None, workspace=None, stream=None, prepare=False):
-    """CSA attention over the entries idx [B, Tq, k] (int32, -1 padded) plus the window."""
-    a, o = _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse)
+                       rope_base=10000.0, o=None, lse=None, workspace=None, stream=None, prepare=False,
+                       append_k=None, append_v=None):
+    """CSA attention over the entries idx [B, Tq, k] (int32, -1 padded) plus the window.
+
+    append_k/append_v [B, 1, dim] bfloat16 (decode): the query tokens' raw rows, first
+    written into the window stores at the query positions (fused window append)."""
+    a, o = _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse, append_k, append_v)
     _need(idx, 'idx', torch.int32)
     k = idx.shape[-1]
     L = lib()
     nbytes = L.sparse_window_attn_workspace(ctypes.byref(a), k)
     ws = _workspace(workspace, q, 'attn')
     ptr, size = ws.get(nbytes, stream)
-    keep = (a, q, q_pos, ent_k, ent_v, win_k, win_v, idx, o, lse, ws.buf)
+    keep = (a, q, q_pos, ent_k, ent_v, win_k, win_v, idx, o, lse, append_k, append_v, ws.buf)
     call = _finish(L.sparse_window_attn, (ctypes.byref(a), _ptr(idx), k, ptr, size, _stream(stream)), keep, prepare)
     return call if prepare else o
 
 
 def hca_attn(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, n_entries_override=-1, sm_scale=0.0,
-             rope_base=10000.0, o=None, lse=None, workspace=None, stream=None, prepare=False):
-    """HCA attention over every visible entry plus the window (n_entries_override=0: window only)."""
-    a, o = _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse)
+             rope_base=10000.0, o=None, lse=None, workspace=None, stream=None, prepare=False,
+             append_k=None, append_v=None):
+    """HCA attention over every visible entry plus the window (n_entries_override=0: window only).
+
+    append_k/append_v: fused window append, as in sparse_window_attn."""
+    a, o = _attn_args(q, q_pos, ent_k, ent_v, m, win_k, win_v, W, sm_scale, rope_base, o, lse, append_k, append_v)
     L = lib()
     nbytes = L.hca_attn_workspace(ctypes.byref(a), n_entries_override)
     ws = _workspace(workspace, q, 'attn')
     ptr, size = ws.get(nbytes, stream)
-    keep = (a, q, q_pos, ent_k, ent_v, win_k, win_v, o, lse, ws.buf)
+    keep = (a, q, q_pos, ent_k, ent_v, win_k, win_v, o, lse, append_k, append_v, ws.buf)
     call = _finish(L.hca_attn, (ctypes.byref(a), n_entries_override, ptr, size, _stream(stream)), keep, prepare)
     return call if prepare else o

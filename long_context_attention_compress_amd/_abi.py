@@ -50,7 +50,8 @@ class AttnArgs(ctypes.Structure):
                 ('q_fmt', c_i32), ('q', c_p),
                 ('ent_k', ctypes.POINTER(KvStoreC)), ('ent_v', ctypes.POINTER(KvStoreC)), ('m', c_i32),
                 ('win_k', ctypes.POINTER(KvStoreC)), ('win_v', ctypes.POINTER(KvStoreC)), ('W', c_i32),
-                ('sm_scale', c_f), ('rope_base', c_d), ('o_fmt', c_i32), ('o', c_p), ('lse', c_p)]
+                ('sm_scale', c_f), ('rope_base', c_d), ('o_fmt', c_i32), ('o', c_p), ('lse', c_p),
+                ('append_k', c_p), ('append_v', c_p)]
 
 
 EXPORTS = {

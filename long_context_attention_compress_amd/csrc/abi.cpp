@@ -253,6 +253,13 @@ int check_attn(const v4a_attn_args *a, AttnPlan *P) {
         if (!aligned(a->q, 16) || !aligned(a->o, 16)) return fail(V4A_EALIGN, "q and o must be 16-byte aligned");
     }
     if (!aligned(a->q_pos, 8) || (a->lse && !aligned(a->lse, 4))) return fail(V4A_EALIGN, "q_pos/lse misaligned");
+    if (a->append_k || a->append_v) {
+        if (!a->append_k || !a->append_v) return fail(V4A_ENULL, "append_k and append_v must both be given or both NULL");
+        if (fmt != V4A_KV_E4M3_BF16) return fail(V4A_EFORMAT, "the fused window append needs E4M3_BF16 stores");
+        if (a->Tq != 1) return fail(V4A_EINVAL, "the fused window append needs Tq == 1 (got %d)", a->Tq);
+        if (a->W < 1) return fail(V4A_EINVAL, "the fused window append needs W >= 1");
+        if (!aligned(a->append_k, 4) || !aligned(a->append_v, 4)) return fail(V4A_EALIGN, "append_k/append_v must be 4-byte aligned");
+    }
     if (!(a->sm_scale >= 0.0f) || !isfinite(a->sm_scale)) return fail(V4A_EINVAL, "sm_scale must be finite and >= 0");
     if ((int64_t)a->B * a->Tq > (1 << 24)) return fail(V4A_EINVAL, "too many queries");
     P->Q = a->B * a->Tq;
@@ -269,6 +276,9 @@ int check_attn(const v4a_attn_args *a, AttnPlan *P) {
     P->o = a->o;
     P->o_bf16 = a->o_fmt == V4A_ACT_BF16;
     P->lse = a->lse;
+    P->has_app = a->append_k != nullptr;
+    P->app_k = (const uint16_t *)(P->has_app ? a->append_k : a->q);
+    P->app_v = (const uint16_t *)(P->has_app ? a->append_v : a->q);
     return V4A_OK;
 }
 
@@ -423,6 +433,9 @@ int sparse_window_attn(const v4a_attn_args *a, const int32_t *idx, int32_t k, vo
     P.sparse = 1;
     P.k = k;
     P.idx = idx;
+    P.id_src = idx;
+    P.id_stride = k;
+    P.id_jmax = k - 1;
     P.n_override = -1;
     return run_attn(P, attn_layout(a, true, k, -1), ws, ws_bytes, (hipStream_t)stream);
 }
@@ -440,6 +453,9 @@ int hca_attn(const v4a_attn_args *a, int64_t n_override, void *ws, size_t ws_byt
     P.sparse = 0;
     P.k = 0;
     P.idx = nullptr;
+    P.id_src = (const int32_t *)a->q_pos;
+    P.id_stride = 0;
+    P.id_jmax = 0;
     P.n_override = n_override;
     if (n_override == 0) P.has_ent = 0;
     return run_attn(P, attn_layout(a, false, 0, n_override), ws, ws_bytes, (hipStream_t)stream);

@@ -32,6 +32,11 @@
 //    ahead of the tile being computed.
 //  * The running max is raised lazily (only when a tile beats it by 2^8), so
 //    the 48 accumulator registers are rarely rescaled.
+//  * Fused window append (decode): the workgroup whose split holds the query
+//    token's own key (the last window row) encodes the token's raw K and V
+//    rows exactly as the m = 1 compressor does, writes them into the window
+//    stores and stages them from LDS in place of the store's old contents;
+//    this saves the separate append launch.
 
 #include "common.hpp"
 
@@ -233,6 +238,16 @@ struct TileBuf {
     float vsc[TK] __attribute__((aligned(16)));
 };
 
+// The row of a fused window append, encoded as the stores hold it: E4M3
+// codes and BF16 RoPE pairs of K and V, and the two row scales.
+struct AppRow {
+    uint8_t kc[MDN] __attribute__((aligned(16)));
+    uint8_t kr[2 * ROPE_DIM] __attribute__((aligned(16)));
+    uint8_t vc[MDN] __attribute__((aligned(16)));
+    uint8_t vr[2 * ROPE_DIM] __attribute__((aligned(16)));
+    float ksc, vsc;
+};
+
 // NS key streams per workgroup, each with its own tile buffer; at the end the
 // streams' partial results meet in the (then free) tile buffers.
 template <int NS>
@@ -242,6 +257,7 @@ struct MxSmem {
     double rsin[ROPE_PAIRS];
     int32_t rows[MAX_KS];       // row of each key of the split; bit 30 marks a window row; -1: no key
     float xml[NS > 1 ? 2 * AT : 1];
+    AppRow app;
 };
 
 constexpr int32_t WIN_BIT = 1 << 30;
@@ -337,8 +353,12 @@ __device__ __forceinline__ void store_codes(__bf16 *dst, const v4i &c) {
     *(v4i *)(dst + 8) = hi;
 }
 
+// `cur`: the split-relative key of a fused append (-1: none). The threads
+// that stage its slot then overwrite it with the encoded row from LDS (the
+// same threads, so the later store wins), in place of the loaded (previous)
+// store contents.
 __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *rows, TileBuf &sm, int rel, int n_rel,
-                                           int tid) {
+                                           int tid, const AppRow &app, int cur) {
     const int part = tid & 15;
     const v4i z = {0, 0, 0, 0};
 #pragma unroll
@@ -359,6 +379,22 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *row
         sm.kbias[tid] = (rel + tid < n_rel && rows[rel + tid] >= 0) ? 0.f : -__builtin_inff();
     } else if (tid < 2 * TK) {
         sm.vsc[tid - TK] = sc;
+    }
+    if (cur >= rel && cur < rel + TK) {  // uniform: this tile holds the appended key
+        const int r = cur - rel;
+        if ((tid >> 4) == (r & 15)) {
+            const v4i kx = *(const v4i *)(part < 8 ? &app.kc[16 * part] : &app.kr[16 * (part - 8)]);
+            const v4i vx = *(const v4i *)(part < 8 ? &app.vc[16 * part] : &app.vr[16 * (part - 8)]);
+            if (part < 8) {
+                store_codes(&sm.kb[r * KB_LD + 16 * part], kx);
+                store_codes(&sm.vb[r * KB_LD + 16 * part], vx);
+            } else {
+                *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * (part - 8)] = kx;
+                *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * (part - 8)] = vx;
+            }
+        }
+        if (tid == r) sm.ksc[r] = app.ksc;
+        if (tid == TK + r) sm.vsc[r] = app.vsc;
     }
 }
 
@@ -420,9 +456,9 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const bool active = wave < NW;
     const int head = 16 * wave + col;
     // the position (a pointer, then the value: the longest scalar chain of the
-    // prologue) is asked for first
+    // prologue) is asked for first, ahead of everything below
     const int64_t t_pos = p.q_pos[q];
-
+    __builtin_amdgcn_sched_barrier(0);
     // The query and (sparse) this split's selected ids do not depend on the
     // query position: their loads are issued before the position arrives.
     const __bf16 *qp = (const __bf16 *)p.q + ((size_t)q * H + (active ? head : 0)) * MD;
@@ -436,8 +472,8 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // Id loads without per-lane branches (which would wait for each load in
     // turn): clamped positions, a dense call reading a valid dummy address; the
     // values are masked where they are used.
-    const int32_t *ip = p.sparse ? p.idx + (size_t)q * p.k : (const int32_t *)p.q_pos;
-    const int64_t jmax = p.sparse ? p.k - 1 : 0;
+    const int32_t *ip = p.id_src + q * p.id_stride;
+    const int64_t jmax = p.id_jmax;
     int32_t ids[IDS];
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
@@ -448,6 +484,20 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const int64_t n_keys = ki.n_list + ki.n_win;
     const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
     const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
+    // Fused window append: the token's own key is the last of the list (the
+    // window row at t). The workgroup whose split holds it reads the token's
+    // raw K and V rows, one 32-bit word (two BF16 values) per lane of its last
+    // three waves: the last wave K's no-RoPE dims 2l, 2l + 1, the one before
+    // V's, and the third last the RoPE pairs (K's on lanes 0..31, V's on
+    // 32..63). Only these waves read them, so the rows are not a hot spot.
+    const int aw = (AT * NS - 1 - tid) >> 6;
+    const bool app_here = p.has_app && ki.n_win > 0 && n_keys - 1 >= j0 && n_keys - 1 < j1;  // uniform
+    uint32_t araw = 0;
+    if (app_here && aw < 3) {
+        const uint32_t *rk = (const uint32_t *)(p.app_k + (size_t)q * MD);
+        const uint32_t *rv = (const uint32_t *)(p.app_v + (size_t)q * MD);
+        araw = aw == 0 ? rk[lane] : aw == 1 ? rv[lane] : lane < 32 ? rk[MDN / 2 + lane] : rv[MDN / 2 - 32 + lane];
+    }
     // resolve the split's keys to store rows once, and the RoPE table
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
@@ -589,16 +639,60 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     TileRegs RA, RB;
     load_tile(src, sm.rows, TK * stream, n_rel, RA, tids);
     load_tile(src, sm.rows, TK * (stream + NS), n_rel, RB, tids);
+    // The workgroup holding the appended key encodes the row while the first
+    // tiles are in flight (the loop's first barrier publishes it).
+    int cur = -1;
+    if (app_here) {
+        const int c = (int)(n_keys - 1 - j0);
+        if (sm.rows[c] >= 0) cur = c;
+    }
+    // three waves split the encoding: the no-RoPE codes of K (the last
+    // wave) and of V (the one before), and both RoPE pairs (the third last)
+    if (cur >= 0 && aw < 3) {
+        const int64_t row = sm.rows[cur] & (WIN_BIT - 1);
+        const uint32_t raw = araw;
+        if (aw < 2) {
+            const bool isk = aw == 0;
+            const KvView &st = isk ? p.wk : p.wv;
+            uint8_t c0, c1;
+            const float sc = e4m3_group128(bf16_decode((uint16_t)raw), bf16_decode((uint16_t)(raw >> 16)), &c0, &c1);
+            const uint16_t cc = (uint16_t)(c0 | (c1 << 8));
+            ((uint16_t *)(isk ? sm.app.kc : sm.app.vc))[lane] = cc;
+            ((uint16_t *)(st.nope + b * st.nope_bs + row * st.nope_rs))[lane] = cc;
+            if (lane == 0) {
+                *(isk ? &sm.app.ksc : &sm.app.vsc) = sc;
+                *(float *)(st.scale + b * st.scale_bs + row * st.scale_rs) = sc;
+            }
+        } else {
+            // K's pair rotated at t (lanes 0..31), V's as it is (lanes 32..63)
+            const int lr = lane & 31;
+            const bool isk = lane < 32;
+            uint32_t bits;
+            if (isk) {
+                double xr, yr;
+                rope_rotate((double)bf16_decode((uint16_t)raw), (double)bf16_decode((uint16_t)(raw >> 16)),
+                            sm.rsin[lr], sm.rcos[lr], &xr, &yr);
+                bits = (uint32_t)bf16_encode((float)xr) | ((uint32_t)bf16_encode((float)yr) << 16);
+            } else {
+                bits = (uint32_t)bf16_encode(bf16_decode((uint16_t)raw)) |
+                       ((uint32_t)bf16_encode(bf16_decode((uint16_t)(raw >> 16))) << 16);
+            }
+            ((uint32_t *)(isk ? sm.app.kr : sm.app.vr))[lr] = bits;
+            const char *rp = isk ? p.wk.rope + b * p.wk.rope_bs + row * p.wk.rope_rs
+                                 : p.wv.rope + b * p.wv.rope_bs + row * p.wv.rope_rs;
+            ((uint32_t *)rp)[lr] = bits;
+        }
+    }
     for (int i = 0; i < n_rounds; i += 2) {
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         __syncthreads();
-        stage_tile(RA, sm.rows, tb, ta * TK, n_rel, tids);
+        stage_tile(RA, sm.rows, tb, ta * TK, n_rel, tids, sm.app, cur);
         load_tile(src, sm.rows, (ta + 2 * NS) * TK, n_rel, RA, tids);
         __syncthreads();
         if (ta < n_tiles) compute();
         if (i + 1 >= n_rounds) break;
         __syncthreads();
-        stage_tile(RB, sm.rows, tb, tb_ * TK, n_rel, tids);
+        stage_tile(RB, sm.rows, tb, tb_ * TK, n_rel, tids, sm.app, cur);
         load_tile(src, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
         __syncthreads();
         if (tb_ < n_tiles) compute();

@@ -190,6 +190,33 @@ __device__ __forceinline__ void rope_sincos(double x, double *sn, double *cs) {
     }
 }
 
+// One RoPE pair rotated by the angle with sine sn and cosine cs, in float64.
+// Contraction is off, so every kernel that rotates a raw key row (the
+// compressor and the attention kernels' fused window append) rounds the same
+// products the same way and writes the same bits.
+__device__ __forceinline__ void rope_rotate(double x, double y, double sn, double cs, double *xr, double *yr) {
+#pragma clang fp contract(off)
+    *xr = x * cs - y * sn;
+    *yr = x * sn + y * cs;
+}
+
+// ---------------------------------------------------------- E4M3 KV rows ----
+// E4M3 codes of one 128-dim no-RoPE group that a wave holds as two values per
+// lane (any two dims: each code depends only on its value and the group's
+// scale), under the group's float32 scale amax / 448 (1 for an all-zero
+// group; a NaN in the group makes the scale, and so every code, NaN).
+// Returns the scale.
+__device__ __forceinline__ float e4m3_group128(float x0, float x1, uint8_t *c0, uint8_t *c1) {
+    float a = amax_acc(0.0f, x0);
+    a = amax_acc(a, x1);
+    a = wave_amax_bits(a);
+    float sc = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
+    if (__builtin_isnan(a)) sc = a;
+    *c0 = e4m3_encode(__fdiv_rn(x0, sc));
+    *c1 = e4m3_encode(__fdiv_rn(x1, sc));
+    return sc;
+}
+
 // --------------------------------------------------- order-preserving key ----
 // Larger float -> larger key; -0 == +0; NaN -> 0 (below every number).
 __device__ __forceinline__ uint32_t score_key(float s) {

@@ -46,13 +46,10 @@ __device__ void store_kv_row(const KvView &s, int b, int64_t row, const float *n
     uint8_t *codes = (uint8_t *)(s.nope + b * s.nope_bs + row * s.nope_rs);
     float *scales = (float *)(s.scale + b * s.scale_bs + row * s.scale_rs);
     for (int g = 0; g < n_nope_it / 2; ++g) {  // groups of 128 dims = two lane iterations
-        float a = amax_acc(0.0f, nope[2 * g]);
-        a = amax_acc(a, nope[2 * g + 1]);
-        a = wave_amax_bits(a);
-        float sc = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
-        if (__builtin_isnan(a)) sc = a;
-        codes[128 * g + lane] = e4m3_encode(__fdiv_rn(nope[2 * g], sc));
-        codes[128 * g + 64 + lane] = e4m3_encode(__fdiv_rn(nope[2 * g + 1], sc));
+        uint8_t c0, c1;
+        const float sc = e4m3_group128(nope[2 * g], nope[2 * g + 1], &c0, &c1);
+        codes[128 * g + lane] = c0;
+        codes[128 * g + 64 + lane] = c1;
         if (lane == 0) scales[g] = sc;
     }
     if (lane < ROPE_PAIRS) {
@@ -137,10 +134,9 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
                     double x = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane);
                     double y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
                     if (which == 0) {
-                        double sn, cs;
+                        double sn, cs, xr, yr;
                         rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
-                        double xr = x * cs - y * sn;
-                        double yr = x * sn + y * cs;
+                        rope_rotate(x, y, sn, cs, &xr, &yr);
                         x = xr;
                         y = yr;
                     }
@@ -253,34 +249,54 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
 
     if (do_kv) {
         float nk[4], nv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            double ak = 0.0, av = 0.0;
-#pragma unroll
-            for (int r = 0; r < M; ++r) {
-                ak += alpha[r] * (double)bits_val<ACT>(kn[r][i]);
-                av += alpha[r] * (double)bits_val<ACT>(vn[r][i]);
-            }
-            nk[i] = (float)ak;
-            nv[i] = (float)av;
-        }
         float rkx = 0.f, rky = 0.f, rvx = 0.f, rvy = 0.f;
-        if (rl) {
-            double akx = 0.0, aky = 0.0, avx = 0.0, avy = 0.0;
+        if constexpr (M == 1) {
+            // one token: the pooling is the identity (alpha = 1 for any finite
+            // gate) and the gate is not used. The attention kernels' fused
+            // window append computes this same row with the same operations.
 #pragma unroll
-            for (int r = 0; r < M; ++r) {
-                double sn, cs;
-                rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
-                const double x = bits_val<ACT>(kx[r]), y = bits_val<ACT>(ky[r]);
-                akx += alpha[r] * (x * cs - y * sn);
-                aky += alpha[r] * (x * sn + y * cs);
-                avx += alpha[r] * (double)bits_val<ACT>(vx[r]);
-                avy += alpha[r] * (double)bits_val<ACT>(vy[r]);
+            for (int i = 0; i < 4; ++i) {
+                nk[i] = bits_val<ACT>(kn[0][i]);
+                nv[i] = bits_val<ACT>(vn[0][i]);
             }
-            rkx = (float)akx;
-            rky = (float)aky;
-            rvx = (float)avx;
-            rvy = (float)avy;
+            if (rl) {
+                double sn, cs, xr, yr;
+                rope_sincos((double)(p.pos0 + tok0) * f, &sn, &cs);
+                rope_rotate((double)bits_val<ACT>(kx[0]), (double)bits_val<ACT>(ky[0]), sn, cs, &xr, &yr);
+                rkx = (float)xr;
+                rky = (float)yr;
+                rvx = bits_val<ACT>(vx[0]);
+                rvy = bits_val<ACT>(vy[0]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                double ak = 0.0, av = 0.0;
+#pragma unroll
+                for (int r = 0; r < M; ++r) {
+                    ak += alpha[r] * (double)bits_val<ACT>(kn[r][i]);
+                    av += alpha[r] * (double)bits_val<ACT>(vn[r][i]);
+                }
+                nk[i] = (float)ak;
+                nv[i] = (float)av;
+            }
+            if (rl) {
+                double akx = 0.0, aky = 0.0, avx = 0.0, avy = 0.0;
+#pragma unroll
+                for (int r = 0; r < M; ++r) {
+                    double sn, cs, xr, yr;
+                    rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                    rope_rotate((double)bits_val<ACT>(kx[r]), (double)bits_val<ACT>(ky[r]), sn, cs, &xr, &yr);
+                    akx += alpha[r] * xr;
+                    aky += alpha[r] * yr;
+                    avx += alpha[r] * (double)bits_val<ACT>(vx[r]);
+                    avy += alpha[r] * (double)bits_val<ACT>(vy[r]);
+                }
+                rkx = (float)akx;
+                rky = (float)aky;
+                rvx = (float)avx;
+                rvy = (float)avy;
+            }
         }
         store_kv_row(p.k, b, kv_row(p.k, entry), nk, nit, rkx, rky);
         store_kv_row(p.v, b, kv_row(p.v, entry), nv, nit, rvx, rvy);
@@ -290,11 +306,17 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (i >= nit_i) break;
-            double acc = 0.0;
-#pragma unroll
-            for (int r = 0; r < M; ++r) acc += alpha[r] * (double)bits_val<ACT>(lane + 64 * i < dI ? ui[r][i] : 0u);
             const int d = lane + 64 * i;
-            store_ik_value(p.ik, b, entry, d, d < dI, (float)acc);
+            float x;
+            if constexpr (M == 1) {
+                x = bits_val<ACT>(d < dI ? ui[0][i] : 0u);
+            } else {
+                double acc = 0.0;
+#pragma unroll
+                for (int r = 0; r < M; ++r) acc += alpha[r] * (double)bits_val<ACT>(d < dI ? ui[r][i] : 0u);
+                x = (float)acc;
+            }
+            store_ik_value(p.ik, b, entry, d, d < dI, x);
         }
     }
 }

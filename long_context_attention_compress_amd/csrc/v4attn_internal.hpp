@@ -78,6 +78,11 @@ struct AttnPlan {
     const void *q;
     KvView ek, ev, wk, wv;
     const int32_t *idx;
+    // where the FP8 kernel reads the ids of query q's list (position j <=
+    // id_jmax): id_src + q * id_stride; a dense call reads a valid dummy
+    // (q_pos) there, so the loads need no branch
+    const int32_t *id_src;
+    int64_t id_stride, id_jmax;
     float sm_scale;
     double inv_freq[ROPE_PAIRS];
     void *o;
@@ -85,6 +90,12 @@ struct AttnPlan {
     float *lse;
     float *part_o;   // [Q][n_split][H][D]
     float *part_ml;  // [Q][n_split][H][2]
+    // fused window append (FP8 path, one query token per sequence): raw BF16
+    // K and V rows [Q][D] of the query tokens, written into the window stores
+    // at the query positions before they are attended (has_app = 1); without
+    // an append both point at q (read, never used)
+    int has_app;
+    const uint16_t *app_k, *app_v;
 };
 
 hipError_t launch_compress(const CompressPlan &p, hipStream_t s);

@@ -161,3 +161,19 @@ def test_attention_rejections():
     ring_ent = _kv(ring=64)
     r, _ = _status('hca_attn', args(ent_k=ctypes.pointer(ring_ent)), -1, FAKE, 1 << 30, None)
     assert r == _abi.V4A_EINVAL
+    # fused window append: both rows or neither, one query token per sequence,
+    # a window, 4-byte alignment, FP8 stores only
+    app = dict(append_k=FAKE, append_v=FAKE)
+    f32s = [ctypes.pointer(_kv(fmt=_abi.KV_F32, dim=128, ring=r_, rows=128 if r_ else 4096)) for r_ in (0, 0, 128, 128)]
+    f32_args = dict(ent_k=f32s[0], ent_v=f32s[1], win_k=f32s[2], win_v=f32s[3], dim=128, H_q=16,
+                    q_fmt=_abi.ACT_F32, o_fmt=_abi.ACT_F32)
+    assert lib.hca_attn_workspace(args(**f32_args), -1) > 0   # valid without the append
+    app_cases = [(dict(append_k=FAKE), _abi.V4A_ENULL), (dict(append_v=FAKE), _abi.V4A_ENULL),
+                 (dict(app, Tq=2), _abi.V4A_EINVAL), (dict(app, W=0), _abi.V4A_EINVAL),
+                 (dict(app, append_v=FAKE + 2), _abi.V4A_EALIGN), (dict(app, **f32_args), _abi.V4A_EFORMAT)]
+    for kw, want in app_cases:
+        r, msg = _status('hca_attn', args(**kw), -1, FAKE, 1 << 30, None)
+        assert r == want, (kw, r, msg)
+    r, msg = _status('sparse_window_attn', args(**dict(app, Tq=3)), FAKE, 1024, FAKE, 1 << 30, None)
+    assert r == _abi.V4A_EINVAL and 'Tq' in msg, (r, msg)
+    assert lib.hca_attn_workspace(args(**app), -1) > 0

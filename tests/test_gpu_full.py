@@ -58,7 +58,9 @@ def _decode_check(x, cfg, k, idx, o, ik_deq, iq_deq, m, N, run_oracle_sel):
     return swaps
 
 
-def _csa_decode(x, cfg, k):
+def _csa_decode(x, cfg, k, fused=False):
+    """fused: the newest window row (position t) is appended by the attention
+    launch itself (bfloat16 raw rows), as the decode benchmark runs it."""
     B, N, D = x['ent_k'].shape
     t = int(x['q_pos'][0, 0])
     W, m = cfg['W'], cfg['m']
@@ -73,13 +75,20 @@ def _csa_decode(x, cfg, k):
                         dev(kf), dev(vf), ks, vs)
         return ks, vs
     ek, ev = kv_pair(x['ent_k'], x['ent_v'], 0)
-    wk, wv = kv_pair(x['win_k'], x['win_v'], t - W + 1, ring=W)
+    app = {}
+    if fused:
+        for n in ('win_k', 'win_v'):
+            x[n][:, -1] = synth.to_bf16_values(x[n][:, -1])
+        wk, wv = kv_pair(x['win_k'][:, :-1], x['win_v'][:, :-1], t - W + 1, ring=W)
+        app = dict(append_k=bf16_dev(x['win_k'][:, -1:]), append_v=bf16_dev(x['win_v'][:, -1:]))
+    else:
+        wk, wv = kv_pair(x['win_k'], x['win_v'], t - W + 1, ring=W)
     pos = dev(x['q_pos'])
     q = bf16_dev(x['q'])
     print(f'csa decode B={B} N={N} k={k}: index', flush=True)
     idx = v4.lightning_index_topk(pos, dev(iqp), dev(x['w']), ik, k, m, iq_scale=dev(iqs))
-    print('sparse attention', flush=True)
-    o = v4.sparse_window_attn(q, pos, ek, ev, m, wk, wv, W, idx)
+    print(f'sparse attention (fused append: {fused})', flush=True)
+    o = v4.sparse_window_attn(q, pos, ek, ev, m, wk, wv, W, idx, **app)
     torch.cuda.synchronize()
 
     def rerun(b, sel):
@@ -103,9 +112,10 @@ def test_c1_csa_decode_64k():
 
 
 def test_c3_csa_decode_1m():
-    """1M context, batch 4, top-1024, 64 planted winners per query: every query checked."""
+    """1M context, batch 4, top-1024, 64 planted winners per query: every query checked
+    (the newest window row appended inside the attention launch, as the decode benchmark runs)."""
     cfg, x = synth.c3(3)
-    _csa_decode(x, cfg, cfg['k'])
+    _csa_decode(x, cfg, cfg['k'], fused=True)
 
 
 def test_c2_hca_decode_1m():
@@ -119,7 +129,7 @@ def test_c2_hca_decode_1m():
     N = T // m
     ek, ev = v4.KVStore.empty(B, N, D), v4.KVStore.empty(B, N, D)
     wk, wv = v4.KVStore.empty(B, W, D, ring=W), v4.KVStore.empty(B, W, D, ring=W)
-    raws = []
+    raws, app_k, app_v = [], [], []
     for b in range(B):
         print(f'c2 batch {b}: generate + compress', flush=True)
         r = synth.c2_batch(2, b)
@@ -128,13 +138,16 @@ def test_c2_hca_decode_1m():
                                   scale=s.scale[b:b + 1])
         rk, rv = bf16_dev(r['raw_k']), bf16_dev(r['raw_v'])
         v4.csa_compress(dev(r['gate']), dev(r['pos_bias']), 0, rk, rv, sl(ek), sl(ev))
-        v4.csa_compress(torch.zeros(1, W, device='cuda'), torch.zeros(1, device='cuda'), T - W,
-                        rk[:, T - W:].contiguous(), rv[:, T - W:].contiguous(), sl(wk), sl(wv))
+        # window: the last W - 1 tokens here, the newest one appended by the attention launch
+        v4.csa_compress(torch.zeros(1, W - 1, device='cuda'), torch.zeros(1, device='cuda'), T - W,
+                        rk[:, T - W:T - 1].contiguous(), rv[:, T - W:T - 1].contiguous(), sl(wk), sl(wv))
+        app_k.append(rk[:, T - 1:].clone())
+        app_v.append(rv[:, T - 1:].clone())
         del rk, rv
     q = bf16_dev(xq['q'])
     pos = dev(xq['q_pos'])
-    print('hca attention', flush=True)
-    o = v4.hca_attn(q, pos, ek, ev, m, wk, wv, W)
+    print('hca attention (fused window append)', flush=True)
+    o = v4.hca_attn(q, pos, ek, ev, m, wk, wv, W, append_k=torch.cat(app_k), append_v=torch.cat(app_v))
     torch.cuda.synchronize()
     o = o.cpu().numpy()
     g = np.random.default_rng(0)

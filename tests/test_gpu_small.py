@@ -341,6 +341,89 @@ def test_attn_window_only_first_positions():
         assert_close_rms(o[0, i], ro, TOL_BF16, f'o i{i}')
 
 
+def _batch_view(st, b):
+    return v4.KVStore(st.fmt, st.dim, st.ring, nope=st.nope[b:b + 1], rope=st.rope[b:b + 1],
+                      scale=st.scale[b:b + 1])
+
+
+# (kind, B, rows, k, q positions, window ring): the fused append's key in a
+# sparse split (linear window store and ring), in a short linear window
+# (t = 60), in a two-stream dense workgroup, and in a window-only layer.
+# Queries of one case that use a ring share their position.
+APPEND_CASES = [
+    ('sparse', 2, 1000, 192, [3999, 3001], 0),
+    ('sparse', 2, 1000, 192, [3999, 3999], 200),
+    ('dense', 2, 700, 0, [2799, 60], 0),
+    ('dense', 1, 6000, 0, [23999], 130),
+    ('window', 1, 8, 0, [1000], 129),
+]
+
+
+@pytest.mark.parametrize('case', range(len(APPEND_CASES)))
+def test_attn_fused_window_append(case):
+    """Attention with the fused window append against csa_compress (m = 1) then
+    attention without it: bitwise-equal window stores and outputs. The appended
+    row also equals the oracle's m = 1 compression of the raw row, and the
+    output matches the oracle over the updated window."""
+    kind, B, rows, k, pos, ring = APPEND_CASES[case]
+    m = 4
+    q_pos = np.array(pos, np.int64).reshape(B, 1)
+    c = _attn_case(40 + case, B, 1, 64, 192, rows, q_pos, 'fp8', ring=ring)
+    raw_k = synth.to_bf16_values(synth.normal(40 + case, 'app/k', (B, 1, 192), 1.0, 0.01))
+    raw_v = synth.to_bf16_values(synth.normal(40 + case, 'app/v', (B, 1, 192), 1.0, 0.01))
+    idx = None
+    if kind == 'sparse':
+        g = np.random.default_rng(41)
+        idx = np.stack([np.sort(g.choice(rows, k, replace=False)) for _ in range(B)]).astype(np.int32)[:, None]
+    override = 0 if kind == 'window' else -1
+
+    def attend(stores, app):
+        ek, ev, wk, wv = stores
+        kw = dict(append_k=bf16_dev(raw_k), append_v=bf16_dev(raw_v)) if app else {}
+        if kind == 'sparse':
+            return v4.sparse_window_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'], dev(idx), **kw)
+        return v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'], n_entries_override=override, **kw)
+
+    print(f'attn fused append case {case} ({kind}, t={pos})', flush=True)
+    sa = _stores(c)
+    for b in range(B):
+        v4.csa_compress(torch.zeros(1, 1, device='cuda'), torch.zeros(1, device='cuda'), int(q_pos[b, 0]),
+                        bf16_dev(raw_k[b:b + 1]), bf16_dev(raw_v[b:b + 1]), _batch_view(sa[2], b),
+                        _batch_view(sa[3], b))
+    oa = attend(sa, False)
+    sb = _stores(c)
+    ob = attend(sb, True)
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob), 'fused and separate append give different outputs'
+    for x, y, n in ((sa[2], sb[2], 'win_k'), (sa[3], sb[3], 'win_v')):
+        for pl in ('nope', 'rope', 'scale'):
+            assert torch.equal(getattr(x, pl), getattr(y, pl)), f'{n}.{pl} differs'
+    # the appended row against the oracle's m = 1 compression, and the output
+    # against the oracle over the window that now holds it
+    ob = ob.float().cpu().numpy()
+    gk, gv = host_kv(sb[2]), host_kv(sb[3])
+    for b in range(B):
+        t = int(q_pos[b, 0])
+        slot = t % ring if ring else t
+        k32, v32, _ = OC.compress(raw_k[b:b + 1], raw_v[b:b + 1], np.zeros((1, 1), np.float32),
+                                  np.zeros(1, np.float32), t)
+        for name, x32, g in (('k', k32, gk), ('v', v32, gv)):
+            codes, rope_bits, scale = F.kv_quantize(x32)
+            assert np.array_equal(g['scale'][b:b + 1, slot:slot + 1], scale), f'{name}: scale b{b}'
+            assert np.array_equal(g['rope'][b:b + 1, slot:slot + 1], rope_bits), f'{name}: rope b{b}'
+            assert_codes_e4m3(g['nope'][b:b + 1, slot:slot + 1], codes, (x32[..., :128] / scale).astype(np.float32),
+                              name)
+        row = {n: {pl: a[b:b + 1, slot:slot + 1] for pl, a in g.items()} for n, g in (('wk', gk), ('wv', gv))}
+        c['dec']['wk'][b, t - c['first']] = OC.decode_kv(row['wk'])[0, 0]
+        c['dec']['wv'][b, t - c['first']] = OC.decode_kv(row['wv'])[0, 0]
+        if kind == 'sparse':
+            ids = idx[b, 0]
+        else:
+            ids = np.arange(0 if kind == 'window' else min((t + 1) // m, rows))
+        ro, _ = _oracle_attn(c, b, 0, ids)
+        assert_close_rms(ob[b, 0], ro, TOL_BF16, f'o b{b}')
+
+
 # ---------------------------------------------------------- end to end ----
 
 def test_c0_fp32_layer_end_to_end():
