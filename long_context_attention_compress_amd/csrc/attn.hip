@@ -253,8 +253,9 @@ struct AppRow {
 template <int NS>
 struct MxSmem {
     TileBuf tb[NS];
-    double rcos[ROPE_PAIRS];
+    double rcos[ROPE_PAIRS];   // RoPE at the query position, float64 (the fused append's key rotation)
     double rsin[ROPE_PAIRS];
+    float2 rsc[ROPE_PAIRS];    // the same (sin, cos) rounded to float32 (the query rotation)
     int32_t rows[MAX_KS];       // row of each key of the split; bit 30 marks a window row; -1: no key
     float xml[NS > 1 ? 2 * AT : 1];
     AppRow app;
@@ -459,6 +460,9 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // prologue) is asked for first, ahead of everything below
     const int64_t t_pos = p.q_pos[q];
     __builtin_amdgcn_sched_barrier(0);
+    // RoPE frequency of pair `lane & 31` (the table below is built by lanes
+    // 0..31 of the first wave), asked for now so that it has arrived by then
+    const double ifreq = p.inv_freq[lane & 31];
     // The query and (sparse) this split's selected ids do not depend on the
     // query position: their loads are issued before the position arrives.
     const __bf16 *qp = (const __bf16 *)p.q + ((size_t)q * H + (active ? head : 0)) * MD;
@@ -515,7 +519,13 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
             sm.rows[i] = row < 0 ? -1 : (int32_t)row | (win ? WIN_BIT : 0);
         }
     }
-    if (tid < ROPE_PAIRS) rope_sincos((double)ki.t * p.inv_freq[tid], &sm.rsin[tid], &sm.rcos[tid]);
+    if (tid < ROPE_PAIRS) {
+        double sn, cs;
+        rope_sincos((double)ki.t * ifreq, &sn, &cs);
+        sm.rsin[tid] = sn;
+        sm.rcos[tid] = cs;
+        sm.rsc[tid] = make_float2((float)sn, (float)cs);
+    }
     __syncthreads();
 
     // query operands (B of S^T = K Q^T): head `col` of this wave, dims 32c + 8g .. +8
@@ -526,10 +536,12 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         bf16x8 hi, lo;
 #pragma unroll
         for (int i = 0; i < 8; i += 2) {
+            // float32 rotation: the hi + lo BF16 terms keep about 16 bits, far
+            // below float32's rounding
             const int pr = (32 * c + 8 * g + i) >> 1;
-            const double sn = sm.rsin[pr], cs = sm.rcos[pr];
-            const double x = (double)(float)raw[i], y = (double)(float)raw[i + 1];
-            const float rx = (float)(x * cs - y * sn), ry = (float)(x * sn + y * cs);
+            const float2 t = sm.rsc[pr];
+            const float x = (float)raw[i], y = (float)raw[i + 1];
+            const float rx = x * t.y - y * t.x, ry = x * t.x + y * t.y;
             hi[i] = (__bf16)rx;
             hi[i + 1] = (__bf16)ry;
             lo[i] = (__bf16)(rx - (float)hi[i]);
