@@ -456,19 +456,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const int H = p.H;
     const bool active = wave < NW;
     const int head = 16 * wave + col;
-    // Every line of the plan (the kernel arguments) is fetched into the scalar
-    // cache at once: the fields are read lazily all through the kernel, and
-    // each first touch of a line would otherwise be a round trip of its own.
-    {
-        static_assert(sizeof(AttnPlan) <= 16 * 64, "the plan spans at most 16 lines");
-        const uint32_t *kp = (const uint32_t *)&p;
-        constexpr int NL = (int)((sizeof(AttnPlan) + 63) / 64);
-        uint32_t w[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = i < NL ? kp[16 * i] : 0u;
-        asm volatile("" ::"s"(w[0]), "s"(w[1]), "s"(w[2]), "s"(w[3]), "s"(w[4]), "s"(w[5]), "s"(w[6]), "s"(w[7]),
-                     "s"(w[8]), "s"(w[9]), "s"(w[10]), "s"(w[11]), "s"(w[12]), "s"(w[13]), "s"(w[14]), "s"(w[15]));
-    }
+    touch_args(p);  // every line of the plan in one scalar round trip
     // the position (a pointer, then the value: the longest scalar chain of the
     // prologue) is asked for first, ahead of everything below
     const int64_t t_pos = p.q_pos[q];

@@ -17,6 +17,22 @@ namespace v4a {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// ---------------------------------------------------------- kernel args ----
+// Fetch every 64-byte line of a kernel's argument block into the scalar cache
+// in one batch (one wait): the fields are read lazily all through a kernel,
+// and each first touch of a line would otherwise be a round trip of its own.
+template <typename T>
+__device__ __forceinline__ void touch_args(const T &p) {
+    static_assert(sizeof(T) <= 16 * 64, "the argument block spans at most 16 lines");
+    const uint32_t *kp = (const uint32_t *)&p;
+    constexpr int NL = (int)((sizeof(T) + 63) / 64);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = i < NL ? kp[16 * i] : 0u;
+    asm volatile("" ::"s"(w[0]), "s"(w[1]), "s"(w[2]), "s"(w[3]), "s"(w[4]), "s"(w[5]), "s"(w[6]), "s"(w[7]),
+                 "s"(w[8]), "s"(w[9]), "s"(w[10]), "s"(w[11]), "s"(w[12]), "s"(w[13]), "s"(w[14]), "s"(w[15]));
+}
+
 // ------------------------------------------------------------ reductions ----
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
