@@ -248,11 +248,12 @@ struct AppRow {
     float ksc, vsc;
 };
 
-// NS key streams per workgroup, each with its own tile buffer; at the end the
-// streams' partial results meet in the (then free) tile buffers.
+// NS key streams per workgroup, each with two tile buffers (one is computed
+// while the next tile is staged into the other); at the end the streams'
+// partial results meet in the (then free) tile buffers.
 template <int NS>
 struct MxSmem {
-    TileBuf tb[NS];
+    TileBuf tb[NS][2];
     double rcos[ROPE_PAIRS];   // RoPE at the query position, float64 (the fused append's key rotation)
     double rsin[ROPE_PAIRS];
     float2 rsc[ROPE_PAIRS];    // the same (sin, cos) rounded to float32 (the query rotation)
@@ -569,8 +570,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // window row 0 and is never staged), and the loop is unrolled by two, so
     // the wait before staging tile t only covers tile t's loads and tile t+1's
     // stay in flight.
-    TileBuf &tb = sm.tb[stream];
-    auto compute = [&]() {
+    auto compute = [&](const TileBuf &tb) {
         if (!active) return;
         // per-key scales of this lane's eight keys (4g..4g+3 and 16+4g..), read as vectors
         v4f ks[2], kb[2], vs[2];
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     load_tile(src, sm.rows, TK * stream, n_rel, RA, tids);
     load_tile(src, sm.rows, TK * (stream + NS), n_rel, RB, tids);
     // The workgroup holding the appended key encodes the row while the first
-    // tiles are in flight (the loop's first barrier publishes it).
+    // tiles are in flight (the barrier before the first staging publishes it).
     int cur = -1;
     if (app_here) {
         const int c = (int)(n_keys - 1 - j0);
@@ -696,25 +696,33 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
             ((uint32_t *)rp)[lr] = bits;
         }
     }
+    // Double-buffered rounds with one barrier each: round r computes the
+    // stream's tile r from one buffer while its tile r + 1 is staged into the
+    // other (whose loads were issued a round earlier), and issues the loads of
+    // tile r + 2 into the register set that staging freed.
+    TileBuf &b0 = sm.tb[stream][0], &b1 = sm.tb[stream][1];
+    __syncthreads();  // the resolved rows and the appended row are published
+    stage_tile(RA, sm.rows, b0, stream * TK, n_rel, tids, sm.app, cur);
+    load_tile(src, sm.rows, (stream + 2 * NS) * TK, n_rel, RA, tids);
+    __syncthreads();
     for (int i = 0; i < n_rounds; i += 2) {
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
-        __syncthreads();
-        stage_tile(RA, sm.rows, tb, ta * TK, n_rel, tids, sm.app, cur);
-        load_tile(src, sm.rows, (ta + 2 * NS) * TK, n_rel, RA, tids);
-        __syncthreads();
-        if (ta < n_tiles) compute();
+        if (ta < n_tiles) compute(b0);
         if (i + 1 >= n_rounds) break;
-        __syncthreads();
-        stage_tile(RB, sm.rows, tb, tb_ * TK, n_rel, tids, sm.app, cur);
+        stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur);
         load_tile(src, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
         __syncthreads();
-        if (tb_ < n_tiles) compute();
+        if (tb_ < n_tiles) compute(b1);
+        if (i + 2 >= n_rounds) break;
+        stage_tile(RA, sm.rows, b0, (ta + 2 * NS) * TK, n_rel, tids, sm.app, cur);
+        load_tile(src, sm.rows, (ta + 4 * NS) * TK, n_rel, RA, tids);
+        __syncthreads();
     }
     if (NS > 1) {
         // the other streams hand their (max, sum, O) to stream 0 through the tile buffers
         __syncthreads();
-        float *xo = (float *)&sm.tb[0];
-        static_assert(sizeof(TileBuf) * NS >= sizeof(float) * AT * 48 * (NS - 1), "exchange fits the tile buffers");
+        float *xo = (float *)&sm.tb[0][0];
+        static_assert(sizeof(TileBuf) * 2 * NS >= sizeof(float) * AT * 48 * (NS - 1), "exchange fits the tile buffers");
         if (stream > 0 && active) {
             const int base = (stream - 1) * AT * 48;
 #pragma unroll
