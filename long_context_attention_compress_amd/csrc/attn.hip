@@ -298,27 +298,56 @@ struct TileSrc {
 template <typename T>
 __device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
 
+// What a lane loads of every tile, fixed for the whole kernel: the row-0
+// address of its 16-byte piece (no-RoPE codes or RoPE pairs, by lane) in
+// each store and those planes' row strides, and (lanes of threads 0..63) the
+// scale plane of K (threads < 32) or V. Per tile only the row changes, so a
+// load costs one select of the store and one 32 x 32 + 64-bit multiply-add.
+struct LaneSrc {
+    const char *kw, *ke, *vw, *ve;
+    uint32_t krw, kre, vrw, vre;
+    const char *sw, *se;
+    uint32_t srw, sre;
+};
+__device__ __forceinline__ LaneSrc lane_src(const TileSrc &S, int tid) {
+    const int part = tid & 15;
+    const bool nope = part < 8;
+    const int koff = nope ? 16 * part : 16 * (part - 8);
+    LaneSrc L;
+    L.kw = pick(nope, S.wk.nope, S.wk.rope) + koff;
+    L.ke = pick(nope, S.ek.nope, S.ek.rope) + koff;
+    L.vw = pick(nope, S.wv.nope, S.wv.rope) + koff;
+    L.ve = pick(nope, S.ev.nope, S.ev.rope) + koff;
+    L.krw = (uint32_t)pick(nope, S.wk.nope_rs, S.wk.rope_rs);
+    L.kre = (uint32_t)pick(nope, S.ek.nope_rs, S.ek.rope_rs);
+    L.vrw = (uint32_t)pick(nope, S.wv.nope_rs, S.wv.rope_rs);
+    L.vre = (uint32_t)pick(nope, S.ev.nope_rs, S.ev.rope_rs);
+    const bool isk = tid < TK;
+    L.sw = pick(isk, S.wk.scale, S.wv.scale);
+    L.se = pick(isk, S.ek.scale, S.ev.scale);
+    L.srw = (uint32_t)pick(isk, S.wk.scale_rs, S.wv.scale_rs);
+    L.sre = (uint32_t)pick(isk, S.ek.scale_rs, S.ev.scale_rs);
+    return L;
+}
+
+__device__ __forceinline__ const char *row_addr(const char *base, uint32_t row, uint32_t stride) {
+    return base + (uint64_t)row * stride;
+}
+
 // Issue the loads of one 32-key tile. Branch-free: a slot without a key reads
 // row 0 of the window store (always present) and is zeroed afterwards, so the
 // compiler keeps every load of the tile in flight together.
-__device__ __forceinline__ void load_tile(const TileSrc &S, const int32_t *rows, int rel, int n_rel, TileRegs &R,
+__device__ __forceinline__ void load_tile(const LaneSrc &L, const int32_t *rows, int rel, int n_rel, TileRegs &R,
                                           int tid) {
-    const int part = tid & 15;
-    const int64_t koff = part < 8 ? 16 * part : 16 * (part - 8);
-    const bool nope = part < 8;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int r = (tid >> 4) + 16 * h;
         const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
         const bool ok = code >= 0;
         const bool win = !ok || (code & WIN_BIT);
-        const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
-        const char *kb = pick(win, pick(nope, S.wk.nope, S.wk.rope), pick(nope, S.ek.nope, S.ek.rope));
-        const int64_t krs = pick(win, pick(nope, S.wk.nope_rs, S.wk.rope_rs), pick(nope, S.ek.nope_rs, S.ek.rope_rs));
-        const char *vb = pick(win, pick(nope, S.wv.nope, S.wv.rope), pick(nope, S.ev.nope, S.ev.rope));
-        const int64_t vrs = pick(win, pick(nope, S.wv.nope_rs, S.wv.rope_rs), pick(nope, S.ev.nope_rs, S.ev.rope_rs));
-        R.k[h] = __builtin_nontemporal_load((const v4i *)(kb + row * krs + koff));
-        R.v[h] = __builtin_nontemporal_load((const v4i *)(vb + row * vrs + koff));
+        const uint32_t row = ok ? (uint32_t)(code & (WIN_BIT - 1)) : 0u;
+        R.k[h] = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.kw, L.ke), row, pick(win, L.krw, L.kre)));
+        R.v[h] = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.vw, L.ve), row, pick(win, L.vrw, L.vre)));
         R.ok[h] = ok;
     }
     // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
@@ -326,11 +355,8 @@ __device__ __forceinline__ void load_tile(const TileSrc &S, const int32_t *rows,
     const int32_t code = (tid < 2 * TK && rel + r < n_rel) ? rows[rel + r] : -1;
     const bool ok = code >= 0;
     const bool win = !ok || (code & WIN_BIT);
-    const int64_t row = ok ? (code & (WIN_BIT - 1)) : 0;
-    const bool isk = tid < TK;
-    const char *sb = pick(isk, pick(win, S.wk.scale, S.ek.scale), pick(win, S.wv.scale, S.ev.scale));
-    const int64_t srs = pick(isk, pick(win, S.wk.scale_rs, S.ek.scale_rs), pick(win, S.wv.scale_rs, S.ev.scale_rs));
-    R.sc = *(const float *)(sb + row * srs);
+    const uint32_t row = ok ? (uint32_t)(code & (WIN_BIT - 1)) : 0u;
+    R.sc = *(const float *)row_addr(pick(win, L.sw, L.se), row, pick(win, L.srw, L.sre));
     R.sok = ok;
 }
 
@@ -566,6 +592,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     src.wv = planes_of(p.wv, b);
     src.ek = p.has_ent ? planes_of(p.ek, b) : src.wk;
     src.ev = p.has_ent ? planes_of(p.ev, b) : src.wv;
+    const LaneSrc lsrc = lane_src(src, tids);
     // Every tile load is issued unconditionally (a tile past the end reads
     // window row 0 and is never staged), and the loop is unrolled by two, so
     // the wait before staging tile t only covers tile t's loads and tile t+1's
@@ -650,8 +677,8 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // (a round past its last tile stages an empty tile and skips the compute)
     const int n_rounds = (n_tiles + NS - 1) / NS;
     TileRegs RA, RB;
-    load_tile(src, sm.rows, TK * stream, n_rel, RA, tids);
-    load_tile(src, sm.rows, TK * (stream + NS), n_rel, RB, tids);
+    load_tile(lsrc, sm.rows, TK * stream, n_rel, RA, tids);
+    load_tile(lsrc, sm.rows, TK * (stream + NS), n_rel, RB, tids);
     // The workgroup holding the appended key encodes the row while the first
     // tiles are in flight (the barrier before the first staging publishes it).
     int cur = -1;
@@ -703,19 +730,19 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     TileBuf &b0 = sm.tb[stream][0], &b1 = sm.tb[stream][1];
     __syncthreads();  // the resolved rows and the appended row are published
     stage_tile(RA, sm.rows, b0, stream * TK, n_rel, tids, sm.app, cur);
-    load_tile(src, sm.rows, (stream + 2 * NS) * TK, n_rel, RA, tids);
+    load_tile(lsrc, sm.rows, (stream + 2 * NS) * TK, n_rel, RA, tids);
     __syncthreads();
     for (int i = 0; i < n_rounds; i += 2) {
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         if (ta < n_tiles) compute(b0);
         if (i + 1 >= n_rounds) break;
         stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur);
-        load_tile(src, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
+        load_tile(lsrc, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
         __syncthreads();
         if (tb_ < n_tiles) compute(b1);
         if (i + 2 >= n_rounds) break;
         stage_tile(RA, sm.rows, b0, (ta + 2 * NS) * TK, n_rel, tids, sm.app, cur);
-        load_tile(src, sm.rows, (ta + 4 * NS) * TK, n_rel, RA, tids);
+        load_tile(lsrc, sm.rows, (ta + 4 * NS) * TK, n_rel, RA, tids);
         __syncthreads();
     }
     if (NS > 1) {
