@@ -579,7 +579,9 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         qrl[c] = lo;
     }
     const float sc2 = p.sm_scale * 1.4426950408889634f;
-    float mrun = -__builtin_inff(), lrun = 0.f;
+    // The running max starts at a finite floor far below any logit, so that
+    // exp2(s - mrun) is 0 for an empty slot (s = -inf) with no test.
+    float mrun = -1e30f, lrun = 0.f;
     v4f O[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) O[i] = (v4f){0.f, 0.f, 0.f, 0.f};
@@ -638,7 +640,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         // raise the running max (and rescale) only when this tile exceeds it by the slack
         if (__builtin_amdgcn_ballot_w64(mx > mrun + RESCALE_SLACK)) {
             const float mn = __builtin_fmaxf(mrun, mx);
-            const float c = mn == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(mrun - mn);
+            const float c = __builtin_amdgcn_exp2f(mrun - mn);
             lrun *= c;
 #pragma unroll
             for (int i = 0; i < 12; ++i) O[i] *= c;
@@ -649,7 +651,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                pr[st][j] = s[st][j] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(s[st][j] - mrun);
+                pr[st][j] = __builtin_amdgcn_exp2f(s[st][j] - mrun);
                 psum += pr[st][j];
             }
         lrun += swap32_sum(swap16_sum(psum));
@@ -765,8 +767,8 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
                 const int base = (os - 1) * AT * 48;
                 const float m1 = sm.xml[2 * tids], l1 = sm.xml[2 * tids + 1];
                 const float mn = __builtin_fmaxf(mrun, m1);
-                const float c0 = mrun == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
-                const float c1 = m1 == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+                const float c0 = __builtin_amdgcn_exp2f(mrun - mn);
+                const float c1 = __builtin_amdgcn_exp2f(m1 - mn);
 #pragma unroll
                 for (int dt = 0; dt < 12; ++dt) O[dt] = O[dt] * c0 + *(const v4f *)&xo[base + (dt * AT + tids) * 4] * c1;
                 lrun = lrun * c0 + l1 * c1;
