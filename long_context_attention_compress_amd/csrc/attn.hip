@@ -267,10 +267,13 @@ constexpr int32_t WIN_BIT = 1 << 30;
 // A tile in flight: the raw loads and which of them hold a key. Slots without
 // a key are zeroed only when the tile is staged, so that issuing the next
 // tile's loads never waits for this one's data.
+// Thread t of a stream loads row t / 8 of the tile: the 16-byte piece t % 8
+// of its E4M3 codes (16 codes) and of its BF16 RoPE dims (8 values), for K
+// and for V, so every lane converts codes when the tile is staged.
 struct TileRegs {
-    v4i k[2], v[2];
+    v4i kn, kr, vn, vr;
     float sc;
-    bool ok[2], sok;
+    bool ok, sok;
 };
 
 // One batch element's planes of one store, with their row strides. Built
@@ -299,29 +302,25 @@ template <typename T>
 __device__ __forceinline__ T pick(bool c, T a, T b) { return c ? a : b; }
 
 // What a lane loads of every tile, fixed for the whole kernel: the row-0
-// address of its 16-byte piece (no-RoPE codes or RoPE pairs, by lane) in
-// each store and those planes' row strides, and (lanes of threads 0..63) the
-// scale plane of K (threads < 32) or V. Per tile only the row changes, so a
-// load costs one select of the store and one 32 x 32 + 64-bit multiply-add.
+// addresses of its pieces in each store's planes (no-RoPE codes, RoPE pairs)
+// and the planes' row strides, and (lanes of threads 0..63) the scale plane
+// of K (threads < 32) or V. Per tile only the row changes, so a load costs
+// one select of the store and one 32 x 32 + 64-bit multiply-add.
 struct LaneSrc {
-    const char *kw, *ke, *vw, *ve;
-    uint32_t krw, kre, vrw, vre;
+    const char *kwn, *ken, *kwr, *ker, *vwn, *ven, *vwr, *ver;
+    uint32_t kwn_s, ken_s, kwr_s, ker_s, vwn_s, ven_s, vwr_s, ver_s;
     const char *sw, *se;
     uint32_t srw, sre;
 };
 __device__ __forceinline__ LaneSrc lane_src(const TileSrc &S, int tid) {
-    const int part = tid & 15;
-    const bool nope = part < 8;
-    const int koff = nope ? 16 * part : 16 * (part - 8);
+    const int off = 16 * (tid & 7);
     LaneSrc L;
-    L.kw = pick(nope, S.wk.nope, S.wk.rope) + koff;
-    L.ke = pick(nope, S.ek.nope, S.ek.rope) + koff;
-    L.vw = pick(nope, S.wv.nope, S.wv.rope) + koff;
-    L.ve = pick(nope, S.ev.nope, S.ev.rope) + koff;
-    L.krw = (uint32_t)pick(nope, S.wk.nope_rs, S.wk.rope_rs);
-    L.kre = (uint32_t)pick(nope, S.ek.nope_rs, S.ek.rope_rs);
-    L.vrw = (uint32_t)pick(nope, S.wv.nope_rs, S.wv.rope_rs);
-    L.vre = (uint32_t)pick(nope, S.ev.nope_rs, S.ev.rope_rs);
+    L.kwn = S.wk.nope + off; L.ken = S.ek.nope + off; L.kwr = S.wk.rope + off; L.ker = S.ek.rope + off;
+    L.vwn = S.wv.nope + off; L.ven = S.ev.nope + off; L.vwr = S.wv.rope + off; L.ver = S.ev.rope + off;
+    L.kwn_s = (uint32_t)S.wk.nope_rs; L.ken_s = (uint32_t)S.ek.nope_rs;
+    L.kwr_s = (uint32_t)S.wk.rope_rs; L.ker_s = (uint32_t)S.ek.rope_rs;
+    L.vwn_s = (uint32_t)S.wv.nope_rs; L.ven_s = (uint32_t)S.ev.nope_rs;
+    L.vwr_s = (uint32_t)S.wv.rope_rs; L.ver_s = (uint32_t)S.ev.rope_rs;
     const bool isk = tid < TK;
     L.sw = pick(isk, S.wk.scale, S.wv.scale);
     L.se = pick(isk, S.ek.scale, S.ev.scale);
@@ -339,25 +338,24 @@ __device__ __forceinline__ const char *row_addr(const char *base, uint32_t row, 
 // compiler keeps every load of the tile in flight together.
 __device__ __forceinline__ void load_tile(const LaneSrc &L, const int32_t *rows, int rel, int n_rel, TileRegs &R,
                                           int tid) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = (tid >> 4) + 16 * h;
-        const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
-        const bool ok = code >= 0;
-        const bool win = !ok || (code & WIN_BIT);
-        const uint32_t row = ok ? (uint32_t)(code & (WIN_BIT - 1)) : 0u;
-        R.k[h] = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.kw, L.ke), row, pick(win, L.krw, L.kre)));
-        R.v[h] = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.vw, L.ve), row, pick(win, L.vrw, L.vre)));
-        R.ok[h] = ok;
-    }
-    // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
-    const int r = tid & (TK - 1);
-    const int32_t code = (tid < 2 * TK && rel + r < n_rel) ? rows[rel + r] : -1;
+    const int r = tid >> 3;
+    const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
     const bool ok = code >= 0;
     const bool win = !ok || (code & WIN_BIT);
     const uint32_t row = ok ? (uint32_t)(code & (WIN_BIT - 1)) : 0u;
-    R.sc = *(const float *)row_addr(pick(win, L.sw, L.se), row, pick(win, L.srw, L.sre));
-    R.sok = ok;
+    R.kn = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.kwn, L.ken), row, pick(win, L.kwn_s, L.ken_s)));
+    R.kr = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.kwr, L.ker), row, pick(win, L.kwr_s, L.ker_s)));
+    R.vn = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.vwn, L.ven), row, pick(win, L.vwn_s, L.ven_s)));
+    R.vr = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.vwr, L.ver), row, pick(win, L.vwr_s, L.ver_s)));
+    R.ok = ok;
+    // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
+    const int rs = tid & (TK - 1);
+    const int32_t cs = (tid < 2 * TK && rel + rs < n_rel) ? rows[rel + rs] : -1;
+    const bool oks = cs >= 0;
+    const bool wins = !oks || (cs & WIN_BIT);
+    const uint32_t rows_ = oks ? (uint32_t)(cs & (WIN_BIT - 1)) : 0u;
+    R.sc = *(const float *)row_addr(pick(wins, L.sw, L.se), rows_, pick(wins, L.srw, L.sre));
+    R.sok = oks;
 }
 
 template <bool HI>
@@ -387,20 +385,13 @@ __device__ __forceinline__ void store_codes(__bf16 *dst, const v4i &c) {
 // store contents.
 __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *rows, TileBuf &sm, int rel, int n_rel,
                                            int tid, const AppRow &app, int cur) {
-    const int part = tid & 15;
+    const int r = tid >> 3, part = tid & 7;
     const v4i z = {0, 0, 0, 0};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int r = (tid >> 4) + 16 * h;
-        const v4i kx = R.ok[h] ? R.k[h] : z, vx = R.ok[h] ? R.v[h] : z;
-        if (part < 8) {
-            store_codes(&sm.kb[r * KB_LD + 16 * part], kx);
-            store_codes(&sm.vb[r * KB_LD + 16 * part], vx);
-        } else {
-            *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * (part - 8)] = kx;
-            *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * (part - 8)] = vx;
-        }
-    }
+    const v4i kn = R.ok ? R.kn : z, vn = R.ok ? R.vn : z, kr = R.ok ? R.kr : z, vr = R.ok ? R.vr : z;
+    store_codes(&sm.kb[r * KB_LD + 16 * part], kn);
+    store_codes(&sm.vb[r * KB_LD + 16 * part], vn);
+    *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * part] = kr;
+    *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * part] = vr;
     const float sc = R.sok ? R.sc : 0.f;
     if (tid < TK) {
         sm.ksc[tid] = sc;
@@ -409,20 +400,15 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *row
         sm.vsc[tid - TK] = sc;
     }
     if (cur >= rel && cur < rel + TK) {  // uniform: this tile holds the appended key
-        const int r = cur - rel;
-        if ((tid >> 4) == (r & 15)) {
-            const v4i kx = *(const v4i *)(part < 8 ? &app.kc[16 * part] : &app.kr[16 * (part - 8)]);
-            const v4i vx = *(const v4i *)(part < 8 ? &app.vc[16 * part] : &app.vr[16 * (part - 8)]);
-            if (part < 8) {
-                store_codes(&sm.kb[r * KB_LD + 16 * part], kx);
-                store_codes(&sm.vb[r * KB_LD + 16 * part], vx);
-            } else {
-                *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * (part - 8)] = kx;
-                *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * (part - 8)] = vx;
-            }
+        const int ra = cur - rel;
+        if (r == ra) {
+            store_codes(&sm.kb[ra * KB_LD + 16 * part], *(const v4i *)&app.kc[16 * part]);
+            store_codes(&sm.vb[ra * KB_LD + 16 * part], *(const v4i *)&app.vc[16 * part]);
+            *(v4i *)&sm.kb[ra * KB_LD + MDN + 8 * part] = *(const v4i *)&app.kr[16 * part];
+            *(v4i *)&sm.vb[ra * KB_LD + MDN + 8 * part] = *(const v4i *)&app.vr[16 * part];
         }
-        if (tid == r) sm.ksc[r] = app.ksc;
-        if (tid == TK + r) sm.vsc[r] = app.vsc;
+        if (tid == ra) sm.ksc[ra] = app.ksc;
+        if (tid == TK + ra) sm.vsc[ra] = app.vsc;
     }
 }
 
