@@ -183,49 +183,42 @@ __device__ __forceinline__ float bits_val(uint32_t x) {
     return ACT == 0 ? __uint_as_float(x) : __uint_as_float(x << 16);
 }
 
+// Three waves per block of tokens, one per output: wave 0 the K entry, wave
+// 1 the V entry, wave 2 the indexer key (each evaluates the gate softmax
+// itself), so the three encodes run side by side.
 template <int ACT, int M>
-__global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
-    const int lane = lane_id();
+__global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
+    const int lane = lane_id(), role = threadIdx.x >> 6;
     const int j = blockIdx.x, b = blockIdx.y;
     const int64_t tok0 = (int64_t)j * M;
     const int64_t entry = p.pos0 / M + j;
     const bool do_kv = p.has_kv && (p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring);
+    if (role < 2 ? !do_kv : !p.has_ik) return;  // uniform per wave
     const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
     const int dI = p.dI;
+    const int width = role < 2 ? D : dI;
     const bool rl = lane < ROPE_PAIRS;
     // Every load is unconditional, so all of them are in flight together: an
-    // absent source reads element 0 of the gate instead, and an element past
-    // the row reads the row's first; the values are masked after the loads.
-    const char *gsrc = (const char *)p.gate;
-    const char *ksrc = do_kv ? (const char *)p.raw_k : gsrc;
-    const char *vsrc = do_kv ? (const char *)p.raw_v : gsrc;
-    const char *isrc = p.has_ik ? (const char *)p.raw_ik : gsrc;
+    // element past the row reads the row's first; the values are masked after
+    // the loads.
+    const char *src = (const char *)(role == 0 ? p.raw_k : role == 1 ? p.raw_v : p.raw_ik);
     double f = p.inv_freq[rl ? lane : 0];
     float gz[M], gb[M];
-    uint32_t kn[M][4], vn[M][4], kx[M], ky[M], vx[M], vy[M], ui[M][4];
+    uint32_t xn[M][4], xa[M], xb[M];
 #pragma unroll
     for (int r = 0; r < M; ++r) {
         const int64_t t = (int64_t)b * p.t_new + tok0 + r;
         gz[r] = p.gate[t];
         gb[r] = p.pos_bias[r];
-        const int64_t row = do_kv ? t * D : 0;
+        const int64_t row = t * width;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int64_t x = i < nit ? row + lane + 64 * i : row;
-            kn[r][i] = load_bits<ACT>(ksrc, x);
-            vn[r][i] = load_bits<ACT>(vsrc, x);
+            const bool on = role < 2 ? i < nit : lane + 64 * i < dI;
+            xn[r][i] = load_bits<ACT>(src, on ? row + lane + 64 * i : row);
         }
-        const int64_t xr = rl ? row + Dn + 2 * lane : row;
-        kx[r] = load_bits<ACT>(ksrc, xr);
-        ky[r] = load_bits<ACT>(ksrc, xr + (rl ? 1 : 0));
-        vx[r] = load_bits<ACT>(vsrc, xr);
-        vy[r] = load_bits<ACT>(vsrc, xr + (rl ? 1 : 0));
-        const int64_t irow = p.has_ik ? t * dI : 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool on = p.has_ik && lane + 64 * i < dI;
-            ui[r][i] = load_bits<ACT>(isrc, on ? irow + lane + 64 * i : irow);
-        }
+        const int64_t xr = (role < 2 && rl) ? row + Dn + 2 * lane : row;
+        xa[r] = load_bits<ACT>(src, xr);
+        xb[r] = load_bits<ACT>(src, xr + ((role < 2 && rl) ? 1 : 0));
     }
     // no load is sunk into the branches that use it (the register fence also
     // pins the rotation frequency, a kernel-argument load, up here)
@@ -247,61 +240,58 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
 #pragma unroll
     for (int r = 0; r < M; ++r) alpha[r] = e[r] / zsum;
 
-    if (do_kv) {
-        float nk[4], nv[4];
-        float rkx = 0.f, rky = 0.f, rvx = 0.f, rvy = 0.f;
+    if (role < 2) {
+        // K (rotated at each token's position) or V
+        float nx[4];
+        float rx = 0.f, ry = 0.f;
         if constexpr (M == 1) {
             // one token: the pooling is the identity (alpha = 1 for any finite
             // gate) and the gate is not used. The attention kernels' fused
             // window append computes this same row with the same operations.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                nk[i] = bits_val<ACT>(kn[0][i]);
-                nv[i] = bits_val<ACT>(vn[0][i]);
-            }
+            for (int i = 0; i < 4; ++i) nx[i] = bits_val<ACT>(xn[0][i]);
             if (rl) {
-                double sn, cs, xr, yr;
-                rope_sincos((double)(p.pos0 + tok0) * f, &sn, &cs);
-                rope_rotate((double)bits_val<ACT>(kx[0]), (double)bits_val<ACT>(ky[0]), sn, cs, &xr, &yr);
-                rkx = (float)xr;
-                rky = (float)yr;
-                rvx = bits_val<ACT>(vx[0]);
-                rvy = bits_val<ACT>(vy[0]);
+                if (role == 0) {
+                    double sn, cs, xr, yr;
+                    rope_sincos((double)(p.pos0 + tok0) * f, &sn, &cs);
+                    rope_rotate((double)bits_val<ACT>(xa[0]), (double)bits_val<ACT>(xb[0]), sn, cs, &xr, &yr);
+                    rx = (float)xr;
+                    ry = (float)yr;
+                } else {
+                    rx = bits_val<ACT>(xa[0]);
+                    ry = bits_val<ACT>(xb[0]);
+                }
             }
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                double ak = 0.0, av = 0.0;
+                double a = 0.0;
 #pragma unroll
-                for (int r = 0; r < M; ++r) {
-                    ak += alpha[r] * (double)bits_val<ACT>(kn[r][i]);
-                    av += alpha[r] * (double)bits_val<ACT>(vn[r][i]);
-                }
-                nk[i] = (float)ak;
-                nv[i] = (float)av;
+                for (int r = 0; r < M; ++r) a += alpha[r] * (double)bits_val<ACT>(xn[r][i]);
+                nx[i] = (float)a;
             }
             if (rl) {
-                double akx = 0.0, aky = 0.0, avx = 0.0, avy = 0.0;
+                double ax = 0.0, ay = 0.0;
 #pragma unroll
                 for (int r = 0; r < M; ++r) {
-                    double sn, cs, xr, yr;
-                    rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
-                    rope_rotate((double)bits_val<ACT>(kx[r]), (double)bits_val<ACT>(ky[r]), sn, cs, &xr, &yr);
-                    akx += alpha[r] * xr;
-                    aky += alpha[r] * yr;
-                    avx += alpha[r] * (double)bits_val<ACT>(vx[r]);
-                    avy += alpha[r] * (double)bits_val<ACT>(vy[r]);
+                    double x = (double)bits_val<ACT>(xa[r]), y = (double)bits_val<ACT>(xb[r]);
+                    if (role == 0) {
+                        double sn, cs, xr, yr;
+                        rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                        rope_rotate(x, y, sn, cs, &xr, &yr);
+                        x = xr;
+                        y = yr;
+                    }
+                    ax += alpha[r] * x;
+                    ay += alpha[r] * y;
                 }
-                rkx = (float)akx;
-                rky = (float)aky;
-                rvx = (float)avx;
-                rvy = (float)avy;
+                rx = (float)ax;
+                ry = (float)ay;
             }
         }
-        store_kv_row(p.k, b, kv_row(p.k, entry), nk, nit, rkx, rky);
-        store_kv_row(p.v, b, kv_row(p.v, entry), nv, nit, rvx, rvy);
-    }
-    if (p.has_ik) {
+        const KvView &dst = role == 0 ? p.k : p.v;
+        store_kv_row(dst, b, kv_row(dst, entry), nx, nit, rx, ry);
+    } else {
         const int nit_i = (dI + 63) / 64;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -309,11 +299,11 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
             const int d = lane + 64 * i;
             float x;
             if constexpr (M == 1) {
-                x = bits_val<ACT>(d < dI ? ui[0][i] : 0u);
+                x = bits_val<ACT>(d < dI ? xn[0][i] : 0u);
             } else {
                 double acc = 0.0;
 #pragma unroll
-                for (int r = 0; r < M; ++r) acc += alpha[r] * (double)bits_val<ACT>(d < dI ? ui[r][i] : 0u);
+                for (int r = 0; r < M; ++r) acc += alpha[r] * (double)bits_val<ACT>(d < dI ? xn[r][i] : 0u);
                 x = (float)acc;
             }
             store_ik_value(p.ik, b, entry, d, d < dI, x);
@@ -324,10 +314,10 @@ __global__ __launch_bounds__(64) void compress_small_kernel(CompressPlan p) {
 template <int ACT>
 static void launch_small(const CompressPlan &p, dim3 grid, hipStream_t s) {
     switch (p.m) {
-        case 1: hipLaunchKernelGGL((compress_small_kernel<ACT, 1>), grid, dim3(64), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((compress_small_kernel<ACT, 2>), grid, dim3(64), 0, s, p); break;
-        case 3: hipLaunchKernelGGL((compress_small_kernel<ACT, 3>), grid, dim3(64), 0, s, p); break;
-        default: hipLaunchKernelGGL((compress_small_kernel<ACT, 4>), grid, dim3(64), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((compress_small_kernel<ACT, 1>), grid, dim3(192), 0, s, p); break;
+        case 2: hipLaunchKernelGGL((compress_small_kernel<ACT, 2>), grid, dim3(192), 0, s, p); break;
+        case 3: hipLaunchKernelGGL((compress_small_kernel<ACT, 3>), grid, dim3(192), 0, s, p); break;
+        default: hipLaunchKernelGGL((compress_small_kernel<ACT, 4>), grid, dim3(192), 0, s, p); break;
     }
 }
 
