@@ -7,12 +7,13 @@
 // große Wirkung", section "Komprimierte Erinnerung für längere Kontexte"]: the
 // last 64 values carry RoPE and stay BF16, the rest is FP8.
 //
-// One wave per (entry, batch element). The gate weights, the RoPE rotation
-// and the weighted sum are evaluated in float64 and the entry is rounded to
-// float32 before it is encoded, so every encoding decision (FP8 scale and
-// codes, BF16 rounding, MX exponent and E2M1 codes) is taken on a float32
-// value. Compression is a negligible share of decode time (one block per m
-// tokens), so the kernel favours exactness over speed.
+// One wave per (entry, batch element) for long blocks, three (one per output)
+// for blocks of up to four tokens. The gate weights, the RoPE rotation and the
+// weighted sum are evaluated in float64 and the entry is rounded to float32
+// before it is encoded, so every encoding decision (FP8 scale and codes, BF16
+// rounding, MX exponent and E2M1 codes) is taken on a float32 value.
+// Compression is a small share of decode time (one block per m tokens), so the
+// kernels favour exactness over speed.
 
 #include "common.hpp"
 
@@ -169,7 +170,8 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
 // Blocks of at most SMALL_M tokens (the per-token window append, the CSA
 // block): every global load is issued before any arithmetic, so one memory
 // round trip precedes the encode, and each lane evaluates the gate softmax
-// itself. Same float64 arithmetic as the general kernel.
+// itself. Same float64 arithmetic as the general kernel (for m = 1 the
+// pooling is skipped: it is the identity).
 constexpr int SMALL_M = 4;
 
 // Raw bits of one activation (float32 or BF16) and its float32 value.
