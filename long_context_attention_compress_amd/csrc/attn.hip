@@ -333,11 +333,17 @@ __device__ __forceinline__ const char *row_addr(const char *base, uint32_t row, 
     return base + (uint64_t)row * stride;
 }
 
-// Issue the loads of one 32-key tile. Branch-free: a slot without a key reads
-// row 0 of the window store (always present) and is zeroed afterwards, so the
-// compiler keeps every load of the tile in flight together.
+// Issue the loads of one 32-key tile. Branch-free within the tile: a slot
+// without a key reads row 0 of the window store (always present) and is
+// zeroed afterwards, so the compiler keeps every load of the tile in flight
+// together. A tile wholly past the split's end loads nothing.
 __device__ __forceinline__ void load_tile(const LaneSrc &L, const int32_t *rows, int rel, int n_rel, TileRegs &R,
                                           int tid) {
+    if (rel >= n_rel) {  // uniform: a tile past the split's end is never computed
+        R.ok = false;
+        R.sok = false;
+        return;
+    }
     const int r = tid >> 3;
     const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
     const bool ok = code >= 0;
