@@ -150,7 +150,8 @@ typedef struct {
  * m = 1 turns the call into an append of raw rows (RoPE + encode), which is
  * how the window is filled.
  *
- *  B, t_new    batch size and raw tokens per batch element (t_new % m == 0).
+ *  B, t_new    batch size (1 .. 65535) and raw tokens per batch element
+ *              (t_new % m == 0).
  *  pos0        position of the first raw token (pos0 % m == 0, >= 0).
  *  m           1 .. 1024.
  *  act_fmt     format of raw_k, raw_v, raw_ik (float32 or bfloat16).

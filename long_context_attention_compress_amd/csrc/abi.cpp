@@ -327,6 +327,7 @@ int v4a_workspace_init(void *ws, size_t bytes, v4a_stream stream) {
 int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
     if (!a) return fail(V4A_ENULL, "args is NULL");
     if (a->B <= 0 || a->t_new < 0) return fail(V4A_EINVAL, "B must be positive and t_new >= 0");
+    if (a->B > MAX_GRID_Y) return fail(V4A_EINVAL, "B must be at most %d (got %d)", MAX_GRID_Y, a->B);
     if (a->m < 1 || a->m > 1024) return fail(V4A_EINVAL, "m must be in 1..1024 (got %d)", a->m);
     if (a->pos0 < 0 || a->pos0 % a->m || a->t_new % a->m)
         return fail(V4A_EINVAL, "pos0 and t_new must be non-negative multiples of m");

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(AT) void attn_f32_kernel(AttnPlan p) {
     float *mrun = corr + H;           // [H]
     float *lrun = mrun + H;           // [H]
     const int tid = threadIdx.x;
-    const int q = blockIdx.y, split = blockIdx.x;
+    const int q = blockIdx.y + p.q_base, split = blockIdx.x;
     const int b = q / p.Tq;
     const KeyInfo ki = key_info(p, p.q_pos[q]);
     const float *qin = (const float *)p.q + (size_t)q * H * D;
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int stream = tid / AT, tids = tid % AT, wave = tids >> 6;
     const int col = lane & 15, g = lane >> 4;
-    const int q = blockIdx.y, split = blockIdx.x;
+    const int q = blockIdx.y + p.q_base, split = blockIdx.x;
     const int b = q / p.Tq;
     const int H = p.H;
     const bool active = wave < NW;
@@ -893,8 +893,8 @@ __global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
         p.lse[(size_t)q * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -__builtin_inff();
 }
 
-hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
-    dim3 grid(p.n_split, p.Q);
+static void launch_attn_slice(const AttnPlan &p, int nq, hipStream_t s) {
+    const dim3 grid(p.n_split, nq);
     if (p.ek.fmt == 0 && p.wk.fmt == 0) {
         size_t lds = (size_t)(p.H * p.D + 2 * TK * p.D + p.H * TK + 3 * p.H) * 4;
         hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(AT), lds, s, p);
@@ -914,6 +914,14 @@ hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
                 default: hipLaunchKernelGGL((attn_mx_kernel<4, 1>), grid, dim3(AT), 0, s, p); break;
             }
         }
+    }
+}
+
+hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
+    for (int q0 = 0; q0 < p.Q; q0 += MAX_GRID_Y) {
+        AttnPlan ps = p;
+        ps.q_base = q0;
+        launch_attn_slice(ps, p.Q - q0 < MAX_GRID_Y ? p.Q - q0 : MAX_GRID_Y, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;

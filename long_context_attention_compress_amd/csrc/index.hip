@@ -591,7 +591,7 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
     __shared__ EmitSmem em;
     uint32_t *skey = dyn;                                 // [chunk]
     float *sq = (float *)(dyn + p.chunk);                 // f32 mode: query [H][dI]
-    const int chunk = blockIdx.x, q = blockIdx.y;
+    const int chunk = blockIdx.x, q = blockIdx.y + p.q_base;
     const int b = q / p.Tq;
     const int tid = threadIdx.x;
     if (MODE == 0) {
@@ -1039,7 +1039,12 @@ __global__ __launch_bounds__(MT) void index_merge_kernel(IndexPlan p) {
 template <int MODE>
 static void launch_mode(const IndexPlan &p, hipStream_t s) {
     const size_t q_lds = MODE == 0 ? (size_t)p.H * p.dI * 4 : 0;
-    hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, p.Q), dim3(IT), (size_t)p.chunk * 4 + q_lds, s, p);
+    for (int q0 = 0; q0 < p.Q; q0 += MAX_GRID_Y) {
+        IndexPlan ps = p;
+        ps.q_base = q0;
+        const int nq = p.Q - q0 < MAX_GRID_Y ? p.Q - q0 : MAX_GRID_Y;
+        hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, nq), dim3(IT), (size_t)p.chunk * 4 + q_lds, s, ps);
+    }
     hipLaunchKernelGGL(index_merge_kernel<MODE>, dim3(p.Q), dim3(MT),
                        (size_t)(p.n_chunks + 1 + p.chunk) * 4 + q_lds, s, p);
 }

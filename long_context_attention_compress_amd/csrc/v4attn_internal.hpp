@@ -47,8 +47,13 @@ struct CompressPlan {
 // scoring loop over a chunk is fully unrolled.
 constexpr int IDX_CHUNK = 1024;
 
+// Launches put queries on grid y, whose extent is at most 65535: larger
+// query counts run as several launches, each with its first query in q_base.
+constexpr int MAX_GRID_Y = 65535;
+
 struct IndexPlan {
     int Q, Tq, H, dI, k, m;
+    int q_base;      // first query of this launch (score kernel)
     int chunk;       // entries scored per workgroup (IDX_CHUNK)
     int n_chunks;    // workgroups per query
     int s_local;     // candidates a chunk keeps at least (its local top-s)
@@ -67,6 +72,7 @@ struct IndexPlan {
 
 struct AttnPlan {
     int Q, Tq, H, D, W, m;
+    int q_base;        // first query of this launch (attention kernels)
     int sparse;        // 1: key list is idx[q][0..k); 0: entries 0..n_ent-1
     int k;             // sparse list length
     int64_t n_override;  // dense: cap on entries (< 0: none)

@@ -178,6 +178,33 @@ def test_index_mxfp4_exponent_extremes():
     _check_index(c, idx, score, dkeys, diq)
 
 
+def test_index_mxfp4_many_queries_per_sequence():
+    """Thirteen queries per sequence in one call: positions in and out of order, queries
+    that see nothing or only part of a chunk, and one query whose scaled head sends its
+    tiles to the exact pass while its neighbours take the fast form. Checked against the
+    oracle, and bitwise against one call per query (no state leaks between the queries
+    of a call)."""
+    rows, Tq = 6000, 13
+    g = np.random.default_rng(21)
+    q_pos = np.stack([np.arange(rows * 4 - Tq, rows * 4),
+                      np.sort(g.integers(0, rows * 4, Tq))[::-1]]).astype(np.int64)
+    q_pos[1, 5], q_pos[1, 9], q_pos[1, 12] = -1, 2, 4095
+    c = _index_case_mx(21, 2, rows, q_pos, 512)
+    sc, isc = c['sc'].copy(), c['isc'].copy()
+    sc[:, ::97] += 84                     # rows 0, 97, ...: x 2^84
+    isc[1, 3, 3] += 34                    # query 3 of batch 1: head 3 x 2^34 -> exact pass
+    c['sc'], c['isc'] = sc, isc
+    dkeys, diq = F.mxfp4_dequantize(c['packed'], sc), F.mxfp4_dequantize(c['ip'], isc)
+    print('index mxfp4 multi-query', flush=True)
+    idx, score = _run_index(c)
+    _check_index(c, idx, score, dkeys, diq)
+    for i in range(Tq):
+        ci = dict(c, q_pos=c['q_pos'][:, i:i + 1], ip=c['ip'][:, i:i + 1], isc=c['isc'][:, i:i + 1],
+                  w=c['w'][:, i:i + 1])
+        idx1, score1 = _run_index(ci)
+        assert np.array_equal(idx1[:, 0], idx[:, i]) and np.array_equal(score1[:, 0], score[:, i]), f'query {i}'
+
+
 def test_index_mxfp4_repeat_is_bitwise_identical():
     q_pos = np.array([[12000 * 4 - 1]], np.int64)
     c = _index_case_mx(3, 1, 12000, q_pos, 256)
@@ -291,6 +318,39 @@ def test_attn_dense(fmt, override):
                 n = min(n, override)
             ro, _ = _oracle_attn(c, b, i, np.arange(n))
             assert_close_rms(o[b, i], ro, tol, f'o b{b} i{i}')
+
+
+def test_more_queries_than_one_launch_row():
+    """70,000 queries in one call, more than one launch takes along the query axis, so
+    the library splits it: the index and dense attention, with query rows drawn from 64
+    patterns and random positions, checked against the oracle on queries on both sides
+    of each split point."""
+    NQ, P, rows, m = 70000, 64, 300, 4
+    g = np.random.default_rng(31)
+    pat = g.integers(0, P, NQ)
+    q_pos = g.integers(0, rows * m, NQ).astype(np.int64)[None]
+    S = np.array([0, 1, 65533, 65534, 65535, 65536, 69999] + list(g.integers(0, NQ, 6)))
+
+    base = _index_case_mx(31, 1, rows, np.zeros((1, P), np.int64), 16)
+    c = dict(base, ip=base['ip'][:, pat], isc=base['isc'][:, pat], w=base['w'][:, pat], q_pos=q_pos)
+    print('index, 70000 queries', flush=True)
+    idx, score = _run_index(c)
+    cs = dict(c, q_pos=q_pos[:, S], w=c['w'][:, S])
+    _check_index(cs, idx[:, S], score[:, S], base['dkeys'], base['diq'][:, pat[S]])
+
+    H, D = 16, 192
+    a = _attn_case(32, 1, P, H, D, rows, q_pos, 'fp8')
+    ek, ev, wk, wv = _stores(a)
+    qd = bf16_dev(a['q'])[:, torch.from_numpy(pat).cuda()].contiguous()
+    print('dense attention, 70000 queries', flush=True)
+    o = v4.hca_attn(qd, dev(q_pos), ek, ev, m, wk, wv, a['W'])
+    o = o[:, torch.from_numpy(S).cuda()].float().cpu().numpy()
+    for j, s in enumerate(S):
+        t = int(q_pos[0, s])
+        ro, _ = OM.A.attend_query(a['q'][0, pat[s]], t, np.arange(min((t + 1) // m, rows)), a['dec']['ek'][0],
+                                  a['dec']['ev'][0], a['dec']['wk'][0], a['dec']['wv'][0], a['W'],
+                                  win_first=a['first'])
+        assert_close_rms(o[0, j], ro, TOL_BF16, f'o query {s}')
 
 
 def test_attn_dense_two_streams():
