@@ -623,6 +623,203 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
     chunk_emit(p, q, chunk, c0, cnt, s_want, skey, em);
 }
 
+// ---------------------------------------- several chunks per workgroup ----
+
+// Chunked prefill: many queries, each with many chunks. A workgroup takes
+// IDX_CPW consecutive chunks of one query: the query's operands are loaded
+// once, and the next chunk's first two key batches are in flight while the
+// current chunk emits its candidates. Per chunk the tiles, head sums, score
+// keys and emission are those of score_chunk_mx and chunk_emit, so the
+// candidate regions are bitwise identical to the one-chunk kernel's.
+constexpr int IDX_CPW = 4;
+
+struct ChunkGeo {
+    const char *kbase, *sbase;
+    uint32_t kbytes, sbytes;  // byte ranges of the chunk's visible rows
+};
+
+__device__ __forceinline__ ChunkGeo chunk_geo(const IndexPlan &p, int b, int64_t c0, int cnt) {
+    ChunkGeo g;
+    g.kbase = p.keys.e2m1 + (int64_t)b * p.keys.e2m1_bs + c0 * p.keys.e2m1_rs;
+    g.sbase = p.keys.e8m0 + (int64_t)b * p.keys.e8m0_bs + c0 * p.keys.e8m0_rs;
+    g.kbytes = (uint32_t)(cnt - 1) * (uint32_t)p.keys.e2m1_rs + 64u;
+    g.sbytes = (uint32_t)(cnt - 1) * (uint32_t)p.keys.e8m0_rs + 4u;
+    return g;
+}
+
+template <int NT>
+__global__ __launch_bounds__(IT, 4) void index_score_cpw_kernel(IndexPlan p) {
+    constexpr int NW = IT / 64, BATCH = 4;
+    constexpr int STRIDE = NW * BATCH;
+    constexpr int NB = IDX_CHUNK / (16 * STRIDE);
+    static_assert(NB * 16 * STRIDE == IDX_CHUNK && NB % 2 == 0, "a chunk is an even number of batches");
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+    __shared__ EmitSmem em;
+    uint32_t *skey = dyn;  // [chunk], reused by each chunk of the workgroup
+    const int q = blockIdx.y + p.q_base;
+    const int b = q / p.Tq;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int col = lane & 15, grp = lane >> 4;
+    const int ch0 = blockIdx.x * IDX_CPW;
+    const int ch_end = ch0 + IDX_CPW < p.n_chunks ? ch0 + IDX_CPW : p.n_chunks;
+    const int64_t nvis = visible_entries(p, q);
+    const int64_t n_active = (nvis + p.chunk - 1) / p.chunk;
+    const int act_end = n_active < (int64_t)ch_end ? (int)n_active : ch_end;  // chunks ch0 .. act_end-1 score
+    for (int c = (act_end > ch0 ? act_end : ch0) + tid; c < ch_end; c += IT) {
+        uint32_t *meta = p.meta + ((size_t)q * p.n_chunks + c) * 2;
+        meta[0] = 0;
+        meta[1] = 0;
+    }
+    if (act_end <= ch0) return;
+
+    // the query's operands into LDS (read again for each chunk, so that they
+    // hold no registers while the next chunk's keys fly during an emission)
+    constexpr int H = 16 * NT;
+    uint8_t *s_iq = (uint8_t *)(dyn + p.chunk);  // [H][64]
+    uint8_t *s_iqs = s_iq + H * 64;              // [H][4]
+    float *s_w = (float *)(s_iqs + H * 4);       // [H]
+    {
+        const uint8_t *iq = (const uint8_t *)p.iq + (size_t)q * H * 64;
+        uint4 x = make_uint4(0, 0, 0, 0);
+        uint32_t y = 0;
+        float z = 0.f;
+        if (tid < H * 4) {
+            x = ((const uint4 *)iq)[tid];
+            y = p.iq_scale[(size_t)q * H * 4 + tid];
+        }
+        if (tid < H) z = p.w[(size_t)q * H + tid];
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < H * 4) {
+            ((uint4 *)s_iq)[tid] = x;
+            s_iqs[tid] = (uint8_t)y;
+        }
+        if (tid < H) s_w[tid] = z;
+    }
+    const uint32_t krs = (uint32_t)p.keys.e2m1_rs, srs = (uint32_t)p.keys.e8m0_rs;
+    const uint32_t kvo = (uint32_t)(wave * 16 + col) * krs + 16u * grp;
+    const uint32_t svo = (uint32_t)(wave * 16 + col) * srs;
+    v4i ka[BATCH], kb[BATCH];
+    uint32_t sa[BATCH], sb[BATCH];
+    auto issue = [&](v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], const ChunkGeo &g, int bi) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const uint32_t t16 = (uint32_t)(STRIDE * bi + NW * u) * 16u;
+            const uint32_t ko = t16 * krs, so = t16 * srs;
+            const int nk = (int)g.kbytes - (int)ko, ns = (int)g.sbytes - (int)so;
+            const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(g.kbase + ko), (short)0, __builtin_elementwise_max(nk, 0), 0x00020000);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(g.sbase + so), (short)0, __builtin_elementwise_max(ns, 0), 0x00020000);
+            kv[u] = __builtin_amdgcn_raw_buffer_load_b128(rk, kvo, 0, 0);
+            sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, svo, 0, 0);
+        }
+    };
+    auto chunk_cnt = [&](int c) {
+        const int64_t left = nvis - (int64_t)c * p.chunk;
+        return (int)(left < p.chunk ? left : p.chunk);
+    };
+    ChunkGeo geo = chunk_geo(p, b, (int64_t)ch0 * p.chunk, chunk_cnt(ch0));
+    issue(ka, sa, geo, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kb, sb, geo, 1);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // the query is in LDS
+    // the fast-form rule of score_chunk_mx (uniform over the workgroup's chunks)
+    uint32_t sA = 0, qmax = 0, qnan = 0;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        const uint32_t sc = s_iqs[(16 * i + col) * 4 + grp];
+        sA |= sc << (8 * i);
+        qmax = sc > qmax ? sc : qmax;
+        qnan |= sc == 0xFFu;
+    }
+    qmax = wave_max_u32(qmax);
+    const bool q_nan = __ballot(qnan != 0) != 0;
+    int lim = 370 - (int)qmax;
+    lim = lim > 255 ? 255 : lim;
+    if (q_nan) lim = 0;
+    // every full chunk keeps enough that the union holds at least kk entries (as the one-chunk kernel)
+    const int kk = (int)(nvis < p.k ? nvis : p.k);
+    int s_base = p.s_local;
+    {
+        const int64_t div = n_active > 1 ? n_active - 1 : 1;
+        const int64_t spread = (kk + div - 1) / div;
+        if (spread > s_base) s_base = (int)spread;
+    }
+
+    auto unpack = [&](uint32_t (&sv)[BATCH]) {
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            asm volatile("" : "+v"(sv[u]));
+            sv[u] = (sv[u] >> (8 * grp)) & 0xFFu;
+        }
+    };
+    auto finish = [&](const float (&part)[BATCH], int bi) {
+        const float s = scatter_rows(part);
+        skey[(STRIDE * bi + wave + NW * grp) * 16 + col] = score_key(s);
+    };
+    for (int c = ch0; c < act_end; ++c) {
+        const int64_t c0 = (int64_t)c * p.chunk;
+        const int cnt = chunk_cnt(c);
+        v8i A[4];
+        float wv[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            A[i] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+            if (i < NT) {
+                const v4i x = *(const v4i *)&s_iq[(16 * i + col) * 64 + 16 * grp];
+                A[i] = (v8i){x[0], x[1], x[2], x[3], 0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wv[i][j] = i < NT ? s_w[16 * i + 4 * grp + j] : 0.f;
+        }
+        bool redo = q_nan;
+        auto consume = [&](const v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], int bi) {
+            unpack(sv);
+            const uint32_t smax = __builtin_elementwise_max(__builtin_elementwise_max(sv[0], sv[1]),
+                                                            __builtin_elementwise_max(sv[2], sv[3]));
+            redo |= __ballot((int)smax >= lim) != 0;
+            float part[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) part[u] = head_sum<NT, true>(A, sA, kv[u], sv[u], wv);
+            finish(part, bi);
+        };
+#pragma unroll
+        for (int bi = 0; bi < NB; bi += 2) {
+            consume(ka, sa, bi);
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 2 < NB) issue(ka, sa, geo, bi + 2);
+            __builtin_amdgcn_sched_barrier(0);
+            consume(kb, sb, bi + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            if (bi + 3 < NB) issue(kb, sb, geo, bi + 3);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (redo) {  // the exact pass of score_chunk_mx, over this wave's tiles
+            for (int bi = 0; bi < NB; ++bi) {
+                issue(ka, sa, geo, bi);
+                unpack(sa);
+                float part[BATCH];
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u) part[u] = head_sum<NT, false>(A, sA, ka[u], sa[u], wv);
+                finish(part, bi);
+            }
+        }
+        if (c + 1 < act_end) {  // the next chunk's first batches fly during this chunk's emission
+            geo = chunk_geo(p, b, c0 + p.chunk, chunk_cnt(c + 1));
+            issue(ka, sa, geo, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            issue(kb, sb, geo, 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        // chunk_emit reads skey before its first barrier, so the next chunk may overwrite it afterwards
+        chunk_emit(p, q, c, c0, cnt, s_base < cnt ? s_base : cnt, skey, em);
+    }
+}
+
 // ------------------------------------------------------ merge select ----
 
 constexpr int MBITS = 12;                 // radix digit of the merge select
@@ -1039,11 +1236,20 @@ __global__ __launch_bounds__(MT) void index_merge_kernel(IndexPlan p) {
 template <int MODE>
 static void launch_mode(const IndexPlan &p, hipStream_t s) {
     const size_t q_lds = MODE == 0 ? (size_t)p.H * p.dI * 4 : 0;
+    // several queries per sequence with several chunks each (chunked prefill):
+    // a workgroup takes IDX_CPW chunks of one query
+    const bool cpw = MODE != 0 && p.Tq > 1 && p.n_chunks > 1;
     for (int q0 = 0; q0 < p.Q; q0 += MAX_GRID_Y) {
         IndexPlan ps = p;
         ps.q_base = q0;
         const int nq = p.Q - q0 < MAX_GRID_Y ? p.Q - q0 : MAX_GRID_Y;
-        hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, nq), dim3(IT), (size_t)p.chunk * 4 + q_lds, s, ps);
+        if (cpw)
+            hipLaunchKernelGGL(index_score_cpw_kernel<MODE == 0 ? 1 : MODE>,
+                               dim3((p.n_chunks + IDX_CPW - 1) / IDX_CPW, nq), dim3(IT),
+                               (size_t)p.chunk * 4 + (size_t)p.H * 72, s, ps);
+        else
+            hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, nq), dim3(IT), (size_t)p.chunk * 4 + q_lds, s,
+                               ps);
     }
     hipLaunchKernelGGL(index_merge_kernel<MODE>, dim3(p.Q), dim3(MT),
                        (size_t)(p.n_chunks + 1 + p.chunk) * 4 + q_lds, s, p);
