@@ -420,6 +420,18 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *row
 
 __device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *(const bf16x8 *)p; }
 
+// Two floats as hi + lo BF16 terms (hi = RNE(x), lo = RNE(x - hi)) into
+// elements e, e+1 of hi and lo, one conversion instruction per pair.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split_bf16x2(float a, float b, bf16x8 &hi, bf16x8 &lo, int e) {
+    const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);
+    const bf16x2 l = __builtin_convertvector((f32x2){a - (float)h[0], b - (float)h[1]}, bf16x2);
+    hi[e] = h[0];
+    hi[e + 1] = h[1];
+    lo[e] = l[0];
+    lo[e + 1] = l[1];
+}
+
 // V^T operand of the P.V product: lane (group g, position j) gets, for dim
 // 16*dt + j, the keys of its contraction slots: 4g..4g+3 and 16+4g..16+4g+3.
 // Each ds_read_b64_tr_b16 transposes a 16x4 block within the 16-lane group:
@@ -649,16 +661,15 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         lrun += swap32_sum(swap16_sum(psum));
         // P as two BF16 terms (hi + lo): one BF16 alone would cost 2^-9 of the
         // largest output element, which outliers in V turn into a visible error.
+        // (pairs of values per conversion instruction)
         bf16x8 pnh, pnl, pbh, pbl;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float xn = pr[st][j] * vs[st][j], xb = pr[st][j];
-                pnh[4 * st + j] = (__bf16)xn;
-                pnl[4 * st + j] = (__bf16)(xn - (float)pnh[4 * st + j]);
-                pbh[4 * st + j] = (__bf16)xb;
-                pbl[4 * st + j] = (__bf16)(xb - (float)pbh[4 * st + j]);
+            for (int j = 0; j < 4; j += 2) {
+                const int e = 4 * st + j;
+                split_bf16x2(pr[st][j] * vs[st][j], pr[st][j + 1] * vs[st][j + 1], pnh, pnl, e);
+                split_bf16x2(pr[st][j], pr[st][j + 1], pbh, pbl, e);
             }
 #pragma unroll
         for (int dt = 0; dt < 12; ++dt) {
