@@ -205,6 +205,31 @@ def test_index_mxfp4_many_queries_per_sequence():
         assert np.array_equal(idx1[:, 0], idx[:, i]) and np.array_equal(score1[:, 0], score[:, i]), f'query {i}'
 
 
+def test_index_mxfp4_tokens_sharing_a_large_key_set():
+    """Six tokens per sequence over 70,000 entries (4.8 MB of keys, more than an XCD's
+    L2), as when draft tokens are decoded together at a long context: tokens that see
+    all, part or none of the keys, and one token whose scaled head takes the exact pass.
+    Checked against the oracle, and bitwise against one call per token (the one-chunk
+    scorer)."""
+    rows, Tq = 70000, 6
+    q_pos = np.array([[rows * 4 - 1 - i for i in range(Tq)],
+                      [rows * 4 - 1, 123456, -1, 2, 4095, 200001]], np.int64)
+    c = _index_case_mx(41, 2, rows, q_pos, 1024)
+    sc, isc = c['sc'].copy(), c['isc'].copy()
+    sc[:, ::997] += 84                    # every 997th row x 2^84
+    isc[1, 1, 3] += 34                    # token 1 of batch 1: head 3 x 2^34 -> exact pass
+    c['sc'], c['isc'] = sc, isc
+    dkeys, diq = F.mxfp4_dequantize(c['packed'], sc), F.mxfp4_dequantize(c['ip'], isc)
+    print('index mxfp4, six tokens per sequence over 70000 entries', flush=True)
+    idx, score = _run_index(c)
+    _check_index(c, idx, score, dkeys, diq)
+    for i in range(Tq):
+        ci = dict(c, q_pos=c['q_pos'][:, i:i + 1], ip=c['ip'][:, i:i + 1], isc=c['isc'][:, i:i + 1],
+                  w=c['w'][:, i:i + 1])
+        idx1, score1 = _run_index(ci)
+        assert np.array_equal(idx1[:, 0], idx[:, i]) and np.array_equal(score1[:, 0], score[:, i]), f'token {i}'
+
+
 def test_index_mxfp4_repeat_is_bitwise_identical():
     q_pos = np.array([[12000 * 4 - 1]], np.int64)
     c = _index_case_mx(3, 1, 12000, q_pos, 256)
