@@ -22,6 +22,13 @@ The timed region is enqueued behind a spin kernel so that host-side launch
 cost never shows up as GPU idle time; HIP events bracket the region and, in a
 second instrumented pass, every launch of the indexer (the dominant kernel).
 Prints one JSON line.
+
+--workload prefill measures chunked prefill instead: one step is 8,192 new
+tokens appended to 131,072 cached ones through four layers (CSA, HCA, CSA,
+HCA), each compressing the new chunk, writing its raw rows into the window
+buffer and attending for every new token (the CSA layers through the indexer's
+top-1024). Its roofline line is the indexer's FP4 contraction against the
+MXFP4 MFMA peak.
 """
 
 import argparse
@@ -312,6 +319,174 @@ def cpu_baseline(seed):
                        f'caches not timed')}
 
 
+# ------------------------------------------------------------ chunked prefill ----
+
+PF_T0, PF_T1 = 131072, 8192
+PF_LAYERS = ('csa', 'hca', 'csa', 'hca')
+PF_METRIC = 'chunked-prefill tokens/s (8,192 new over 131,072 cached, layers CSA/HCA/CSA/HCA)'
+FP4_PEAK_TFLOPS = 10100.0
+
+
+def pf_index_flops():
+    """FP4 flops of one prefill indexer launch: every new token against its visible entries."""
+    n = sum((t + 1) // M_CSA for t in range(PF_T0, PF_T0 + PF_T1))
+    return 2.0 * HI * DI * n
+
+
+def build_prefill(v4, synth, torch, seed):
+    """Per layer: caches holding the 131,072 old tokens (compressed by the library), the
+    8,192 new raw tokens, and the queries; the prepared launches of one prefill pass."""
+    dev = 'cuda'
+    T = PF_T0 + PF_T1
+    zero1 = torch.zeros(1, device=dev)
+    ring = 128 * ((PF_T1 + W + 127) // 128)
+    pos = torch.arange(PF_T0, T, dtype=torch.int64, device=dev)[None]
+    o = torch.empty(1, PF_T1, H, D, dtype=torch.float32, device=dev)
+    idx = torch.empty(1, PF_T1, K, dtype=torch.int32, device=dev)
+    ws = v4.Workspace()
+    steps = []
+    for l, kind in enumerate(PF_LAYERS):
+        m = M_CSA if kind == 'csa' else M_HCA
+        N = T // m
+        rk = synth.gpu_normal(seed, f'pf/{l}/k', (1, T, D), dtype=torch.bfloat16)
+        rv = synth.gpu_normal(seed, f'pf/{l}/v', (1, T, D), dtype=torch.bfloat16)
+        ru = synth.gpu_normal(seed, f'pf/{l}/u', (1, T, DI), dtype=torch.bfloat16) if kind == 'csa' else None
+        gate = synth.gpu_normal(seed, f'pf/{l}/gate', (1, T))
+        bias = synth.gpu_normal(seed, f'pf/{l}/bias', (m,), 0.1)
+        ek, ev = v4.KVStore.empty(1, N, D), v4.KVStore.empty(1, N, D)
+        ik = v4.IKStore.empty(1, N, DI) if kind == 'csa' else None
+        wk, wv = v4.KVStore.empty(1, ring, D, ring=ring), v4.KVStore.empty(1, ring, D, ring=ring)
+        old = lambda x: None if x is None else x[:, :PF_T0].contiguous()
+        new = lambda x: None if x is None else x[:, PF_T0:].contiguous()
+        v4.csa_compress(old(gate), bias, 0, old(rk), old(rv), ek, ev, old(ru), ik)
+        v4.csa_compress(torch.zeros(1, W, device=dev), zero1, PF_T0 - W, rk[:, PF_T0 - W:PF_T0].contiguous(),
+                        rv[:, PF_T0 - W:PF_T0].contiguous(), wk, wv)
+        g_new, k_new, v_new, u_new = new(gate), new(rk), new(rv), new(ru)
+        del rk, rv, ru, gate
+        q = synth.gpu_normal(seed, f'pf/{l}/q', (1, PF_T1, H, D), outlier_frac=0.01, dtype=torch.bfloat16)
+        st = dict(kind=kind, keep=(g_new, k_new, v_new, u_new, q, ek, ev, ik, wk, wv, bias),
+                  comp=v4.csa_compress(g_new, bias, PF_T0, k_new, v_new, ek, ev, u_new, ik, prepare=True),
+                  win=v4.csa_compress(torch.zeros(1, PF_T1, device=dev), zero1, PF_T0, k_new, v_new, wk, wv,
+                                      prepare=True))
+        if kind == 'csa':
+            iq_f = synth.gpu_normal(seed, f'pf/{l}/iq', (1, PF_T1, HI, DI), outlier_frac=0.01)
+            iq_store = v4.IKStore.empty(1, PF_T1 * HI, DI)
+            v4.csa_compress(torch.zeros(1, PF_T1 * HI, device=dev), zero1, 0,
+                            raw_ik=iq_f.reshape(1, PF_T1 * HI, DI), ik_out=iq_store)
+            del iq_f
+            iq = iq_store.e2m1.reshape(1, PF_T1, HI, DI // 2)
+            iqs = iq_store.e8m0.reshape(1, PF_T1, HI, DI // 32)
+            w = synth.gpu_uniform(seed, f'pf/{l}/w', (1, PF_T1, HI))
+            st['keep'] += (iq_store, w)
+            st['index'] = v4.lightning_index_topk(pos, iq, w, ik, K, m, iq_scale=iqs, out_idx=idx, workspace=ws,
+                                                  prepare=True)
+            st['attn'] = v4.sparse_window_attn(q, pos, ek, ev, m, wk, wv, W, idx, o=o, workspace=ws,
+                                               prepare=True)
+        else:
+            st['attn'] = v4.hca_attn(q, pos, ek, ev, m, wk, wv, W, o=o, workspace=ws, prepare=True)
+        steps.append(st)
+    torch.cuda.synchronize()
+    return steps
+
+
+def run_prefill(steps, ev=None):
+    """One prefill pass; ev (if given) gets a start and an end event around each indexer launch."""
+    for i, st in enumerate(steps):
+        st['comp']()
+        st['win']()
+        if 'index' in st:
+            if ev is not None:
+                ev[i][0].record()
+            st['index']()
+            if ev is not None:
+                ev[i][1].record()
+        st['attn']()
+
+
+def cpu_baseline_prefill(seed):
+    """The oracle on a sample of new tokens of the prefill workload (one CSA and one HCA
+    layer per token, entry-level caches of the same sizes)."""
+    sys.path.insert(0, ROOT)
+    import synth
+    from oracle import formats as F
+    from oracle import model as OM
+    T = PF_T0 + PF_T1
+    threads = int(os.environ.get('OMP_NUM_THREADS', 0)) or len(os.sched_getaffinity(0))
+    n_csa, n_hca = T // M_CSA, T // M_HCA
+    x = synth.entries(seed, 1, n_csa, D, DI, W, 0.01, prefix='cpu_pf')
+    ik = F.mxfp4_dequantize(*F.mxfp4_quantize(x['ik'][0]))
+    ek, evv = F.kv_dequantize(*F.kv_quantize(x['ent_k'][0])), F.kv_dequantize(*F.kv_quantize(x['ent_v'][0]))
+    wk, wv = F.kv_dequantize(*F.kv_quantize(x['win_k'][0])), F.kv_dequantize(*F.kv_quantize(x['win_v'][0]))
+    hx = synth.entries(seed + 1, 1, n_hca, D, 0, W, prefix='cpu_pfh')
+    hk, hv = F.kv_dequantize(*F.kv_quantize(hx['ent_k'][0])), F.kv_dequantize(*F.kv_quantize(hx['ent_v'][0]))
+    NQ = 32
+    qs = synth.queries(seed, 1, NQ, H, D, HI, DI, outlier_frac=0.01, prefix='cpu_pfq')
+    iqs = F.mxfp4_dequantize(*F.mxfp4_quantize(qs['iq'][0]))
+    n, el = 0, 0.0
+    while el < CPU_SAMPLE_S:
+        i = n % NQ
+        t = PF_T0 + (n * 2749) % PF_T1          # spread over the new chunk
+        t0 = time.perf_counter()
+        # the window rows of the sample are the last W rows, placed at (t - W, t]
+        OM.csa_query(qs['q'][0, i], t, iqs[i], qs['w'][0, i], ik, ek, evv, wk, wv, M_CSA, K, W, win_first=t - W + 1)
+        OM.hca_query(qs['q'][0, i], t, hk, hv, wk, wv, M_HCA, W, win_first=t - W + 1)
+        el += time.perf_counter() - t0
+        n += 1
+    per_token_s = el / (2 * n)            # one layer
+    return {'value': round(1.0 / (per_token_s * len(PF_LAYERS)), 4), 'unit': 'tokens/s', 'cores': int(threads),
+            'kind': 'oracle',
+            'sample': (f'{n} new tokens, each through one CSA layer (score up to {n_csa} MXFP4 keys, top-{K}, '
+                       f'attend {K}+{W} keys) and one HCA layer (attend up to {n_hca}+{W} keys), {el:.1f} s; '
+                       f'scaled to the four layers of a pass; float64 numpy; the new chunk\'s compression and '
+                       f'the decoding of the caches not timed')}
+
+
+def prefill_main(a):
+    import torch
+    import long_context_attention_compress_amd as v4
+    import synth
+    print('[bench] building the prefill layers (131,072 + 8,192 tokens, 4 layers)', file=sys.stderr, flush=True)
+    steps = build_prefill(v4, synth, torch, a.seed)
+    print('[bench] warmup', file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        run_prefill(steps)
+    torch.cuda.synchronize()
+    print('[bench] timed', file=sys.stderr, flush=True)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(a.steps):
+        run_prefill(steps)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / a.steps
+    n_idx = sum(1 for st in steps if 'index' in st)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in steps] for _ in range(a.steps)]
+    for r in range(a.steps):
+        run_prefill(steps, evs[r])
+    torch.cuda.synchronize()
+    idx_ms = sum(e[i][0].elapsed_time(e[i][1]) for e in evs for i, st in enumerate(steps) if 'index' in st) \
+        / (a.steps * n_idx)
+    achieved = pf_index_flops() / (idx_ms * 1e-3) / 1e12
+    rec = {
+        'metric': PF_METRIC, 'value': round(PF_T1 / (ms * 1e-3), 1), 'unit': 'tokens/s', 'n_gpus': 1,
+        'steps': a.steps, 'warmup': a.warmup, 'ms_per_step': round(ms, 6), 'higher_is_better': True,
+        'scaling': 'weak', 'vs_baseline': None, 'dtype': 'mxfp4+e4m3/bf16', 'data': 'synthetic',
+        'config': {'workload': 'chunked prefill: 8,192 new tokens over 131,072 cached, one sequence, layers '
+                               'CSA (m=4, top-1024) / HCA (m=128) / CSA / HCA, window 128; each layer compresses '
+                               'the new chunk, writes its raw rows into the window buffer and attends for every '
+                               'new token; 64 query heads, KV dim 192 (E4M3 + BF16 RoPE), MXFP4 indexer 64x128',
+                   'batch': 1, 'context': PF_T0 + PF_T1, 'new_tokens': PF_T1, 'parallelism': 'single GPU'},
+        'roofline': {'bound': 'mfma', 'kernel': 'lightning_index_topk (FP4 contraction)',
+                     'achieved': round(achieved, 1), 'peak': FP4_PEAK_TFLOPS, 'unit': 'TFLOP/s',
+                     'frac': round(achieved / FP4_PEAK_TFLOPS, 4), 'traffic': None},
+        'breakdown_ms': {'index_per_csa_layer': round(idx_ms, 4)},
+    }
+    if not a.no_cpu_baseline:
+        print('[bench] cpu baseline (oracle)', file=sys.stderr, flush=True)
+        rec['cpu_baseline'] = cpu_baseline_prefill(a.seed)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -320,12 +495,15 @@ def main():
     ap.add_argument('--layers', type=int, default=16)
     ap.add_argument('--seed', type=int, default=7)
     ap.add_argument('--no-cpu-baseline', action='store_true')
+    ap.add_argument('--workload', choices=('decode', 'prefill'), default='decode')
     a = ap.parse_args()
     if a.gpus != 1:
         print('bench.py measures one GPU: the hot path is data-parallel over sequences and needs no '
               'inter-GPU exchange, so N GPUs each run this same single-GPU workload on their own batch. '
               'Run it with --gpus 1.', file=sys.stderr)
         sys.exit(2)
+    if a.workload == 'prefill':
+        return prefill_main(a)
     import torch
     import long_context_attention_compress_amd as v4
     import synth

@@ -7,8 +7,8 @@
 // große Wirkung", section "Komprimierte Erinnerung für längere Kontexte"]: the
 // last 64 values carry RoPE and stay BF16, the rest is FP8.
 //
-// One wave per (entry, batch element) for long blocks, three (one per output)
-// for blocks of up to four tokens. The gate weights, the RoPE rotation and the
+// One wave per (entry, batch element, output) for long blocks, three waves
+// (one per output) in one workgroup for blocks of up to four tokens. The gate weights, the RoPE rotation and the
 // weighted sum are evaluated in float64 and the entry is rounded to float32
 // before it is encoded, so every encoding decision (FP8 scale and codes, BF16
 // rounding, MX exponent and E2M1 codes) is taken on a float32 value.
@@ -85,15 +85,37 @@ __device__ __forceinline__ void store_ik_value(const IkView &s, int b, int64_t e
         ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[d >> 5] = nbad ? 0xFF : (uint8_t)(E + 127);
 }
 
+// sum_r alpha[r] * x(r) over r < m in float64, as four interleaved partial
+// sums (independent FMA chains) added pairwise at the end.
+template <class F>
+__device__ __forceinline__ double pooled(const double *alpha, int m, F x) {
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int r = 0;
+    for (; r + 4 <= m; r += 4) {
+        a0 += alpha[r] * x(r);
+        a1 += alpha[r + 1] * x(r + 1);
+        a2 += alpha[r + 2] * x(r + 2);
+        a3 += alpha[r + 3] * x(r + 3);
+    }
+    for (; r < m; ++r) a0 += alpha[r] * x(r);
+    return (a0 + a1) + (a2 + a3);
+}
+
+// One wave per (block, batch element, output): blockIdx.z = 0 the K entry,
+// 1 the V entry, 2 the indexer key; each evaluates the gate softmax itself.
 template <int ACT>
 __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
     __shared__ double alpha[MAX_M];
     const int lane = lane_id();
     const int j = blockIdx.x;  // block within the chunk
     const int b = blockIdx.y;
+    const int role = blockIdx.z;
     const int m = p.m;
     const int64_t tok0 = (int64_t)j * m;                 // first raw token of the block (chunk-relative)
     const int64_t entry = p.pos0 / m + j;
+    // A ring store keeps only the last `ring` entries written by one call.
+    const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
+    if (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik) return;  // uniform per workgroup
 
     // alpha_r = softmax_r(gate + pos_bias), float64
     double zmax = -__builtin_inf();
@@ -113,55 +135,61 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
     for (int r = lane; r < m; r += 64) alpha[r] = alpha[r] / zsum;
     __syncthreads();
 
-    // A ring store keeps only the last `ring` entries written by one call.
-    const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
-    if (p.has_kv && kv_keep) {
+    if (role < 2) {
+        // values (never rotated) and keys (rotated at each token's position)
         const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
         const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * D;
-        // values (never rotated) and keys (rotated at each token's position)
-        for (int which = 0; which < 2; ++which) {
-            const void *src = which == 0 ? p.raw_k : p.raw_v;
-            float nope[4];
-            for (int i = 0; i < nit; ++i) {
-                double acc = 0.0;
-                for (int r = 0; r < m; ++r) acc += alpha[r] * load_act<ACT>(src, rowbase + (int64_t)r * D + lane + 64 * i);
-                nope[i] = (float)acc;
-            }
-            float rx = 0.0f, ry = 0.0f;
-            if (lane < ROPE_PAIRS) {
-                double ax = 0.0, ay = 0.0;
-                const double f = p.inv_freq[lane];
-                for (int r = 0; r < m; ++r) {
-                    double x = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane);
-                    double y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
-                    if (which == 0) {
-                        double sn, cs, xr, yr;
-                        rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
-                        rope_rotate(x, y, sn, cs, &xr, &yr);
-                        x = xr;
-                        y = yr;
-                    }
-                    ax += alpha[r] * x;
-                    ay += alpha[r] * y;
+        const void *src = role == 0 ? p.raw_k : p.raw_v;
+        float nope[4];
+        for (int i = 0; i < nit; ++i)
+            nope[i] = (float)pooled(alpha, m, [&](int r) {
+                return load_act<ACT>(src, rowbase + (int64_t)r * D + lane + 64 * i);
+            });
+        float rx = 0.0f, ry = 0.0f;
+        if (lane < ROPE_PAIRS) {
+            const double f = p.inv_freq[lane];
+            auto pair = [&](int r, double *x, double *y) {
+                *x = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane);
+                *y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
+                if (role == 0) {
+                    double sn, cs, xr, yr;
+                    rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                    rope_rotate(*x, *y, sn, cs, &xr, &yr);
+                    *x = xr;
+                    *y = yr;
                 }
-                rx = (float)ax;
-                ry = (float)ay;
+            };
+            double ax[4] = {0.0, 0.0, 0.0, 0.0}, ay[4] = {0.0, 0.0, 0.0, 0.0};
+            int r = 0;
+            for (; r + 4 <= m; r += 4)
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    double x, y;
+                    pair(r + u, &x, &y);
+                    ax[u] += alpha[r + u] * x;
+                    ay[u] += alpha[r + u] * y;
+                }
+            for (; r < m; ++r) {
+                double x, y;
+                pair(r, &x, &y);
+                ax[0] += alpha[r] * x;
+                ay[0] += alpha[r] * y;
             }
-            const KvView &dst = which == 0 ? p.k : p.v;
-            store_kv_row(dst, b, kv_row(dst, entry), nope, nit, rx, ry);
+            rx = (float)((ax[0] + ax[1]) + (ax[2] + ax[3]));
+            ry = (float)((ay[0] + ay[1]) + (ay[2] + ay[3]));
         }
-    }
-
-    if (p.has_ik) {
+        const KvView &dst = role == 0 ? p.k : p.v;
+        store_kv_row(dst, b, kv_row(dst, entry), nope, nit, rx, ry);
+    } else {
         const int dI = p.dI, nit = dI / 64 + (dI % 64 ? 1 : 0);
         const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * dI;
         const IkView &s = p.ik;
         for (int i = 0; i < nit; ++i) {
             const int d = lane + 64 * i;
             const bool on = d < dI;
-            double acc = 0.0;
-            if (on)
-                for (int r = 0; r < m; ++r) acc += alpha[r] * load_act<ACT>(p.raw_ik, rowbase + (int64_t)r * dI + d);
+            const double acc = on ? pooled(alpha, m, [&](int r) {
+                return load_act<ACT>(p.raw_ik, rowbase + (int64_t)r * dI + d);
+            }) : 0.0;
             store_ik_value(s, b, entry, d, on, (float)acc);
         }
     }
@@ -329,8 +357,11 @@ hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
     if (p.m <= SMALL_M) {
         if (p.act == 0) launch_small<0>(p, grid, s);
         else launch_small<1>(p, grid, s);
-    } else if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, grid, dim3(64), 0, s, p);
-    else hipLaunchKernelGGL(compress_kernel<1>, grid, dim3(64), 0, s, p);
+    } else {
+        const dim3 g3(grid.x, grid.y, 3);  // K, V, indexer key
+        if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, g3, dim3(64), 0, s, p);
+        else hipLaunchKernelGGL(compress_kernel<1>, g3, dim3(64), 0, s, p);
+    }
     return hipGetLastError();
 }
 
