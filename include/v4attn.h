@@ -151,7 +151,9 @@ typedef struct {
  * how the window is filled.
  *
  *  B, t_new    batch size (1 .. 65535) and raw tokens per batch element
- *              (t_new % m == 0).
+ *              (t_new % m == 0). t_new = 0 returns V4A_OK once B, m, pos0 and
+ *              act_fmt are valid; then no pointer is read and nothing is
+ *              enqueued.
  *  pos0        position of the first raw token (pos0 % m == 0, >= 0).
  *  m           1 .. 1024.
  *  act_fmt     format of raw_k, raw_v, raw_ik (float32 or bfloat16).

@@ -332,6 +332,7 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
     if (a->pos0 < 0 || a->pos0 % a->m || a->t_new % a->m)
         return fail(V4A_EINVAL, "pos0 and t_new must be non-negative multiples of m");
     if (a->act_fmt != V4A_ACT_F32 && a->act_fmt != V4A_ACT_BF16) return fail(V4A_EFORMAT, "unknown activation format");
+    if (a->t_new == 0) return V4A_OK;  // nothing to compress: no pointer is read, nothing is launched
     if (!a->gate || !a->pos_bias) return fail(V4A_ENULL, "gate and pos_bias are required");
     if ((a->k_out == nullptr) != (a->v_out == nullptr)) return fail(V4A_ENULL, "k_out and v_out must both be given or both NULL");
     if ((a->ik_out == nullptr) != (a->raw_ik == nullptr)) return fail(V4A_ENULL, "raw_ik and ik_out go together");

@@ -88,6 +88,11 @@ def test_compress_rejections():
     for kw, want in cases:
         r, msg = _status('csa_compress', args(**kw), None)
         assert r == want, (kw, r, msg)
+    # zero tokens: a no-op once the sizes are valid, whatever the pointers
+    r, msg = _status('csa_compress', args(t_new=0, gate=None, raw_k=None, raw_v=None, raw_ik=None), None)
+    assert r == _abi.V4A_OK, msg
+    r, _ = _status('csa_compress', args(t_new=0, m=0), None)
+    assert r == _abi.V4A_EINVAL
     bad_dim = _kv(dim=128)
     r, _ = _status('csa_compress', args(k_out=ctypes.pointer(bad_dim), v_out=ctypes.pointer(bad_dim)), None)
     assert r == _abi.V4A_EFORMAT

@@ -542,6 +542,49 @@ def test_c0_fp32_layer_end_to_end():
             assert_close_rms(o2.cpu().numpy()[0, 0], ro, TOL_F32, f'o q{i} (oracle selection)')
 
 
+def test_empty_inputs():
+    """Calls with nothing to do: compression of zero tokens leaves the stores as they
+    were; an index call whose queries see no entry (t = -1, 0, 2 with m = 4) returns only
+    padding; attention for a query with an empty key list (t = -1) gives o = 0 and
+    lse = -inf, next to a query at t = 0 (window row 0 only) checked against the oracle."""
+    B, D, m = 1, 192, 4
+    ks, vs = v4.KVStore.empty(B, 8, D), v4.KVStore.empty(B, 8, D)
+    iks = v4.IKStore.empty(B, 8, 128)
+    for t in (ks.nope, vs.nope, iks.e2m1, iks.e8m0):
+        t.fill_(0xAB)
+    before = [t.clone() for t in (ks.nope, ks.rope, ks.scale, vs.nope, iks.e2m1, iks.e8m0)]
+    g = torch.zeros(B, 8, device='cuda')
+    raw = torch.ones(B, 8, D, dtype=torch.bfloat16, device='cuda')
+    u = torch.ones(B, 8, 128, dtype=torch.bfloat16, device='cuda')
+    print('empty compress', flush=True)
+    v4.csa_compress(g[:, :0], torch.zeros(m, device='cuda'), 0, raw[:, :0], raw[:, :0], ks, vs, u[:, :0], iks)
+    torch.cuda.synchronize()
+    after = (ks.nope, ks.rope, ks.scale, vs.nope, iks.e2m1, iks.e8m0)
+    assert all(torch.equal(a, b) for a, b in zip(before, after))
+
+    q_pos = np.array([[-1, 0, 2]], np.int64)
+    c = _index_case_mx(51, 1, 100, q_pos, 16)
+    print('index with no visible entries', flush=True)
+    idx, score = _run_index(c)
+    assert np.all(idx == -1) and np.all(score == 0)
+
+    q_pos = np.array([[-1, 0]], np.int64)
+    a = _attn_case(52, 1, 2, 64, D, 50, q_pos, 'fp8')
+    ek, ev, wk, wv = _stores(a)
+    ids = np.full((1, 2, 8), -1, np.int32)
+    lse = torch.zeros(1, 2, 64, dtype=torch.float32, device='cuda')
+    print('attention over empty key lists', flush=True)
+    for name, o in (('sparse', v4.sparse_window_attn(_qdev(a), dev(q_pos), ek, ev, m, wk, wv, a['W'], dev(ids),
+                                                      lse=lse)),
+                    ('dense', v4.hca_attn(_qdev(a), dev(q_pos), ek, ev, m, wk, wv, a['W'], lse=lse))):
+        torch.cuda.synchronize()
+        o, l = o.float().cpu().numpy(), lse.cpu().numpy()
+        assert np.all(o[0, 0] == 0) and np.all(np.isneginf(l[0, 0])), name
+        ro, rl = _oracle_attn(a, 0, 1, np.arange(0))
+        assert_close_rms(o[0, 1], ro, TOL_BF16, f'{name} t=0')
+        assert np.allclose(l[0, 1], rl, atol=2e-2), name
+
+
 def test_attn_bf16_output():
     """bfloat16 output: the kernel's error plus the output's own rounding (2^-8 relative)."""
     B, Tq, rows, H, D = 1, 2, 600, 64, 192
