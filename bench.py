@@ -29,6 +29,11 @@ HCA), each compressing the new chunk, writing its raw rows into the window
 buffer and attending for every new token (the CSA layers through the indexer's
 top-1024). Its roofline line is the indexer's FP4 contraction against the
 MXFP4 MFMA peak.
+
+--workload stack runs the decode step through a 43-layer attention stack (two
+window-only layers, then CSA and HCA alternating) at 1M context, four steps
+captured in one HIP graph, and reports the graph's time per step next to the
+eagerly enqueued one.
 """
 
 import argparse
@@ -487,6 +492,128 @@ def prefill_main(a):
     print(json.dumps(rec), flush=True)
 
 
+# ---------------------------------------------------------------- layer stack ----
+
+STACK_LAYERS = 43  # 2 window-only, then CSA and HCA alternating (21 + 20)
+STACK_METRIC = 'decode query-tokens/s through a 43-layer attention stack at 1M ctx (one HIP graph)'
+
+
+def stack_kinds(n):
+    return ['win', 'win'] + ['csa' if i % 2 == 0 else 'hca' for i in range(n - 2)]
+
+
+def prepare_stack(v4, synth, torch, seed, n_layers, stream):
+    """Caches and prepared launches of every layer of the stack, bound to `stream`."""
+    kinds = stack_kinds(n_layers)
+    n_csa = kinds.count('csa')
+    # one copy of the caches per CSA layer and per HCA or window-only layer (no sharing)
+    layers, inputs = build_layers(v4, synth, torch, max(n_csa, n_layers - n_csa), seed)
+    dev = 'cuda'
+    pos = torch.full((B, 1), T - 1, dtype=torch.int64, device=dev)
+    new_k = synth.gpu_normal(seed, 'stack/k', (B, 1, D), dtype=torch.bfloat16)
+    new_v = synth.gpu_normal(seed, 'stack/v', (B, 1, D), dtype=torch.bfloat16)
+    blk_k4 = synth.gpu_normal(seed, 'stack/k4', (B, M_CSA, D), dtype=torch.bfloat16)
+    blk_v4 = synth.gpu_normal(seed, 'stack/v4', (B, M_CSA, D), dtype=torch.bfloat16)
+    blk_u4 = synth.gpu_normal(seed, 'stack/u4', (B, M_CSA, DI), dtype=torch.bfloat16)
+    g4 = synth.gpu_normal(seed, 'stack/g4', (B, M_CSA))
+    idx = torch.zeros(B, 1, K, dtype=torch.int32, device=dev)
+    outs, calls = [], []
+    ws_i, ws_a = v4.Workspace(), v4.Workspace()
+    ci = hi = 0
+    with torch.cuda.stream(stream):
+        for kind in kinds:
+            o = torch.zeros(B, 1, H, D, dtype=torch.float32, device=dev)
+            outs.append(o)
+            if kind == 'csa':
+                Ld = layers[ci]
+                ci += 1
+                calls.append(dict(
+                    block=v4.csa_compress(g4, inputs['bias4'], T - M_CSA, blk_k4, blk_v4, Ld['ek'], Ld['ev'], blk_u4,
+                                          Ld['ik'], prepare=True),
+                    run=[v4.lightning_index_topk(pos, inputs['iq'], inputs['w'], Ld['ik'], K, M_CSA,
+                                                 iq_scale=inputs['iq_scale'], out_idx=idx, workspace=ws_i,
+                                                 prepare=True),
+                         v4.sparse_window_attn(inputs['q_csa'], pos, Ld['ek'], Ld['ev'], M_CSA, Ld['cwk'], Ld['cwv'],
+                                               W, idx, o=o, workspace=ws_a, prepare=True, append_k=new_k,
+                                               append_v=new_v)]))
+            else:
+                Ld = layers[hi]
+                hi += 1
+                win = kind == 'win'
+                calls.append(dict(block=None, run=[v4.hca_attn(
+                    inputs['q_hca'], pos, None if win else Ld['hk'], None if win else Ld['hv'], M_HCA, Ld['hwk'],
+                    Ld['hwv'], W, n_entries_override=0 if win else -1, o=o, workspace=ws_a, prepare=True,
+                    append_k=new_k, append_v=new_v)]))
+    torch.cuda.synchronize()
+    return calls, outs, (layers, inputs, pos, new_k, new_v, blk_k4, blk_v4, blk_u4, g4, idx, ws_i, ws_a)
+
+
+def run_stack(calls, step):
+    """One decode step through the stack: each CSA layer compresses its finished block
+    of four every fourth step (the HCA layers' block of 128 comes once per 128 steps
+    and is left out)."""
+    for c in calls:
+        if c['block'] is not None and step % M_CSA == M_CSA - 1:
+            c['block']()
+        for f in c['run']:
+            f()
+
+
+def stack_main(a):
+    import torch
+    import long_context_attention_compress_amd as v4
+    import synth
+    n = a.stack_layers
+    print(f'[bench] building a {n}-layer stack (B={B}, context {T})', file=sys.stderr, flush=True)
+    s = torch.cuda.Stream()
+    calls, outs, keep = prepare_stack(v4, synth, torch, a.seed, n, s)
+    with torch.cuda.stream(s):
+        for i in range(max(a.warmup, M_CSA)):
+            run_stack(calls, i)
+    torch.cuda.synchronize()
+    # eager: four steps enqueued directly (host launch cost included)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    reps = max(1, a.steps // M_CSA)
+    with torch.cuda.stream(s):
+        ev[0].record()
+        for r in range(reps):
+            for i in range(M_CSA):
+                run_stack(calls, i)
+        ev[1].record()
+    torch.cuda.synchronize()
+    eager_ms = ev[0].elapsed_time(ev[1]) / (reps * M_CSA)
+    # one graph holds four steps (so each CSA layer's block compression appears once)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(M_CSA):
+            run_stack(calls, i)
+    g.replay()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ev[0].record()
+        for r in range(reps):
+            g.replay()
+        ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / (reps * M_CSA)
+    kinds = stack_kinds(n)
+    rec = {
+        'metric': STACK_METRIC, 'value': round(B / (ms * 1e-3), 1), 'unit': 'query-tokens/s', 'n_gpus': 1,
+        'steps': reps * M_CSA, 'warmup': max(a.warmup, M_CSA), 'ms_per_step': round(ms, 6),
+        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None, 'dtype': 'mxfp4+e4m3/bf16',
+        'data': 'synthetic',
+        'config': {'workload': f'decode at 1,048,576-token context, batch 4, through {n} attention layers: '
+                               f'{kinds.count("win")} window-only, {kinds.count("csa")} CSA (m=4, top-1024, block '
+                               f'compression every 4th step), {kinds.count("hca")} HCA (m=128); every layer appends '
+                               'the new token to its window inside the attention launch; four steps captured in '
+                               'one HIP graph and replayed',
+                   'batch': B, 'context': T, 'layers': n, 'parallelism': 'single GPU'},
+        'eager_ms_per_step': round(eager_ms, 6),
+        'roofline': None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -495,7 +622,8 @@ def main():
     ap.add_argument('--layers', type=int, default=16)
     ap.add_argument('--seed', type=int, default=7)
     ap.add_argument('--no-cpu-baseline', action='store_true')
-    ap.add_argument('--workload', choices=('decode', 'prefill'), default='decode')
+    ap.add_argument('--workload', choices=('decode', 'prefill', 'stack'), default='decode')
+    ap.add_argument('--stack-layers', type=int, default=STACK_LAYERS)
     a = ap.parse_args()
     if a.gpus != 1:
         print('bench.py measures one GPU: the hot path is data-parallel over sequences and needs no '
@@ -504,6 +632,8 @@ def main():
         sys.exit(2)
     if a.workload == 'prefill':
         return prefill_main(a)
+    if a.workload == 'stack':
+        return stack_main(a)
     import torch
     import long_context_attention_compress_amd as v4
     import synth

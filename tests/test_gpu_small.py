@@ -585,6 +585,87 @@ def test_empty_inputs():
         assert np.allclose(l[0, 1], rl, atol=2e-2), name
 
 
+def test_layer_stack_graph_replays():
+    """A decode step through a small stack (window-only, CSA, HCA, CSA; B = 2, 8,192
+    tokens of context), four steps captured in one HIP graph: three replays, with eager
+    work and synchronisations between them, each give outputs bitwise equal to the
+    eager steps (the block compression and the window appends rewrite the same rows)."""
+    B, T, D, H, HI, DI, K, W = 2, 8192, 192, 64, 64, 128, 256, 128
+    g = torch.Generator(device='cuda').manual_seed(61)
+    rn = lambda *sh: torch.randn(*sh, generator=g, device='cuda')
+    z1 = torch.zeros(1, device='cuda')
+    pos = torch.full((B, 1), T - 1, dtype=torch.int64, device='cuda')
+    s = torch.cuda.Stream()
+
+    def caches(m, ik):
+        n = T // m
+        ek, ev = v4.KVStore.empty(B, n, D), v4.KVStore.empty(B, n, D)
+        iks = v4.IKStore.empty(B, n, DI) if ik else None
+        v4.csa_compress(rn(B, T), rn(m) * 0.1, 0, rn(B, T, D).bfloat16(), rn(B, T, D).bfloat16(), ek, ev,
+                        rn(B, T, DI).bfloat16() if ik else None, iks)
+        wk, wv = v4.KVStore.empty(B, W, D, ring=W), v4.KVStore.empty(B, W, D, ring=W)
+        v4.csa_compress(torch.zeros(B, W, device='cuda'), z1, T - W, rn(B, W, D).bfloat16(), rn(B, W, D).bfloat16(),
+                        wk, wv)
+        return ek, ev, iks, wk, wv
+
+    iq_store = v4.IKStore.empty(1, B * HI, DI)
+    v4.csa_compress(torch.zeros(1, B * HI, device='cuda'), z1, 0, raw_ik=rn(1, B * HI, DI), ik_out=iq_store)
+    iq, iqs = iq_store.e2m1.reshape(B, 1, HI, DI // 2), iq_store.e8m0.reshape(B, 1, HI, DI // 32)
+    w = torch.rand(B, 1, HI, generator=g, device='cuda')
+    q = rn(B, 1, H, D).bfloat16()
+    nk, nv = rn(B, 1, D).bfloat16(), rn(B, 1, D).bfloat16()
+    bk, bv, bu, bg = rn(B, 4, D).bfloat16(), rn(B, 4, D).bfloat16(), rn(B, 4, DI).bfloat16(), rn(B, 4)
+    b4 = rn(4) * 0.1
+    idx = torch.zeros(B, 1, K, dtype=torch.int32, device='cuda')
+    wsi, wsa = v4.Workspace(), v4.Workspace()
+    layers, outs = [], []
+    with torch.cuda.stream(s):
+        for kind in ('win', 'csa', 'hca', 'csa'):
+            o = torch.zeros(B, 1, H, D, device='cuda')
+            outs.append(o)
+            if kind == 'csa':
+                ek, ev, iks, wk, wv = caches(4, True)
+                layers.append((v4.csa_compress(bg, b4, T - 4, bk, bv, ek, ev, bu, iks, prepare=True),
+                               [v4.lightning_index_topk(pos, iq, w, iks, K, 4, iq_scale=iqs, out_idx=idx,
+                                                        workspace=wsi, prepare=True),
+                                v4.sparse_window_attn(q, pos, ek, ev, 4, wk, wv, W, idx, o=o, workspace=wsa,
+                                                      prepare=True, append_k=nk, append_v=nv)]))
+            else:
+                ek, ev, _, wk, wv = caches(128, False)
+                win = kind == 'win'
+                layers.append((None, [v4.hca_attn(q, pos, None if win else ek, None if win else ev, 128, wk, wv, W,
+                                                  n_entries_override=0 if win else -1, o=o, workspace=wsa,
+                                                  prepare=True, append_k=nk, append_v=nv)]))
+
+    def steps():
+        for i in range(4):
+            for blk, run in layers:
+                if blk is not None and i == 3:
+                    blk()
+                for f in run:
+                    f()
+    print('layer stack: eager', flush=True)
+    with torch.cuda.stream(s):
+        steps()
+        steps()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        steps()
+    for r in range(3):
+        for o in outs:
+            o.fill_(float('nan'))
+        print(f'layer stack: replay {r}', flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, e) for o, e in zip(outs, ref)), f'replay {r}'
+        with torch.cuda.stream(s):   # eager work between replays
+            steps()
+        torch.cuda.synchronize()
+        assert all(torch.equal(o, e) for o, e in zip(outs, ref)), f'eager after replay {r}'
+
+
 def test_attn_bf16_output():
     """bfloat16 output: the kernel's error plus the output's own rounding (2^-8 relative)."""
     B, Tq, rows, H, D = 1, 2, 600, 64, 192
