@@ -180,10 +180,10 @@ def test_index_mxfp4_exponent_extremes():
 
 def test_index_mxfp4_many_queries_per_sequence():
     """Thirteen queries per sequence in one call: positions in and out of order, queries
-    that see nothing or only part of a chunk, and one query whose scaled head sends its
-    tiles to the exact pass while its neighbours take the fast form. Checked against the
-    oracle, and bitwise against one call per query (no state leaks between the queries
-    of a call)."""
+    that see nothing or only part of a chunk, one query whose scaled head sends its tiles
+    to the exact pass while its neighbours take the fast form, and one with a NaN query
+    exponent (every tile exact). Checked against the oracle, and bitwise against one call
+    per query (no state leaks between the queries of a call)."""
     rows, Tq = 6000, 13
     g = np.random.default_rng(21)
     q_pos = np.stack([np.arange(rows * 4 - Tq, rows * 4),
@@ -193,6 +193,7 @@ def test_index_mxfp4_many_queries_per_sequence():
     sc, isc = c['sc'].copy(), c['isc'].copy()
     sc[:, ::97] += 84                     # rows 0, 97, ...: x 2^84
     isc[1, 3, 3] += 34                    # query 3 of batch 1: head 3 x 2^34 -> exact pass
+    isc[0, 6, 9, 2] = 0xFF                # query 6 of batch 0: a NaN block -> every tile exact
     c['sc'], c['isc'] = sc, isc
     dkeys, diq = F.mxfp4_dequantize(c['packed'], sc), F.mxfp4_dequantize(c['ip'], isc)
     print('index mxfp4 multi-query', flush=True)
