@@ -283,6 +283,37 @@ def test_csa_with_all_selected_equals_hca():
     assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12) and np.allclose(l1, l2)
 
 
+def test_chunked_prefill_equals_one_shot():
+    """P10: compressing a prefix in two chunks (the second starting at its own position)
+    gives exactly the one-shot entries, and a query in the first chunk gets the same CSA
+    and HCA results from the first chunk's caches alone as from the full caches, whose
+    later entries and window rows it must not see."""
+    g = np.random.default_rng(71)
+    T, t0, D, dI, H, HI, m = 64, 32, 128, 64, 4, 4, 4
+    rk, rv = g.standard_normal((1, T, D)).astype(np.float32), g.standard_normal((1, T, D)).astype(np.float32)
+    ru = g.standard_normal((1, T, dI)).astype(np.float32)
+    gate = g.standard_normal((1, T)).astype(np.float32)
+    bias = (0.1 * g.standard_normal(m)).astype(np.float32)
+    one = C.compress(rk, rv, gate, bias, 0, raw_ik=ru)
+    a = C.compress(rk[:, :t0], rv[:, :t0], gate[:, :t0], bias, 0, raw_ik=ru[:, :t0])
+    b = C.compress(rk[:, t0:], rv[:, t0:], gate[:, t0:], bias, t0, raw_ik=ru[:, t0:])
+    for x, y, z in zip(one, a, b):
+        assert np.array_equal(x, np.concatenate([y, z], axis=1))
+    full = M.build_caches(rk, rv, gate, bias, 'f32', raw_ik=ru, ik_fmt='f32')
+    half = M.build_caches(rk[:, :t0], rv[:, :t0], gate[:, :t0], bias, 'f32', raw_ik=ru[:, :t0], ik_fmt='f32')
+    for t in (2, 3, 17, t0 - 1):
+        q, iq = g.standard_normal((H, D)), g.standard_normal((HI, dI))
+        w = g.uniform(size=HI)
+        got = []
+        for c in (full, half):
+            got.append((M.csa_query(q, t, iq, w, c['dik'][0], c['dk'][0], c['dv'][0], c['dwk'][0], c['dwv'][0], m, 3,
+                                    W=16),
+                        M.hca_query(q, t, c['dk'][0], c['dv'][0], c['dwk'][0], c['dwv'][0], m, W=16)))
+        for x, y in zip(got[0], got[1]):
+            for u, v in zip(x, y):
+                assert np.array_equal(np.asarray(u), np.asarray(v)), t
+
+
 def test_visibility_rule():
     assert [I.n_visible(t, 4) for t in (0, 2, 3, 4, 7, 8)] == [0, 0, 1, 1, 2, 2]
     assert I.n_visible(1048575, 128) == 8192 and I.n_visible(1048575, 4) == 262144
