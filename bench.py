@@ -492,6 +492,78 @@ def prefill_main(a):
     print(json.dumps(rec), flush=True)
 
 
+# ------------------------------------------------------- several tokens per sequence ----
+
+DRAFT_METRIC = 'decode query-tokens/s at 1M ctx with several tokens per sequence (CSA top-1024 + HCA)'
+
+
+def drafts_main(a):
+    """Tq tokens per sequence decoded together (for example draft tokens), B = 4, one CSA
+    and one HCA layer per step at 1M context; the new tokens' window rows are written by
+    csa_compress (m = 1) before the attention of each layer."""
+    import torch
+    import long_context_attention_compress_amd as v4
+    import synth
+    Tq, L = a.tokens, a.layers
+    dev = 'cuda'
+    print(f'[bench] building {L} layer caches (B={B}, context {T}, {Tq} tokens per sequence)', file=sys.stderr,
+          flush=True)
+    layers, inputs = build_layers(v4, synth, torch, L, a.seed)
+    z1 = torch.zeros(1, device=dev)
+    pos = torch.arange(T - Tq, T, dtype=torch.int64, device=dev)[None].repeat(B, 1)
+    iq_f = synth.gpu_normal(a.seed, 'drafts/iq', (B, Tq, HI, DI), outlier_frac=0.01)
+    iq_store = v4.IKStore.empty(1, B * Tq * HI, DI)
+    v4.csa_compress(torch.zeros(1, B * Tq * HI, device=dev), z1, 0, raw_ik=iq_f.reshape(1, -1, DI), ik_out=iq_store)
+    iq = iq_store.e2m1.reshape(B, Tq, HI, DI // 2)
+    iqs = iq_store.e8m0.reshape(B, Tq, HI, DI // 32)
+    w = synth.gpu_uniform(a.seed, 'drafts/w', (B, Tq, HI))
+    q_csa = synth.gpu_normal(a.seed, 'drafts/qc', (B, Tq, H, D), outlier_frac=0.01, dtype=torch.bfloat16)
+    q_hca = synth.gpu_normal(a.seed, 'drafts/qh', (B, Tq, H, D), dtype=torch.bfloat16)
+    nk = synth.gpu_normal(a.seed, 'drafts/k', (B, Tq, D), dtype=torch.bfloat16)
+    nv = synth.gpu_normal(a.seed, 'drafts/v', (B, Tq, D), dtype=torch.bfloat16)
+    gz = torch.zeros(B, Tq, device=dev)
+    idx = torch.zeros(B, Tq, K, dtype=torch.int32, device=dev)
+    o1 = torch.zeros(B, Tq, H, D, device=dev)
+    o2 = torch.zeros(B, Tq, H, D, device=dev)
+    ws_i, ws_a = v4.Workspace(), v4.Workspace()
+    calls = []
+    for Ld in layers:
+        calls.append([
+            v4.csa_compress(gz, z1, T - Tq, nk, nv, Ld['cwk'], Ld['cwv'], prepare=True),
+            v4.lightning_index_topk(pos, iq, w, Ld['ik'], K, M_CSA, iq_scale=iqs, out_idx=idx, workspace=ws_i,
+                                    prepare=True),
+            v4.sparse_window_attn(q_csa, pos, Ld['ek'], Ld['ev'], M_CSA, Ld['cwk'], Ld['cwv'], W, idx, o=o1,
+                                  workspace=ws_a, prepare=True),
+            v4.csa_compress(gz, z1, T - Tq, nk, nv, Ld['hwk'], Ld['hwv'], prepare=True),
+            v4.hca_attn(q_hca, pos, Ld['hk'], Ld['hv'], M_HCA, Ld['hwk'], Ld['hwv'], W, o=o2, workspace=ws_a,
+                        prepare=True)])
+    run = lambda i: [f() for f in calls[i % L]]
+    for i in range(a.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    cyc = sleep_cycles_per_ms(torch)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda._sleep(int(max(20.0, 0.2 * a.steps) * cyc))   # park the stream while the steps are enqueued
+    ev[0].record()
+    for i in range(a.steps):
+        run(a.warmup + i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / a.steps
+    rec = {
+        'metric': DRAFT_METRIC, 'value': round(B * Tq / (ms * 1e-3), 1), 'unit': 'query-tokens/s', 'n_gpus': 1,
+        'steps': a.steps, 'warmup': a.warmup, 'ms_per_step': round(ms, 6), 'higher_is_better': True,
+        'scaling': 'weak', 'vs_baseline': None, 'dtype': 'mxfp4+e4m3/bf16', 'data': 'synthetic',
+        'config': {'workload': f'{Tq} tokens per sequence decoded together at 1,048,576-token context, batch 4: '
+                               'window rows of the new tokens (csa_compress, m=1), then one CSA layer (m=4, 262,144 '
+                               'entries, top-1024) and one HCA layer (m=128, 8,192 entries) per step',
+                   'batch': B, 'context': T, 'tokens_per_sequence': Tq, 'layers_rotated': L,
+                   'parallelism': 'single GPU'},
+        'roofline': None,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 # ---------------------------------------------------------------- layer stack ----
 
 STACK_LAYERS = 43  # 2 window-only, then CSA and HCA alternating (21 + 20)
@@ -622,7 +694,8 @@ def main():
     ap.add_argument('--layers', type=int, default=16)
     ap.add_argument('--seed', type=int, default=7)
     ap.add_argument('--no-cpu-baseline', action='store_true')
-    ap.add_argument('--workload', choices=('decode', 'prefill', 'stack'), default='decode')
+    ap.add_argument('--workload', choices=('decode', 'prefill', 'stack', 'drafts'), default='decode')
+    ap.add_argument('--tokens', type=int, default=4, help='tokens per sequence (--workload drafts)')
     ap.add_argument('--stack-layers', type=int, default=STACK_LAYERS)
     a = ap.parse_args()
     if a.gpus != 1:
@@ -634,6 +707,8 @@ def main():
         return prefill_main(a)
     if a.workload == 'stack':
         return stack_main(a)
+    if a.workload == 'drafts':
+        return drafts_main(a)
     import torch
     import long_context_attention_compress_amd as v4
     import synth
