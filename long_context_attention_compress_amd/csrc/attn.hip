@@ -814,20 +814,22 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
 // -------------------------------------------------------------- combine ----
 
 constexpr int MAX_SPLIT = 1024;
-constexpr int CMB_G = 4;                 // threads sharing one output dim
-constexpr int CMB_T = CMB_G * 192;       // combine workgroup (dims up to 192)
+constexpr int CMB_G = 4;                 // threads sharing one output dim (few query-head pairs)
+constexpr int CMB_MANY = 1024;           // query-head pairs from which one thread per dim is used
 constexpr int CMB_CHUNK = 32;            // splits a combine thread loads at once
 
-// Merge the splits of one (query, head). CMB_G threads share output dim d:
-// thread group gi takes splits gi, gi + CMB_G, ...; every partial output a
+// Merge the splits of one (query, head). G threads share output dim d:
+// thread group gi takes splits gi, gi + G, ...; every partial output a
 // thread needs (up to CMB_CHUNK) is loaded before the split weights are known,
 // so one memory round trip covers the partials and the (max, sum) pairs. The
 // groups' sums are added in a fixed order (deterministic).
-template <int OUT_BF16>
-__global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
+template <int OUT_BF16, int G>
+__global__ __launch_bounds__(G * 192) void attn_combine_kernel(AttnPlan p) {
+    constexpr int CMB_T = G * 192;
+    constexpr int NK = (MAX_SPLIT + CMB_T - 1) / CMB_T;  // (max, sum) pairs a thread loads
     __shared__ float wgt[MAX_SPLIT];
     __shared__ float red[2][CMB_T / 64];
-    __shared__ float part[CMB_G - 1][192];
+    __shared__ float part[G > 1 ? G - 1 : 1][192];
     const int q = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int D = p.D, H = p.H, S = p.n_split;
@@ -839,13 +841,13 @@ __global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
     float v[CMB_CHUNK];
 #pragma unroll
     for (int i = 0; i < CMB_CHUNK; ++i) {
-        const int sp = gi + CMB_G * i;
+        const int sp = gi + G * i;
         v[i] = (own && sp < S) ? po[(size_t)sp * stride] : 0.f;
     }
-    float2 ml[2];
+    float2 ml[NK];
     float mloc = -__builtin_inff();
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
         const int sp = tid + CMB_T * k;
         ml[k] = sp < S ? *(const float2 *)&p.part_ml[((base + (size_t)sp * H) + h) * 2]
                        : make_float2(-__builtin_inff(), 0.f);
@@ -859,7 +861,7 @@ __global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
     for (int w = 1; w < CMB_T / 64; ++w) M = __builtin_fmaxf(M, red[0][w]);
     float lloc = 0.f;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < NK; ++k) {
         const int sp = tid + CMB_T * k;
         if (sp < S) {
             const float w = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
@@ -876,18 +878,18 @@ __global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < CMB_CHUNK; ++i) {
-        const int sp = gi + CMB_G * i;
+        const int sp = gi + G * i;
         if (sp < S) acc += v[i] * wgt[sp];
     }
-    for (int s0 = CMB_G * CMB_CHUNK; s0 < S; s0 += CMB_G * CMB_CHUNK) {  // more than 128 splits
+    for (int s0 = G * CMB_CHUNK; s0 < S; s0 += G * CMB_CHUNK) {  // more than 128 splits
 #pragma unroll
         for (int i = 0; i < CMB_CHUNK; ++i) {
-            const int sp = s0 + gi + CMB_G * i;
+            const int sp = s0 + gi + G * i;
             v[i] = (own && sp < S) ? po[(size_t)sp * stride] : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < CMB_CHUNK; ++i) {
-            const int sp = s0 + gi + CMB_G * i;
+            const int sp = s0 + gi + G * i;
             if (sp < S) acc += v[i] * wgt[sp];
         }
     }
@@ -895,7 +897,7 @@ __global__ __launch_bounds__(CMB_T) void attn_combine_kernel(AttnPlan p) {
     __syncthreads();
     if (gi == 0 && own) {
 #pragma unroll
-        for (int k = 0; k < CMB_G - 1; ++k) acc += part[k][d];
+        for (int k = 0; k < G - 1; ++k) acc += part[k][d];
         const float o = L > 0.f ? acc / L : 0.f;
         if (OUT_BF16) ((__bf16 *)p.o)[((size_t)q * H + h) * D + d] = (__bf16)o;
         else ((float *)p.o)[((size_t)q * H + h) * D + d] = o;
@@ -936,8 +938,16 @@ hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
-    if (p.o_bf16) hipLaunchKernelGGL(attn_combine_kernel<1>, dim3(p.Q, p.H), dim3(CMB_T), 0, s, p);
-    else hipLaunchKernelGGL(attn_combine_kernel<0>, dim3(p.Q, p.H), dim3(CMB_T), 0, s, p);
+    // many query-head pairs (several tokens per sequence): one thread per output dim
+    // sums every split; few pairs (one decode token): CMB_G threads share a dim
+    const bool many = (int64_t)p.Q * p.H >= CMB_MANY;
+    if (p.o_bf16) {
+        if (many) hipLaunchKernelGGL((attn_combine_kernel<1, 1>), dim3(p.Q, p.H), dim3(192), 0, s, p);
+        else hipLaunchKernelGGL((attn_combine_kernel<1, CMB_G>), dim3(p.Q, p.H), dim3(CMB_G * 192), 0, s, p);
+    } else {
+        if (many) hipLaunchKernelGGL((attn_combine_kernel<0, 1>), dim3(p.Q, p.H), dim3(192), 0, s, p);
+        else hipLaunchKernelGGL((attn_combine_kernel<0, CMB_G>), dim3(p.Q, p.H), dim3(CMB_G * 192), 0, s, p);
+    }
     return hipGetLastError();
 }
 

@@ -379,6 +379,38 @@ def test_more_queries_than_one_launch_row():
         assert_close_rms(o[0, j], ro, TOL_BF16, f'o query {s}')
 
 
+def test_attn_many_query_head_pairs_combine():
+    """Four tokens per sequence, B = 4, 64 heads: 1,024 query-head pairs, where the split
+    partials are merged by one thread per output dimension; sparse and dense against the
+    oracle."""
+    B, Tq, rows, m, H, D, k = 4, 4, 1500, 4, 64, 192, 256
+    q_pos = np.array([[rows * m - 1 - i for i in range(Tq)]] * B, np.int64)
+    q_pos[2, 1] = 777
+    c = _attn_case(71, B, Tq, H, D, rows, q_pos, 'fp8')
+    ek, ev, wk, wv = _stores(c)
+    g = np.random.default_rng(72)
+    idx = np.full((B, Tq, k), -1, np.int32)
+    for b in range(B):
+        for i in range(Tq):
+            nv = min((int(q_pos[b, i]) + 1) // m, rows)
+            sel = np.sort(g.choice(nv, min(k, nv), replace=False))
+            idx[b, i, :len(sel)] = sel
+    print('combine with 1024 query-head pairs', flush=True)
+    for name in ('sparse', 'dense'):
+        if name == 'sparse':
+            o = v4.sparse_window_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'], dev(idx))
+        else:
+            o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'])
+        torch.cuda.synchronize()
+        o = o.float().cpu().numpy()
+        for b in range(B):
+            for i in range(Tq):
+                t = int(q_pos[b, i])
+                ids = idx[b, i][idx[b, i] >= 0] if name == 'sparse' else np.arange(min((t + 1) // m, rows))
+                ro, _ = _oracle_attn(c, b, i, ids)
+                assert_close_rms(o[b, i], ro, TOL_BF16, f'{name} b{b} i{i}')
+
+
 def test_attn_dense_two_streams():
     """A key list long enough (>= 4096 with the window) for the two-stream
     workgroups, with queries that see all entries, part of them, and almost
