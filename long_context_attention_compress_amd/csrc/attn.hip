@@ -815,7 +815,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
 
 constexpr int MAX_SPLIT = 1024;
 constexpr int CMB_G = 4;                 // threads sharing one output dim (few query-head pairs)
-constexpr int CMB_MANY = 1024;           // query-head pairs from which one thread per dim is used
+constexpr int CMB_MANY = 512;            // query-head pairs from which one thread per dim is used
 constexpr int CMB_CHUNK = 32;            // splits a combine thread loads at once
 
 // Merge the splits of one (query, head). G threads share output dim d:

@@ -380,7 +380,7 @@ def test_more_queries_than_one_launch_row():
 
 
 def test_attn_many_query_head_pairs_combine():
-    """Four tokens per sequence, B = 4, 64 heads: 1,024 query-head pairs, where the split
+    """Four tokens per sequence, B = 4, 64 heads: 1,024 query-head pairs (at least 512), where the split
     partials are merged by one thread per output dimension; sparse and dense against the
     oracle."""
     B, Tq, rows, m, H, D, k = 4, 4, 1500, 4, 64, 192, 256
