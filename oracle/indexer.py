@@ -14,6 +14,12 @@ compressed entry,
 
     I_{t,e} = sum_h w_{t,h} * max(0, q_{t,h} . u_e).
 
+Non-finite values: max(0, x) is the IEEE 754-2019 maximum operation, which
+propagates NaN (as numpy's maximum and torch's relu do): a NaN dot product of
+any head makes the entry's score NaN. The pages say nothing about non-finite
+inputs; propagation is the plain arithmetic reading, so nothing is dropped
+silently.
+
 Selection: among the entries visible to t (entry e covers positions
 [e*m, e*m+m) and is visible when e*m + m - 1 <= t), keep the min(k, n_vis) with
 the largest score; equal scores go to the lower entry index. Scores are
@@ -22,7 +28,9 @@ compared as float32 values (the precision the kernel decides in); -0 equals
 and padded with -1 to length k.
 
 Parity: pinned in tests against a pure-Python double loop, exact rational dot
-products of MXFP4 operands, and a stable brute-force argsort.
+products of MXFP4 operands, hand-derived selections with NaN key blocks and
+NaN query heads, and a stable brute-force sort (ties, -0, NaN) for both the
+selection and the k-th score.
 """
 
 import numpy as np
@@ -38,8 +46,8 @@ def index_scores(iq, w, keys):
     iq = np.asarray(iq, np.float64)
     keys = np.asarray(keys, np.float64)
     dots = keys @ iq.T                           # [N, H]
-    # max(0, x) as IEEE maxNum: a NaN dot product counts as 0
-    return np.fmax(dots, 0.0) @ np.asarray(w, np.float32).astype(np.float64)
+    # max(0, x) propagating NaN (IEEE 754-2019 maximum)
+    return np.maximum(dots, 0.0) @ np.asarray(w, np.float32).astype(np.float64)
 
 
 def topk_select(scores, n_vis, k):
@@ -56,7 +64,11 @@ def topk_select(scores, n_vis, k):
 
 
 def kth_score(scores, n_vis, k):
-    """float32 value of the k-th best visible score (the boundary of the tie band)."""
+    """float32 value of the k-th best visible score (the boundary of the tie band).
+
+    The score of the min(k, n_vis)-th entry in selection order. NaN ranks below
+    every number, so when that entry's score is NaN the boundary is -inf.
+    """
     s = np.asarray(scores, np.float64)[:n_vis].astype(np.float32).astype(np.float64)
     s = np.where(np.isnan(s), -np.inf, s)
     if n_vis == 0:

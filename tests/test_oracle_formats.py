@@ -163,3 +163,25 @@ def test_fp8_row_quantize_error_bound():
     big = np.argmax(np.abs(nope), 1)
     assert np.all((codes[np.arange(300), big] & 0x7F)[amax > 0] == 0x7E)
     assert np.array_equal(deq[:, 128:], torch.from_numpy(x[:, 128:]).to(torch.bfloat16).double().numpy())
+
+
+def test_fp8_row_scale_nan_group_propagates():
+    """A NaN anywhere in a 128-dim group makes the group's scale NaN and every code of the
+    group the E4M3 NaN code 0x7F (x / NaN is NaN); another group and the BF16 RoPE dims
+    are unaffected. An infinite element makes the scale infinite: its own code is NaN
+    (inf / inf) and every finite element of the group becomes a zero code."""
+    x = np.zeros((3, 192), np.float32)
+    x[:, :128] = np.linspace(-2, 2, 128, dtype=np.float32)
+    x[:, 128:] = 0.75
+    x[1, 17] = np.nan
+    x[2, 5] = np.inf
+    assert np.isnan(F.fp8_row_scale(np.array([np.nan], np.float32)))[0]
+    assert F.fp8_row_scale(np.array([0.0], np.float32))[0] == 1.0
+    assert F.fp8_row_scale(np.array([448.0], np.float32))[0] == 1.0
+    codes, rope_bits, s = F.kv_quantize(x)
+    assert s[0, 0] == np.float32(2.0) / np.float32(448.0)
+    assert np.isnan(s[1, 0]) and np.all(codes[1] == 0x7F)
+    assert np.isinf(s[2, 0]) and codes[2, 5] == 0x7F
+    assert np.all((codes[2, np.arange(128) != 5] & 0x7F) == 0)
+    assert np.array_equal(codes[0], F.e4m3_encode(x[0, :128] / s[0, 0]))
+    assert np.all(F.bf16_decode(rope_bits) == 0.75)

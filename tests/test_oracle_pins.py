@@ -196,6 +196,104 @@ def test_topk_nan_ranks_last():
     assert list(I.topk_select(s, 5, 4)) == [0, 2, 3, 4]
 
 
+def _mx_keys_with_dots(dots_h0, dots_h1):
+    """Queries and MXFP4 keys (32 dims, one block each) whose dot products with the two
+    query heads are the given small integers: head 0 reads dim 0, head 1 reads dim 1."""
+    n = len(dots_h0)
+    iq = np.zeros((2, 32), np.float32)
+    iq[0, 0] = 1.0
+    iq[1, 1] = 1.0
+    keys = np.zeros((n, 32), np.float32)
+    keys[:, 0] = dots_h0
+    keys[:, 1] = dots_h1
+    keys[:, 2] = 4.0                      # keeps every block's scale at 2^0 (amax 4 -> E = 0)
+    return iq, keys
+
+
+def test_index_scores_nan_key_block_propagates():
+    """A key whose MXFP4 block scale is NaN (E8M0 0xFF) decodes to NaN, so every dot
+    product with it is NaN and, with max(0, x) propagating NaN, so is its score: it
+    ranks below every number. Hand-derived: w = (1, 1), dots (h0, h1) per key
+    0: (3, 0), 1: (1, 1), 2: (0, 6) with a NaN block, 3: (2, 2), 4: (-1, 0), 5: (0, 2).
+    Scores 3, 2, NaN, 4, 0, 2 -> top-3 = {0, 3} plus the lower of the tied 1 and 5 = {0, 1, 3}.
+    Under the other reading (a NaN dot product counted as 0) key 2 would score 6 and be
+    selected instead of key 1."""
+    iq, keys = _mx_keys_with_dots([3, 1, 0, 2, -1, 0], [0, 1, 6, 2, 0, 2])
+    packed, sc = F.mxfp4_quantize(keys)
+    assert np.all(sc == 127)
+    sc = sc.copy()
+    sc[2, 0] = 0xFF
+    dk = F.mxfp4_dequantize(packed, sc)
+    assert np.isnan(dk[2]).all() and np.isfinite(np.delete(dk, 2, 0)).all()
+    ip, isc = F.mxfp4_quantize(iq)
+    s = I.index_scores(F.mxfp4_dequantize(ip, isc), np.ones(2, np.float32), dk)
+    assert np.isnan(s[2]) and list(s[[0, 1, 3, 4, 5]]) == [3.0, 2.0, 4.0, 0.0, 2.0]
+    assert list(I.topk_select(s, 6, 3)) == [0, 1, 3]
+    assert list(I.topk_select(s, 6, 6)) == [0, 1, 2, 3, 4, 5]
+    assert I.kth_score(s, 6, 3) == 2.0 and I.kth_score(s, 6, 6) == -np.inf
+
+
+def test_index_scores_nan_query_head_propagates():
+    """A NaN block in one query head makes that head's dot product NaN for every key,
+    so every score is NaN (even where the head's weight is 0: 0 * NaN = NaN) and the
+    selection is the k lowest ids. Hand-derived, same keys as above: top-3 = {0, 1, 2}."""
+    iq, keys = _mx_keys_with_dots([3, 1, 0, 2, -1, 0], [0, 1, 6, 2, 0, 2])
+    packed, sc = F.mxfp4_quantize(keys)
+    ip, isc = F.mxfp4_quantize(iq)
+    isc = isc.copy()
+    isc[1, 0] = 0xFF
+    for w in (np.ones(2, np.float32), np.array([1.0, 0.0], np.float32)):
+        s = I.index_scores(F.mxfp4_dequantize(ip, isc), w, F.mxfp4_dequantize(packed, sc))
+        assert np.isnan(s).all()
+        assert list(I.topk_select(s, 6, 3)) == [0, 1, 2]
+        assert I.kth_score(s, 6, 3) == -np.inf
+
+
+def test_index_scores_negative_and_zero_dots():
+    """max(0, x) clamps negative dot products and -0 to +0 (no NaN involved): one head
+    with dots -5, -0.0, 7 and weight 2 gives scores 0, 0, 14."""
+    iq = np.array([[1.0, 0.0]])
+    keys = np.array([[-5.0, 1.0], [-0.0, 3.0], [7.0, -2.0]])
+    s = I.index_scores(iq, np.array([2.0], np.float32), keys)
+    assert list(s) == [0.0, 0.0, 14.0] and not np.signbit(s[1])
+
+
+def _kth_brute(scores, n_vis, k):
+    """k-th score by a plain sort of (rank class, value, id), NaN in the lowest class."""
+    vals = [float(np.float32(x)) for x in scores[:n_vis]]
+    order = sorted(range(n_vis), key=lambda e: (math.isnan(vals[e]), -(0.0 if math.isnan(vals[e]) else vals[e]), e))
+    v = vals[order[min(k, n_vis) - 1]]
+    return -math.inf if math.isnan(v) else v
+
+
+def test_kth_score_brute_force_ties_zero_nan():
+    g = np.random.default_rng(31)
+    for trial in range(200):
+        n = int(g.integers(1, 60))
+        k = int(g.integers(1, 70))
+        s = np.round(g.standard_normal(n + 3) * 2) / 2          # many exact ties
+        s[g.random(n + 3) < 0.15] = np.nan
+        s[g.random(n + 3) < 0.1] = -0.0
+        s[g.random(n + 3) < 0.1] = 0.0
+        if trial % 5 == 0:
+            s[:n] = np.nan
+        got, ref = I.kth_score(s, n, k), _kth_brute(s, n, k)
+        assert got == ref, (trial, got, ref)
+        # every selected id scores at or above the k-th score, every other visible one at or below
+        sel = I.topk_select(s, n, k)
+        sel = sel[sel >= 0]
+        key = lambda e: -math.inf if math.isnan(s[e]) else float(np.float32(s[e]))
+        assert all(key(e) >= got for e in sel)
+        assert all(key(e) <= got for e in set(range(n)) - set(sel.tolist()))
+    # hand-checked: ties straddling the boundary, -0 equal to +0, scores rounded to float32
+    assert I.kth_score(np.array([1.0, 2.0, 2.0, 2.0, 0.5]), 5, 2) == 2.0
+    assert I.kth_score(np.array([-0.0, 0.0, -1.0]), 3, 2) == 0.0
+    assert I.kth_score(np.array([1.0 + 1e-12, 1.0, 3.0]), 3, 3) == 1.0
+    assert I.kth_score(np.array([np.nan, 5.0, np.nan]), 3, 1) == 5.0
+    assert I.kth_score(np.array([np.nan, 5.0, np.nan]), 3, 2) == -np.inf
+    assert I.kth_score(np.array([4.0, 9.0]), 1, 5) == 4.0          # fewer visible than k
+
+
 # ------------------------------------------------------------- attention ----
 
 def _sdpa(q, K, V, scale, mask=None):
