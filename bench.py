@@ -277,6 +277,17 @@ def timed(torch, calls, L, first, steps, instrument, cyc_per_ms):
 CPU_SAMPLE_S = 10.0  # seconds of oracle work per run
 
 
+def cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        for line in open('/proc/cpuinfo'):
+            if line.startswith('model name'):
+                return line.split(':', 1)[1].strip()
+    except OSError:
+        pass
+    return 'unknown'
+
+
 def cpu_baseline(seed):
     """The oracle timed on a bounded sample of the same workload: query tokens of batch
     element 0 (each with its own query, indexer query and weights) through the CSA layer and
@@ -317,7 +328,7 @@ def cpu_baseline(seed):
         t_hca += t2 - t1
         n += 1
     return {'value': round(n / (t_csa + t_hca), 4), 'unit': 'query-tokens/s', 'cores': int(threads),
-            'kind': 'oracle',
+            'cpu_model': cpu_model(), 'kind': 'oracle',
             'sample': (f'{n} query tokens of batch element 0 at 1M context, each through the CSA layer '
                        f'(score {N_CSA} MXFP4 keys, top-{K}, attend {K}+{W} keys; {t_csa:.1f} s in all) and the '
                        f'HCA layer (attend {N_HCA}+{W} keys; {t_hca:.1f} s); float64 numpy; decoding of the '
@@ -439,7 +450,7 @@ def cpu_baseline_prefill(seed):
         n += 1
     per_token_s = el / (2 * n)            # one layer
     return {'value': round(1.0 / (per_token_s * len(PF_LAYERS)), 4), 'unit': 'tokens/s', 'cores': int(threads),
-            'kind': 'oracle',
+            'cpu_model': cpu_model(), 'kind': 'oracle',
             'sample': (f'{n} new tokens, each through one CSA layer (score up to {n_csa} MXFP4 keys, top-{K}, '
                        f'attend {K}+{W} keys) and one HCA layer (attend up to {n_hca}+{W} keys), {el:.1f} s; '
                        f'scaled to the four layers of a pass; float64 numpy; the new chunk\'s compression and '

@@ -142,7 +142,8 @@ typedef struct {
  *   U = sum_r alpha_r * raw_ik[b][j*m + r]
  * computed in float64, rounded to float32, then encoded into the stores at
  * entry pos0/m + j. E4M3_BF16 stores: scale = amax/448 per 128 no-RoPE dims
- * (1 when amax = 0), code = E4M3(x/scale) rounded to nearest even with
+ * (1 when amax = 0; NaN when the group holds a NaN, which then makes every
+ * code of the group NaN), code = E4M3(x/scale) rounded to nearest even with
  * saturation to +-448 (NaN -> 0x7F); RoPE dims rounded to BF16. MXFP4 keys:
  * OCP MX v1.0 scale rule, E = floor(log2 amax) - 2 clamped to [-127, 127],
  * elements rounded to nearest even E2M1 with saturation to +-6; a block with a
@@ -196,7 +197,9 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream);
  * Query (b, i) at position t = q_pos[b][i] sees entries e < min(rows,
  * (t+1)/m). Score (float32):
  *   I_e = sum_h w[b][i][h] * max(0, iq[b][i][h] . key_e)
- * The selection is the min(k, n_visible) entries with the largest score,
+ * max(0, x) propagates NaN (IEEE 754-2019 maximum): a NaN dot product, for
+ * example from an E8M0 NaN scale (0xFF) in a key or a query head, makes I_e
+ * NaN. The selection is the min(k, n_visible) entries with the largest score,
  * equal scores going to the lower entry id (-0 equals +0; NaN ranks lowest).
  * out_idx[b][i][0..k) receives the selected ids in ascending order, padded
  * with -1. out_score (optional) receives the matching scores (0 for padding).
@@ -241,7 +244,8 @@ int lightning_index_topk(const v4a_index_args *a, void *workspace, size_t worksp
  *  q         [B][Tq][H_q][dim] in q_fmt (pre-RoPE).
  *  ent_k/v   entry stores (ring = 0); may be NULL for window-only use.
  *  m         compression ratio of the entries (visibility rule above).
- *  win_k/v   raw window rows, indexed by position (usually a ring).
+ *  win_k/v   raw window rows, indexed by position (usually a ring; a ring
+ *            needs at least W slots, else V4A_EINVAL).
  *  W         window length (0 .. 4096).
  *  sm_scale  logit scale; 0 means 1/sqrt(dim).
  *  o         [B][Tq][H_q][dim] in o_fmt.
@@ -257,6 +261,8 @@ int lightning_index_topk(const v4a_index_args *a, void *workspace, size_t worksp
  *          [chaosnode.de, "DeepSeek-V4: 1 Million Token Context endlich
  *          nutzbar", section "Hybrid Attention: CSA und HCA"]: the window
  *          of the last 128 raw tokens includes the current one.
+ * Key lists (entries + window) of up to 2,097,152 keys per query (1024 splits
+ * of 2048 keys); a longer one returns V4A_EINVAL and its *_workspace() 0.
  * Supported: all stores F32 with q and o float32, dim 128, H_q * dim <= 4096;
  * or all stores E4M3_BF16 with dim == 192, q bfloat16, o float32 or bfloat16,
  * and H_q in {16, 32, 48, 64}. (A bfloat16 output carries its own rounding of

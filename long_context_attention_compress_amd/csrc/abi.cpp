@@ -179,14 +179,19 @@ constexpr int WG_TARGET = 512;  // about two resident workgroups per compute uni
 constexpr int WG_TARGET_NS2 = 256;  // two-stream workgroups: one per compute unit
 constexpr int64_t NS2_MIN_KEYS = 4096;  // key lists at least this long take two streams
 
+constexpr int MAX_SPLITS = 1024;  // splits per query the combine kernel merges
+// Longest key list (entries + window) one query may have: every split resolves
+// its keys' store rows into LDS first, at most KS_MAX of them.
+constexpr int64_t MAX_KEY_LIST = (int64_t)MAX_SPLITS * KS_MAX;
+
 struct AttnLayout {
     int n_split, keys_per_split, n_streams;
     size_t off_ml, total;
 };
 
-AttnLayout attn_layout(const v4a_attn_args *a, bool sparse, int k, int64_t n_override) {
-    AttnLayout L;
-    const int64_t Q = (int64_t)a->B * a->Tq;
+// Upper bound of a query's key list: the sparse list, or every entry of the
+// store (capped by the override), plus the window.
+int64_t key_list_cap(const v4a_attn_args *a, bool sparse, int k, int64_t n_override) {
     int64_t n_list = 0;
     if (a->ent_k) {
         if (sparse) n_list = k;
@@ -195,7 +200,21 @@ AttnLayout attn_layout(const v4a_attn_args *a, bool sparse, int k, int64_t n_ove
             if (n_override >= 0) n_list = std::min(n_list, n_override);
         }
     }
-    const int64_t cap = n_list + a->W;
+    return n_list + a->W;
+}
+
+int check_key_list(const v4a_attn_args *a, bool sparse, int k, int64_t n_override) {
+    const int64_t cap = key_list_cap(a, sparse, k, n_override);
+    if (cap > MAX_KEY_LIST)
+        return fail(V4A_EINVAL, "a key list of up to %lld keys exceeds the supported %lld (%d splits of %d keys)",
+                    (long long)cap, (long long)MAX_KEY_LIST, MAX_SPLITS, KS_MAX);
+    return V4A_OK;
+}
+
+AttnLayout attn_layout(const v4a_attn_args *a, bool sparse, int k, int64_t n_override) {
+    AttnLayout L;
+    const int64_t Q = (int64_t)a->B * a->Tq;
+    const int64_t cap = key_list_cap(a, sparse, k, n_override);
     // Long key lists (FP8 path) run two key streams per workgroup, one
     // workgroup per compute unit; short ones one stream, about two per unit.
     const bool fp8 = a->win_k && a->win_k->fmt == V4A_KV_E4M3_BF16;
@@ -205,7 +224,7 @@ AttnLayout attn_layout(const v4a_attn_args *a, bool sparse, int k, int64_t n_ove
     // one tile per stream, and no split longer than KS_MAX keys
     int64_t n_split = std::min((cap + KS_MIN * L.n_streams - 1) / (KS_MIN * L.n_streams), (target + Q - 1) / Q);
     n_split = std::max<int64_t>(n_split, (cap + KS_MAX - 1) / KS_MAX);
-    n_split = std::max<int64_t>(1, std::min<int64_t>(n_split, 1024));
+    n_split = std::max<int64_t>(1, std::min<int64_t>(n_split, MAX_SPLITS));
     int64_t ks = (cap + n_split - 1) / n_split;
     ks = std::max<int64_t>(KS_MIN, (ks + 31) / 32 * 32);
     n_split = std::max<int64_t>(1, (cap + ks - 1) / ks);
@@ -240,6 +259,10 @@ int check_attn(const v4a_attn_args *a, AttnPlan *P) {
         if (s && (s->fmt != fmt || s->dim != a->dim)) return fail(V4A_EFORMAT, "all stores must share format and dim");
     if (a->win_v->rows < a->win_k->rows || a->win_v->ring != a->win_k->ring)
         return fail(V4A_EINVAL, "win_k and win_v must have the same rows and ring");
+    // a ring shorter than the window would map two window positions to one slot
+    if (a->win_k->ring > 0 && a->win_k->ring < a->W)
+        return fail(V4A_EINVAL, "a window ring of %lld slots cannot hold a window of %d positions",
+                    (long long)a->win_k->ring, a->W);
     if (a->ent_k && a->ent_v->rows < a->ent_k->rows) return fail(V4A_EINVAL, "ent_v has fewer rows than ent_k");
     if (fmt == V4A_KV_F32) {
         if (a->dim > 128) return fail(V4A_EFORMAT, "the fp32 path supports dim <= 128");
@@ -419,7 +442,7 @@ int lightning_index_topk(const v4a_index_args *a, void *ws, size_t ws_bytes, v4a
 
 size_t sparse_window_attn_workspace(const v4a_attn_args *a, int32_t k) {
     AttnPlan P;
-    if (check_attn(a, &P) || k < 1) return 0;
+    if (check_attn(a, &P) || k < 1 || k > 65536 || check_key_list(a, true, k, -1)) return 0;
     return attn_layout(a, true, k, -1).total;
 }
 
@@ -432,6 +455,7 @@ int sparse_window_attn(const v4a_attn_args *a, const int32_t *idx, int32_t k, vo
     if (k < 1 || k > 65536) return fail(V4A_EINVAL, "k must be in 1..65536");
     if (!idx) return fail(V4A_ENULL, "topk_idx is NULL");
     if (!aligned(idx, 4)) return fail(V4A_EALIGN, "topk_idx misaligned");
+    if ((r = check_key_list(a, true, k, -1))) return r;
     P.sparse = 1;
     P.k = k;
     P.idx = idx;
@@ -444,7 +468,7 @@ int sparse_window_attn(const v4a_attn_args *a, const int32_t *idx, int32_t k, vo
 
 size_t hca_attn_workspace(const v4a_attn_args *a, int64_t n_override) {
     AttnPlan P;
-    if (check_attn(a, &P)) return 0;
+    if (check_attn(a, &P) || check_key_list(a, false, 0, n_override)) return 0;
     return attn_layout(a, false, 0, n_override).total;
 }
 
@@ -452,6 +476,7 @@ int hca_attn(const v4a_attn_args *a, int64_t n_override, void *ws, size_t ws_byt
     AttnPlan P;
     int r = check_attn(a, &P);
     if (r) return r;
+    if ((r = check_key_list(a, false, 0, n_override))) return r;
     P.sparse = 0;
     P.k = 0;
     P.idx = nullptr;

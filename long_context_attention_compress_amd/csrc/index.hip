@@ -126,13 +126,16 @@ __device__ __forceinline__ float scatter_rows(const float (&x)[4]) {
 }
 
 
+// max(0, d) propagating NaN (the IEEE 754-2019 maximum): a NaN dot product
+// makes the entry's score NaN, which ranks below every number.
+__device__ __forceinline__ float relu_nan(float d) { return (d > 0.0f || d != d) ? d : 0.0f; }
+
 // sum_h w_h max(0, d_h) over this lane's heads, as an fma chain. The exact
-// form takes max(0, d) with fmaxf semantics (a NaN d counts as 0), which the
-// compiler implements with a canonicalisation per value. The fast form takes
-// the max of the bit patterns as signed integers: one instruction, equal to
-// the exact form for every d that is not NaN (a negative value or -0 gives
-// +0, and +0 or -0 added to a chain that starts at +0 leaves it unchanged);
-// the caller sends a tile to it only when the scale bytes rule out a NaN d.
+// form is relu_nan. The fast form takes the max of the bit patterns as signed
+// integers: one instruction, equal to the exact form for every d that is not
+// NaN (a negative value or -0 gives +0, and +0 or -0 added to a chain that
+// starts at +0 leaves it unchanged); the caller sends a tile to it only when
+// the scale bytes rule out a NaN d.
 template <int NT, bool FAST>
 __device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const v4i &kv, uint32_t sB,
                                           const float (&wv)[4][4]) {
@@ -149,7 +152,7 @@ __device__ __forceinline__ float head_sum(const v8i (&A)[4], uint32_t sA, const 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float r = FAST ? __int_as_float(__builtin_elementwise_max(__float_as_int(acc[i][j]), 0))
-                                 : __builtin_fmaxf(acc[i][j], 0.0f);
+                                 : relu_nan(acc[i][j]);
             s = __builtin_fmaf(wv[i][j], r, s);
         }
     return s;
@@ -341,7 +344,7 @@ __device__ void score_chunk_f32(const IndexPlan &p, int q, int b, int64_t c0, in
         double s = 0.0;
 #pragma unroll
         for (int h = 0; h < F32_MAX_H; ++h)
-            if (h < H) s += (double)w[h] * __builtin_fmax(acc[h], 0.0);
+            if (h < H) s += (double)w[h] * ((acc[h] > 0.0 || acc[h] != acc[h]) ? acc[h] : 0.0);
         skey[r] = score_key((float)s);
     }
 }

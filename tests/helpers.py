@@ -9,7 +9,9 @@ Comparison rules:
   agree outside Band (members inside Band must still be visible ids);
 * cache codes: equal, except where the oracle's float32 value sits within a
   relative 1e-6 of the rounding boundary between the two codes (then they may
-  differ by one step).
+  differ by one step). This applies to E4M3 codes (value x / scale), E2M1 codes
+  (value x / 2^E) and BF16 RoPE dims (value x); FP8 row scales and E8M0 block
+  exponents must be equal.
 """
 
 import numpy as np
@@ -121,3 +123,59 @@ def assert_codes_e4m3(got, ref_codes, ref_vals, what=''):
     near = np.abs(v - mid) <= 1e-6 * np.maximum(np.abs(v), 1e-30)
     assert near.all(), f'{what}: {int((~near).sum())} codes differ away from a rounding boundary'
     return int(bad.sum())
+
+
+def _assert_boundary(got_vals, ref_vals, oracle_vals, what, kind):
+    """Where the decoded values differ, the oracle's value must lie within 1e-6 (relative)
+    of the midpoint between them (a rounding boundary)."""
+    bad = got_vals != ref_vals
+    bad &= ~(np.isnan(got_vals) & np.isnan(ref_vals))
+    if not bad.any():
+        return 0
+    a, b, v = got_vals[bad], ref_vals[bad], np.asarray(oracle_vals, np.float64)[bad]
+    mid = (a + b) / 2
+    near = np.abs(v - mid) <= 1e-6 * np.maximum(np.abs(v), 1e-30)
+    assert near.all(), (f'{what}: {int((~near).sum())} {kind} values differ away from a rounding boundary '
+                        f'(first: got {a[~near][:3]}, oracle code {b[~near][:3]}, value {v[~near][:3]})')
+    return int(bad.sum())
+
+
+def assert_bf16_bits(got, ref_bits, ref_vals, what=''):
+    """BF16 bit patterns equal except where the oracle's float32 value sits at a rounding boundary."""
+    return _assert_boundary(F.bf16_decode(np.asarray(got).view(np.uint16)), F.bf16_decode(ref_bits),
+                            ref_vals, what, 'BF16')
+
+
+def assert_kv_rows(g_nope, g_rope, g_scale, x32, what=''):
+    """Every plane of E4M3_BF16 rows written by the GPU against the oracle's encoding of its
+    float32 rows x32 [..., D]: scales equal, E4M3 codes and BF16 RoPE dims by the boundary rule.
+    Returns the number of boundary differences."""
+    x32 = np.asarray(x32, np.float32)
+    codes, rope_bits, scale = F.kv_quantize(x32)
+    g_scale = np.asarray(g_scale, np.float32).reshape(scale.shape)
+    same = (g_scale == scale) | (np.isnan(g_scale) & np.isnan(scale))
+    assert same.all(), f'{what}: {int((~same).sum())} FP8 row scales differ'
+    q = (x32[..., :codes.shape[-1]].reshape(scale.shape + (-1,)) / scale[..., None]).astype(np.float32)
+    n = assert_codes_e4m3(np.asarray(g_nope), codes, q.reshape(codes.shape), f'{what} E4M3')
+    n += assert_bf16_bits(np.asarray(g_rope), rope_bits, x32[..., codes.shape[-1]:], f'{what} RoPE')
+    return n
+
+
+def assert_ik_rows(g_e2m1, g_e8m0, u32, what=''):
+    """MXFP4 indexer-key rows: E8M0 exponents equal, E2M1 codes by the boundary rule."""
+    u32 = np.asarray(u32, np.float32)
+    packed, scales = F.mxfp4_quantize(u32)
+    assert np.array_equal(np.asarray(g_e8m0), scales), f'{what}: E8M0 exponents differ'
+    d = u32.shape[-1]
+    blk = u32.reshape(u32.shape[:-1] + (d // F.MX_BLOCK, F.MX_BLOCK)).astype(np.float64)
+    vals = (blk / F.e8m0_decode(scales)[..., None]).reshape(u32.shape)
+    return _assert_boundary(F.e2m1_decode(F.mxfp4_unpack(np.asarray(g_e2m1))), F.e2m1_decode(F.mxfp4_unpack(packed)),
+                            vals, f'{what} E2M1', 'E2M1')
+
+
+def kv_planes(store, b, rows):
+    """Host copies of the planes of batch element b, rows `rows`, of a device KVStore."""
+    r = torch.as_tensor(np.asarray(rows, np.int64), device=store.nope.device)
+    return (store.nope[b].index_select(0, r).cpu().numpy(),
+            store.rope[b].index_select(0, r).cpu().numpy().view(np.uint16),
+            store.scale[b].index_select(0, r).cpu().numpy())

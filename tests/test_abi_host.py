@@ -182,3 +182,43 @@ def test_attention_rejections():
     r, msg = _status('sparse_window_attn', args(**dict(app, Tq=3)), FAKE, 1024, FAKE, 1 << 30, None)
     assert r == _abi.V4A_EINVAL and 'Tq' in msg, (r, msg)
     assert lib.hca_attn_workspace(args(**app), -1) > 0
+
+
+def test_attention_key_list_and_ring_limits():
+    """A key list longer than the splits can resolve, and a window ring shorter than the
+    window, are rejected before any launch (and their workspace size is 0)."""
+    lib = _abi.load()
+    big = 1024 * 2048   # splits per query x keys a split resolves
+
+    def args(ek_rows=4096, ring=128, W=128):
+        a = _abi.AttnArgs()
+        ek, ev = _kv(rows=ek_rows), _kv(rows=ek_rows)
+        wk, wv = _kv(ring=ring, rows=max(ring, 128)), _kv(ring=ring, rows=max(ring, 128))
+        a._keep = (ek, ev, wk, wv)
+        a.B, a.Tq, a.H_q, a.dim = 1, 1, 64, 192
+        a.q_pos = a.q = a.o = FAKE
+        a.q_fmt = a.o_fmt = _abi.ACT_BF16
+        a.ent_k, a.ent_v, a.win_k, a.win_v = (ctypes.pointer(s) for s in (ek, ev, wk, wv))
+        a.m, a.W, a.sm_scale, a.rope_base = 1, W, 0.0, 1e4
+        return a
+
+    ok = args(ek_rows=big - 128)
+    assert lib.hca_attn_workspace(ctypes.byref(ok), -1) > 0
+    over = args(ek_rows=big - 127)
+    assert lib.hca_attn_workspace(ctypes.byref(over), -1) == 0
+    r, msg = _status('hca_attn', ctypes.byref(over), -1, FAKE, 1 << 40, None)
+    assert r == _abi.V4A_EINVAL and 'key list' in msg, (r, msg)
+    # capped by the override: accepted again
+    assert lib.hca_attn_workspace(ctypes.byref(over), 1000) > 0
+    # sparse: the list is k long
+    sp = args()
+    assert lib.sparse_window_attn_workspace(ctypes.byref(sp), 65536) > 0
+    r, _ = _status('sparse_window_attn', ctypes.byref(sp), FAKE, 65537, FAKE, 1 << 40, None)
+    assert r == _abi.V4A_EINVAL
+    # window ring: at least W slots
+    short = args(ring=100, W=128)
+    assert lib.hca_attn_workspace(ctypes.byref(short), -1) == 0
+    r, msg = _status('hca_attn', ctypes.byref(short), -1, FAKE, 1 << 30, None)
+    assert r == _abi.V4A_EINVAL and 'ring' in msg, (r, msg)
+    assert lib.hca_attn_workspace(ctypes.byref(args(ring=128, W=128)), -1) > 0
+    assert lib.hca_attn_workspace(ctypes.byref(args(ring=100, W=100)), -1) > 0

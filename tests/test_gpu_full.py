@@ -16,7 +16,9 @@ from oracle import compress as OC
 from oracle import formats as F
 from oracle import indexer as OI
 from oracle import model as OM
-from tests.helpers import TOL_BF16, TOL_F32, assert_close_rms, assert_topk, bf16_dev, dev
+from oracle import rope as OR
+from tests.helpers import (TOL_BF16, TOL_F32, assert_close_rms, assert_ik_rows, assert_kv_rows, assert_topk, bf16_dev,
+                           dev, kv_planes)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +58,26 @@ def _decode_check(x, cfg, k, idx, o, ik_deq, iq_deq, m, N, run_oracle_sel):
         else:
             assert_close_rms(run_oracle_sel(b, sel)[0], ro, TOL_BF16, f'o b{b} (oracle selection)')
     return swaps
+
+
+def _check_decode_caches(x, idx, ek, ev, wk, wv, t, W):
+    """Every plane of sampled entry rows (the selected ones, the first and last 16 and 64
+    random ones; entry-level rows are m = 1 entries, keys rotated at their row) and of
+    every window row (positions t - W + 1 .. t, the newest one written by the fused append
+    when the call had one) against the oracle's own encoding of the same floats."""
+    B, N = x['ent_k'].shape[:2]
+    g = np.random.default_rng(11)
+    wpos = np.arange(t - W + 1, t + 1)
+    for b in range(B):
+        sel = idx[b, 0][idx[b, 0] >= 0]
+        ids = np.unique(np.concatenate([sel, np.arange(16), np.arange(N - 16, N), g.choice(N, 64, replace=False)]))
+        kx = OR.apply(x['ent_k'][b, ids].astype(np.float64), ids).astype(np.float32)
+        n = assert_kv_rows(*kv_planes(ek, b, ids), kx, f'entry K b{b}')
+        n += assert_kv_rows(*kv_planes(ev, b, ids), x['ent_v'][b, ids], f'entry V b{b}')
+        wx = OR.apply(x['win_k'][b].astype(np.float64), wpos).astype(np.float32)
+        n += assert_kv_rows(*kv_planes(wk, b, wpos % W), wx, f'window K b{b}')
+        n += assert_kv_rows(*kv_planes(wv, b, wpos % W), x['win_v'][b], f'window V b{b}')
+        print(f'[planes] b{b}: {len(ids)} entry rows and {W} window rows, {n} boundary differences', flush=True)
 
 
 def _csa_decode(x, cfg, k, fused=False):
@@ -101,7 +123,9 @@ def _csa_decode(x, cfg, k, fused=False):
         return oo.cpu().numpy()[0]
 
     print('oracle', flush=True)
-    return _decode_check(x, cfg, k, idx.cpu().numpy(), o.cpu().numpy(), F.mxfp4_dequantize(packed, scales),
+    idx_h = idx.cpu().numpy()
+    _check_decode_caches(x, idx_h, ek, ev, wk, wv, t, W)
+    return _decode_check(x, cfg, k, idx_h, o.cpu().numpy(), F.mxfp4_dequantize(packed, scales),
                          F.mxfp4_dequantize(iqp, iqs), m, N, rerun)
 
 
@@ -121,8 +145,11 @@ def test_c3_csa_decode_1m():
 def test_c2_hca_decode_1m():
     """1M raw tokens per sequence compressed 128x on the GPU; HCA attention of the last position.
 
-    Compression: every entry of batch elements 0 and 3 and 256 sampled entries of the others
-    against the oracle's codes; attention: all 4 queries against the oracle's own compression.
+    Compression: every plane (E4M3 codes, FP8 scales, BF16 RoPE dims) of K and V, for every
+    entry of batch elements 0 and 3 (entries up to position 2^20 - 1) and 256 sampled entries
+    (plus the last 16) of the others, against the oracle's encoding of its own pooled rows;
+    every window row, the newest one written by the attention launch's fused append.
+    Attention: all 4 queries against the oracle's own compression.
     """
     cfg, xq = synth.c2_queries(2)
     B, T, D, m, W = cfg['B'], cfg['T'], cfg['D'], cfg['m'], cfg['W']
@@ -155,19 +182,25 @@ def test_c2_hca_decode_1m():
         print(f'oracle batch {b}', flush=True)
         r = raws[b]
         dk, dv = np.empty((N, D)), np.empty((N, D))
-        gk, gv = ek.nope[b].cpu().numpy(), ev.nope[b].cpu().numpy()
-        check = np.arange(N) if b in (0, B - 1) else np.sort(g.choice(N, 256, replace=False))
+        gk, gv = kv_planes(ek, b, np.arange(N)), kv_planes(ev, b, np.arange(N))
+        check = np.arange(N) if b in (0, B - 1) else np.unique(np.concatenate(
+            [g.choice(N, 256, replace=False), np.arange(N - 16, N)]))
         step = 8192 // 4     # compress in slices of 2,048 entries to bound memory
+        nb = 0
         for e0 in range(0, N, step):
             sl = slice(e0 * m, (e0 + step) * m)
             k32, v32, _ = OC.compress(r['raw_k'][:, sl], r['raw_v'][:, sl], r['gate'][:, sl], r['pos_bias'], e0 * m)
             kc, vc = F.kv_quantize(k32[0]), F.kv_quantize(v32[0])
             dk[e0:e0 + step], dv[e0:e0 + step] = F.kv_dequantize(*kc), F.kv_dequantize(*vc)
-            sel = check[(check >= e0) & (check < e0 + step)] - e0
-            assert np.array_equal(gk[e0 + sel], kc[0][sel]) or np.mean(gk[e0 + sel] != kc[0][sel]) < 1e-4
-            assert np.array_equal(gv[e0 + sel], vc[0][sel]) or np.mean(gv[e0 + sel] != vc[0][sel]) < 1e-4
+            sel = check[(check >= e0) & (check < e0 + step)]
+            nb += assert_kv_rows(*(pl[sel] for pl in gk), k32[0][sel - e0], f'K b{b} entries {e0}..')
+            nb += assert_kv_rows(*(pl[sel] for pl in gv), v32[0][sel - e0], f'V b{b} entries {e0}..')
         wk32, wv32, _ = OC.compress(r['raw_k'][:, T - W:], r['raw_v'][:, T - W:], np.zeros((1, W), np.float32),
                                     np.zeros(1, np.float32), T - W)
+        wslot = np.arange(T - W, T) % W
+        nb += assert_kv_rows(*kv_planes(wk, b, wslot), wk32[0], f'window K b{b}')
+        nb += assert_kv_rows(*kv_planes(wv, b, wslot), wv32[0], f'window V b{b}')
+        print(f'[planes] b{b}: {len(check)} entries and {W} window rows, {nb} boundary differences', flush=True)
         dwk = F.kv_dequantize(*F.kv_quantize(wk32[0]))
         dwv = F.kv_dequantize(*F.kv_quantize(wv32[0]))
         ro, _ = OM.hca_query(xq['q'][b, 0], T - 1, dk, dv, dwk, dwv, m, W, win_first=T - W)
@@ -212,13 +245,23 @@ def _c4_layer(layer):
     print('oracle', flush=True)
     caches = OM.build_caches(r['raw_k'], r['raw_v'], r['gate'], r['pos_bias'], 'e4m3_bf16',
                              raw_ik=r.get('raw_ik'), ik_fmt='mxfp4')
-    # the new chunk's compressed entries and window rows are part of the checked path
-    gk = ek.nope[0].cpu().numpy()
-    ck = caches['ent_k']['nope'][0]
-    new = slice(T0 // m, T // m)
-    assert np.mean(gk[new] != ck[new]) < 1e-4, 'new entries differ'
+    # the new chunk's compressed entries (every plane of K, V and the indexer key) and the
+    # window rows of the new tokens are part of the checked path
+    k32, v32, u32 = OC.compress(r['raw_k'][:, T0:], r['raw_v'][:, T0:], r['gate'][:, T0:], r['pos_bias'], T0,
+                                raw_ik=r['raw_ik'][:, T0:] if kind == 'csa' else None)
+    new = np.arange(T0 // m, T // m)
+    nb = assert_kv_rows(*kv_planes(ek, 0, new), k32[0], f'layer {layer} new K entries')
+    nb += assert_kv_rows(*kv_planes(ev, 0, new), v32[0], f'layer {layer} new V entries')
     if kind == 'csa':
-        assert np.mean(ik.e2m1[0].cpu().numpy()[new] != caches['ik']['e2m1'][0][new]) < 1e-4
+        nb += assert_ik_rows(ik.e2m1[0, T0 // m:].cpu().numpy(), ik.e8m0[0, T0 // m:].cpu().numpy(), u32[0],
+                             f'layer {layer} new indexer keys')
+    wk32, wv32, _ = OC.compress(r['raw_k'][:, T0 - W:], r['raw_v'][:, T0 - W:], np.zeros((1, T1 + W), np.float32),
+                                np.zeros(1, np.float32), T0 - W)
+    wslot = np.arange(T0 - W, T) % ring
+    nb += assert_kv_rows(*kv_planes(wk, 0, wslot), wk32[0], f'layer {layer} window K')
+    nb += assert_kv_rows(*kv_planes(wv, 0, wslot), wv32[0], f'layer {layer} window V')
+    print(f'[planes] layer {layer}: {len(new)} new entries, {T1 + W} window rows, {nb} boundary differences',
+          flush=True)
     g = np.random.default_rng(layer)
     sample = sorted({0, 1, 2, 3, 127, 128, T1 - 1, *g.choice(T1, 24, replace=False).tolist()})
     diq = F.mxfp4_dequantize(iqp, iqs) if kind == 'csa' else None

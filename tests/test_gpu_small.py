@@ -135,7 +135,7 @@ def _check_index(c, idx, score, dkeys, diq):
             kk = min(c['k'], n_vis)
             sel = idx[b, i, :kk]
             ref = s[sel].astype(np.float32)
-            assert np.allclose(score[b, i, :kk], ref, rtol=2e-6, atol=1e-30), f'scores b{b} i{i}'
+            assert np.allclose(score[b, i, :kk], ref, rtol=2e-6, atol=1e-30, equal_nan=True), f'scores b{b} i{i}'
             assert np.all(score[b, i, kk:] == 0)
 
 
@@ -158,8 +158,9 @@ def test_index_mxfp4_clustered_winners_and_ties():
 def test_index_mxfp4_exponent_extremes():
     """Exponent bytes that send tiles to the exact pass of the scorer: keys scaled by
     2^84 with a query head scaled by 2^34 (no overflow, but the bound on |q.k| no
-    longer rules it out), NaN key exponents (0xFF) and, in batch 1, a NaN query
-    exponent (every tile exact)."""
+    longer rules it out), NaN key exponents (0xFF: those keys score NaN and rank
+    last) and, in batch 1, a NaN query exponent (every tile exact; every score NaN,
+    so the selection is the lowest ids)."""
     rows = 6000
     q_pos = np.array([[rows * 4 - 1], [rows * 4 - 1]], np.int64)
     c = _index_case_mx(5, 2, rows, q_pos, 256)
@@ -172,7 +173,8 @@ def test_index_mxfp4_exponent_extremes():
     dkeys, diq = F.mxfp4_dequantize(c['packed'], sc), F.mxfp4_dequantize(c['ip'], isc)
     for b in range(2):
         s = OI.index_scores(diq[b, 0], c['w'][b, 0], dkeys[b])
-        assert np.all(np.isfinite(s.astype(np.float32))), 'the case must not overflow float32'
+        assert not np.isinf(s.astype(np.float32)).any(), 'the case must not overflow float32'
+    assert np.isnan(OI.index_scores(diq[1, 0], c['w'][1, 0], dkeys[1])).all()
     print('index mxfp4 exponent extremes', flush=True)
     idx, score = _run_index(c)
     _check_index(c, idx, score, dkeys, diq)
