@@ -123,6 +123,11 @@ def _run_index(c, fmt='mx'):
     return idx.cpu().numpy(), score.cpu().numpy()
 
 
+def _same_bits(a, b):
+    """Bitwise equality of float arrays (NaN scores included)."""
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
 def _check_index(c, idx, score, dkeys, diq):
     B, Tq = c['q_pos'].shape
     rows = dkeys.shape[1]
@@ -205,7 +210,7 @@ def test_index_mxfp4_many_queries_per_sequence():
         ci = dict(c, q_pos=c['q_pos'][:, i:i + 1], ip=c['ip'][:, i:i + 1], isc=c['isc'][:, i:i + 1],
                   w=c['w'][:, i:i + 1])
         idx1, score1 = _run_index(ci)
-        assert np.array_equal(idx1[:, 0], idx[:, i]) and np.array_equal(score1[:, 0], score[:, i]), f'query {i}'
+        assert np.array_equal(idx1[:, 0], idx[:, i]) and _same_bits(score1[:, 0], score[:, i]), f'query {i}'
 
 
 def test_index_mxfp4_tokens_sharing_a_large_key_set():
@@ -230,7 +235,7 @@ def test_index_mxfp4_tokens_sharing_a_large_key_set():
         ci = dict(c, q_pos=c['q_pos'][:, i:i + 1], ip=c['ip'][:, i:i + 1], isc=c['isc'][:, i:i + 1],
                   w=c['w'][:, i:i + 1])
         idx1, score1 = _run_index(ci)
-        assert np.array_equal(idx1[:, 0], idx[:, i]) and np.array_equal(score1[:, 0], score[:, i]), f'token {i}'
+        assert np.array_equal(idx1[:, 0], idx[:, i]) and _same_bits(score1[:, 0], score[:, i]), f'token {i}'
 
 
 def test_index_mxfp4_repeat_is_bitwise_identical():
@@ -238,7 +243,7 @@ def test_index_mxfp4_repeat_is_bitwise_identical():
     c = _index_case_mx(3, 1, 12000, q_pos, 256)
     a = _run_index(c)
     b = _run_index(c)
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[0], b[0]) and _same_bits(a[1], b[1])
 
 
 def test_index_f32_small():
