@@ -232,6 +232,19 @@ size_t lightning_index_topk_workspace(const v4a_index_args *a);
 int lightning_index_topk(const v4a_index_args *a, void *workspace, size_t workspace_bytes,
                          v4a_stream stream);
 
+/* lightning_index_topk without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments, results and errors as
+ * lightning_index_topk; its scratch is a static device array of
+ * V4A_NOALLOC_SCRATCH_BYTES per GPU (held until the process ends), zero-filled
+ * on the first call on each device (on that call's stream). A call needing more
+ * scratch than that (lightning_index_topk_workspace() above the limit; about
+ * 264 KB per query at 262,144 entries) returns V4A_EWORKSPACE before anything
+ * is enqueued. It allocates nothing. All calls on one GPU share the array:
+ * calls that overlap in time on one GPU (other streams or host threads) race. */
+#define V4A_NOALLOC_SCRATCH_BYTES (32u << 20)
+int lightning_index_topk_noalloc(const v4a_index_args *a, v4a_stream stream);
+
 /* ------------------------------------------------------------------------
  * Attention over compressed entries plus the raw window, one KV head shared
  * by H_q query heads.

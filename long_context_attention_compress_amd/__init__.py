@@ -19,7 +19,7 @@ from . import _abi
 from ._abi import (ACT_BF16, ACT_F32, IK_F32, IK_MXFP4, KV_E4M3_BF16, KV_F32)
 
 __all__ = ['KVStore', 'IKStore', 'Workspace', 'V4AError', 'Call', 'csa_compress', 'lightning_index_topk',
-           'sparse_window_attn', 'hca_attn', 'lib', 'ROPE_DIM']
+           'lightning_index_topk_noalloc', 'sparse_window_attn', 'hca_attn', 'lib', 'ROPE_DIM']
 
 ROPE_DIM = 64
 
@@ -229,6 +229,28 @@ def lightning_index_topk(q_pos, iq, w, keys, k, m, iq_scale=None, out_idx=None, 
     ptr, size = ws.get(nbytes, stream)
     keep = (a, q_pos, iq, iq_scale, w, keys, out_idx, out_score, ws.buf)
     call = _finish(L.lightning_index_topk, (ctypes.byref(a), ptr, size, _stream(stream)), keep, prepare)
+    return call if prepare else out_idx
+
+
+def lightning_index_topk_noalloc(q_pos, iq, w, keys, k, m, iq_scale=None, out_idx=None, out_score=None,
+                                 stream=None, prepare=False):
+    """lightning_index_topk with the library's static per-GPU scratch instead of a workspace
+    (the call itself allocates nothing; calls that overlap on one GPU race on the scratch)."""
+    _need(q_pos, 'q_pos', torch.int64)
+    _need(iq, 'iq')
+    _need(w, 'w', torch.float32)
+    B, Tq, H = w.shape
+    if out_idx is None:
+        out_idx = torch.empty(B, Tq, k, dtype=torch.int32, device=w.device)
+    a = _abi.IndexArgs()
+    a.B, a.Tq, a.H_I, a.k, a.m = B, Tq, H, k, m
+    a.q_pos, a.iq, a.w = _ptr(q_pos), _ptr(iq), _ptr(w)
+    a.iq_scale = _ptr(_need(iq_scale, 'iq_scale')) if iq_scale is not None else None
+    a.keys = keys.c()
+    a.out_idx = _ptr(_need(out_idx, 'out_idx', torch.int32))
+    a.out_score = _ptr(out_score) if out_score is not None else None
+    keep = (a, q_pos, iq, iq_scale, w, keys, out_idx, out_score)
+    call = _finish(lib().lightning_index_topk_noalloc, (ctypes.byref(a), _stream(stream)), keep, prepare)
     return call if prepare else out_idx
 
 

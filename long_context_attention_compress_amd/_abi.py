@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), 'libv4attn.s
 
 V4A_OK, V4A_EINVAL, V4A_ENULL, V4A_EALIGN, V4A_EFORMAT, V4A_EWORKSPACE, V4A_EHIP = 0, -1, -2, -3, -4, -5, -6
 KV_F32, KV_E4M3_BF16 = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20   # V4A_NOALLOC_SCRATCH_BYTES
 IK_F32, IK_MXFP4 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1
 
@@ -58,6 +59,7 @@ EXPORTS = {
     'csa_compress': (c_i32, [ctypes.POINTER(CompressArgs), c_p]),
     'lightning_index_topk_workspace': (ctypes.c_size_t, [ctypes.POINTER(IndexArgs)]),
     'lightning_index_topk': (c_i32, [ctypes.POINTER(IndexArgs), c_p, ctypes.c_size_t, c_p]),
+    'lightning_index_topk_noalloc': (c_i32, [ctypes.POINTER(IndexArgs), c_p]),
     'sparse_window_attn_workspace': (ctypes.c_size_t, [ctypes.POINTER(AttnArgs), c_i32]),
     'sparse_window_attn': (c_i32, [ctypes.POINTER(AttnArgs), c_p, c_i32, c_p, ctypes.c_size_t, c_p]),
     'hca_attn_workspace': (ctypes.c_size_t, [ctypes.POINTER(AttnArgs), c_i64]),

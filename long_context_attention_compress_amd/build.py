@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, 'csrc')
 BUILD = os.path.join(ROOT, '_build')
 LIB = os.path.join(PKG, 'libv4attn.so')
 
-SOURCES = ['compress.hip', 'index.hip', 'attn.hip', 'abi.cpp']
+SOURCES = ['compress.hip', 'index.hip', 'attn.hip', 'noalloc.hip', 'abi.cpp']
 ARCH = os.environ.get('V4A_OFFLOAD_ARCH', 'gfx950')
 FLAGS = ['-O3', '-fPIC', '-std=c++17', f'--offload-arch={ARCH}', '-Wall', '-Wno-unused-function',
          '-Xclang', '-target-feature', '-Xclang', '-packed-fp32-ops',

@@ -408,6 +408,29 @@ size_t lightning_index_topk_workspace(const v4a_index_args *a) {
 }
 
 int lightning_index_topk(const v4a_index_args *a, void *ws, size_t ws_bytes, v4a_stream stream) {
+    return v4a::index_call(a, ws, ws_bytes, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace v4a {
+
+int report(int status, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    return fail(status, "%s", buf);
+}
+
+int index_workspace(const v4a_index_args *a, size_t *bytes) {
+    const int r = check_index(a);
+    *bytes = r ? 0 : index_layout(a).total;
+    return r;
+}
+
+int index_call(const v4a_index_args *a, void *ws, size_t ws_bytes, hipStream_t stream) {
     int r = check_index(a);
     if (r) return r;
     const IndexLayout L = index_layout(a);
@@ -437,8 +460,16 @@ int lightning_index_topk(const v4a_index_args *a, void *ws, size_t ws_bytes, v4a
     P.meta = (uint32_t *)(w + L.off_meta);
     P.reg_key = (uint32_t *)(w + L.off_key);
     P.reg_idx = (int32_t *)(w + L.off_idx);
-    return hip_status(launch_index(P, (hipStream_t)stream), "index launch");
+    return hip_status(launch_index(P, stream), "index launch");
 }
+
+int fill_zero(void *ptr, size_t bytes, hipStream_t stream) {
+    return hip_status(launch_fill_zero(ptr, bytes, stream), "scratch initialisation");
+}
+
+}  // namespace v4a
+
+extern "C" {
 
 size_t sparse_window_attn_workspace(const v4a_attn_args *a, int32_t k) {
     AttnPlan P;

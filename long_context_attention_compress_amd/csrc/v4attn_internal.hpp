@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "v4attn.h"
+
 namespace v4a {
 
 constexpr int ROPE_DIM = 64;
@@ -103,6 +105,14 @@ struct AttnPlan {
     int has_app;
     const uint16_t *app_k, *app_v;
 };
+
+// Entry-point pieces shared between translation units (abi.cpp defines them):
+// the index call's validation, workspace size and launch; the error report
+// behind v4a_last_error(); a zero fill of device memory on a stream.
+int report(int status, const char *fmt, ...);
+int index_workspace(const v4a_index_args *a, size_t *bytes);
+int index_call(const v4a_index_args *a, void *ws, size_t ws_bytes, hipStream_t stream);
+int fill_zero(void *ptr, size_t bytes, hipStream_t stream);
 
 hipError_t launch_compress(const CompressPlan &p, hipStream_t s);
 hipError_t launch_index(const IndexPlan &p, hipStream_t s);

@@ -222,3 +222,30 @@ def test_attention_key_list_and_ring_limits():
     assert r == _abi.V4A_EINVAL and 'ring' in msg, (r, msg)
     assert lib.hca_attn_workspace(ctypes.byref(args(ring=128, W=128)), -1) > 0
     assert lib.hca_attn_workspace(ctypes.byref(args(ring=100, W=100)), -1) > 0
+
+
+def test_index_noalloc_rejections():
+    """The workspace-free indexer call validates like lightning_index_topk and rejects a call
+    whose scratch would exceed the static array, before touching any device."""
+    keys = _ik(rows=262144)
+
+    def args(**kw):
+        a = _abi.IndexArgs()
+        a.B, a.Tq, a.H_I, a.k, a.m = 4, 1, 64, 1024, 4
+        a.q_pos = a.iq = a.iq_scale = a.w = a.out_idx = FAKE
+        a.keys = ctypes.pointer(keys)
+        for n, val in kw.items():
+            setattr(a, n, val)
+        return a
+
+    lib = _abi.load()
+    need = lib.lightning_index_topk_workspace(ctypes.byref(args()))
+    assert 0 < need <= _abi.NOALLOC_SCRATCH_BYTES
+    for kw, want in [(dict(k=0), _abi.V4A_EINVAL), (dict(q_pos=None), _abi.V4A_ENULL),
+                     (dict(iq=FAKE + 4), _abi.V4A_EALIGN), (dict(H_I=20), _abi.V4A_EFORMAT)]:
+        r, msg = _status('lightning_index_topk_noalloc', ctypes.byref(args(**kw)), None)
+        assert r == want, (kw, r, msg)
+    big = args(Tq=1000)
+    assert lib.lightning_index_topk_workspace(ctypes.byref(big)) > _abi.NOALLOC_SCRATCH_BYTES
+    r, msg = _status('lightning_index_topk_noalloc', ctypes.byref(big), None)
+    assert r == _abi.V4A_EWORKSPACE and 'static scratch' in msg, (r, msg)
