@@ -64,6 +64,11 @@ Q_O = H * D * 2 + H * D * 4                           # bf16 query in, float32 o
 APPEND = 2 * D * 2 + 2 * ROW_KV                       # one window append: raw K,V in, two rows out
 
 
+def sparse_bytes():
+    """Algorithmic HBM bytes of one sparse_window_attn launch with its fused window append."""
+    return B * ((K + W) * 2 * ROW_KV + K * 4 + Q_O + APPEND)
+
+
 def csa_bytes():
     """Algorithmic HBM bytes of the CSA layer of one step (whole batch, block compression amortised)."""
     block = (M_CSA * (2 * D + DI) * 2 + 2 * ROW_KV + ROW_IK) / M_CSA
@@ -272,6 +277,32 @@ def timed(torch, calls, L, first, steps, instrument, cyc_per_ms):
         out['sparse_ms'] = seg(2, 3)
         out['hca_ms'] = seg(3, 4)
     return out
+
+
+def graph_timed(torch, calls, L, stream, first, steps):
+    """Time `steps` steps replayed from HIP graphs, each holding L consecutive steps (one pass
+    over the L layer copies, with the CSA block compression every 4th step). A second graph
+    holds the L steps that end on the HCA block compression (every 128th step); it replays
+    in place of the first wherever the real step sequence has that block."""
+    assert steps % L == 0 and first % L == 0 and M_HCA % L == 0
+    graphs = {}
+    for start in (0, M_HCA - L):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(L):
+                run_step(calls, start + i, L)
+        graphs[start] = g
+    for g in graphs.values():      # one replay each before timing
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for r in range(steps // L):
+        s0 = first + r * L
+        graphs[M_HCA - L if s0 % M_HCA == M_HCA - L else 0].replay()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end)
 
 
 CPU_SAMPLE_S = 10.0  # seconds of oracle work per run
@@ -724,25 +755,39 @@ def main():
     import long_context_attention_compress_amd as v4
     import synth
     L = a.layers
-    print(f'[bench] building {L} layer caches (B={B}, context {T})', file=sys.stderr, flush=True)
-    layers, inputs = build_layers(v4, synth, torch, L, a.seed)
-    calls, outs = prepare_calls(v4, synth, torch, layers, inputs, a.seed)
-    calibration_copy(torch)
-    print('[bench] warmup', file=sys.stderr, flush=True)
-    for s in range(a.warmup):
-        run_step(calls, s, L)
-    torch.cuda.synchronize()
-    print('[bench] timed', file=sys.stderr, flush=True)
-    cyc = sleep_cycles_per_ms(torch)
-    clean = timed(torch, calls, L, a.warmup, a.steps, False, cyc)
-    inst = timed(torch, calls, L, a.warmup + a.steps + 4, a.steps, True, cyc)
-    ms = clean['total_ms'] / a.steps
+    if a.steps % L:
+        a.steps += L - a.steps % L      # whole passes over the layer copies (one graph each)
+    warm = (a.warmup + L - 1) // L * L
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        print(f'[bench] building {L} layer caches (B={B}, context {T})', file=sys.stderr, flush=True)
+        layers, inputs = build_layers(v4, synth, torch, L, a.seed)
+        calls, outs = prepare_calls(v4, synth, torch, layers, inputs, a.seed)
+        calibration_copy(torch)
+        print('[bench] warmup', file=sys.stderr, flush=True)
+        for s in range(warm):
+            run_step(calls, s, L)
+        torch.cuda.synchronize()
+        print('[bench] timed (graph replay)', file=sys.stderr, flush=True)
+        graph_ms = graph_timed(torch, calls, L, stream, warm, a.steps)
+        print('[bench] timed (eager, instrumented)', file=sys.stderr, flush=True)
+        cyc = sleep_cycles_per_ms(torch)
+        clean = timed(torch, calls, L, warm, a.steps, False, cyc)
+        inst = timed(torch, calls, L, warm + a.steps + 4, a.steps, True, cyc)
+    ms = graph_ms / a.steps
+    eager_ms = clean['total_ms'] / a.steps
     value = B / (ms * 1e-3)
     idx_ms = sum(inst['index_ms']) / len(inst['index_ms'])
     achieved = index_bytes() / (idx_ms * 1e-3) / 1e9
     traffic = traffic_from_profile()
     csa_ms = (sum(inst['csa_block_ms']) + sum(inst['index_ms']) + sum(inst['sparse_ms'])) / a.steps
     hca_ms = sum(inst['hca_ms']) / a.steps
+    sparse_ms = sum(inst['sparse_ms']) / a.steps
+
+    def line(kernel, nbytes, t_ms):
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        return {'bound': 'hbm', 'kernel': kernel, 'achieved': round(gbs, 1), 'peak': HBM_PEAK_GBS, 'unit': 'GB/s',
+                'frac': round(gbs / HBM_PEAK_GBS, 4), 'us_per_call': round(t_ms * 1e3, 2)}
     rec = {
         'metric': METRIC, 'value': round(value, 1), 'unit': 'query-tokens/s', 'n_gpus': 1,
         'steps': a.steps, 'warmup': a.warmup, 'ms_per_step': round(ms, 6), 'higher_is_better': True,
@@ -751,10 +796,17 @@ def main():
                                'MXFP4 indexer 64x128, top-1024, window 128) + one HCA layer (m=128, 8,192 entries, '
                                'window 128) per step; 64 query heads, KV dim 192 (E4M3 + BF16 RoPE)',
                    'batch': B, 'context': T, 'layers_rotated': L, 'parallelism': 'single GPU'},
+        'timing': f'{a.steps // L} replays of a HIP graph of {L} steps; eager_ms_per_step: the same steps '
+                  f'enqueued directly behind a spin kernel',
+        'eager_ms_per_step': round(eager_ms, 6),
         'hbm_frac_step': round(step_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         'roofline': {'bound': 'hbm', 'kernel': 'lightning_index_topk', 'achieved': round(achieved, 1),
                      'peak': HBM_PEAK_GBS, 'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
                      'traffic': traffic},
+        'roofline_calls': [line('lightning_index_topk', index_bytes(), idx_ms),
+                           line('sparse_window_attn (with the fused window append)', sparse_bytes(), sparse_ms),
+                           line('hca_attn (with the fused window append; HCA block compression amortised)',
+                                hca_bytes(), hca_ms)],
         'breakdown_us': {'csa_layer': round(csa_ms * 1e3, 2), 'index': round(idx_ms * 1e3, 2),
                          'sparse_attn': round(sum(inst['sparse_ms']) / a.steps * 1e3, 2),
                          'hca_layer': round(hca_ms * 1e3, 2)},
