@@ -427,3 +427,139 @@ def test_page_constants_fixture():
             vals[name] = int(val)
     assert vals['csa_ratio'] == 4 and vals['hca_ratio'] == 128 and vals['window'] == M.WINDOW
     assert vals['rope_dims'] == F.ROPE_DIM and vals['topk_pro'] == 1024 and vals['topk_flash'] == 512
+
+
+# ------------------------------------------------------ compressor variants ----
+
+def _rot_pair_loop(x, p, D, base=10000.0):
+    """Rotate a raw row (list of floats) at position p with complex numbers, pair by pair."""
+    out = list(x)
+    for j in range(32):
+        th = p * base ** (-(2 * j) / 64)
+        z = complex(x[D - 64 + 2 * j], x[D - 64 + 2 * j + 1]) * complex(math.cos(th), math.sin(th))
+        out[D - 64 + 2 * j], out[D - 64 + 2 * j + 1] = z.real, z.imag
+    return out
+
+
+def _variant_case(seed, B, T, D, dI, m, extra=0, channel=False):
+    g = np.random.default_rng(seed)
+    n = T + extra
+    C = 2 * D + dI
+    return dict(k=g.standard_normal((B, n, D)).astype(np.float32), v=g.standard_normal((B, n, D)).astype(np.float32),
+                u=g.standard_normal((B, n, dI)).astype(np.float32),
+                g=g.standard_normal((B, n, C) if channel else (B, n)).astype(np.float32))
+
+
+def test_overlap_with_masked_previous_block_is_block():
+    m, T, D, dI, pos0 = 4, 16, 128, 32, 8
+    c = _variant_case(71, 2, T, D, dI, m, extra=m)
+    beta = np.random.default_rng(72).normal(0, 0.1, m).astype(np.float32)
+    bias = np.concatenate([np.full(m, -np.inf, np.float32), beta])
+    got = C.compress_variant('overlap', c['k'], c['v'], c['g'], bias, pos0, raw_ik=c['u'])
+    ref = C.compress(c['k'][:, m:], c['v'][:, m:], c['g'][:, m:], beta, pos0, raw_ik=c['u'][:, m:])
+    for a, b in zip(got, ref):
+        assert np.abs(a - b).max() <= 1e-6 * np.abs(b).max()
+
+
+def test_overlap_uniform_gate_is_window_mean_and_one_hot():
+    m, T, D, dI = 4, 12, 128, 32
+    c = _variant_case(73, 1, T, D, dI, m, extra=m)
+    gate = np.zeros_like(c['g'])
+    bias = np.zeros(2 * m, np.float32)
+    # pos0 = 0: the first entry has no block before it (mean of its own 4 tokens)
+    k, v, u = C.compress_variant('overlap', c['k'], c['v'], gate, bias, 0, raw_ik=c['u'])
+    pos = np.arange(-m, T)
+    kr = R.apply(c['k'].astype(np.float64), np.maximum(pos, 0)[None])
+    assert np.allclose(v[0, 0], c['v'][0, m:2 * m].mean(0), atol=1e-6)
+    assert np.allclose(k[0, 0], kr[0, m:2 * m].mean(0), atol=1e-6)
+    for e in (1, 2):
+        w = slice(e * m, e * m + 2 * m)
+        assert np.allclose(v[0, e], c['v'][0, w].mean(0), atol=1e-6)
+        assert np.allclose(u[0, e], c['u'][0, w].mean(0), atol=1e-6)
+        assert np.allclose(k[0, e], kr[0, w].mean(0), atol=1e-6)
+    # a one-hot gate on the second token of the previous block picks it (rotated at its own position)
+    gate = np.zeros_like(c['g'])
+    gate[0, m + 1] = 60.0                     # position 1, in the window of entry 1 (positions 0..7)
+    k, v, _ = C.compress_variant('overlap', c['k'], c['v'], gate, bias, 0)
+    assert np.allclose(v[0, 1], c['v'][0, m + 1], atol=1e-6)
+    assert np.allclose(k[0, 1], R.apply(c['k'][0, m + 1].astype(np.float64), np.int64(1)), atol=1e-5)
+
+
+def test_overlap_python_loop():
+    m, T, D, dI, pos0 = 2, 6, 128, 32, 4
+    c = _variant_case(74, 1, T, D, dI, m, extra=m)
+    bias = np.random.default_rng(75).normal(0, 0.5, 2 * m).astype(np.float32)
+    k, v, u = C.compress_variant('overlap', c['k'], c['v'], c['g'], bias, pos0, raw_ik=c['u'])
+    for e in range(T // m):
+        rows = [e * m + r for r in range(2 * m)]                       # window rows of entry e
+        z = [float(c['g'][0, i]) + float(bias[r]) for r, i in enumerate(rows)]
+        zmax = max(z)
+        ex = [math.exp(zz - zmax) for zz in z]
+        a = [x / sum(ex) for x in ex]
+        krot = [_rot_pair_loop([float(x) for x in c['k'][0, i]], pos0 - m + i, D) for i in rows]
+        for ch in (0, 77, 64 + 3, D - 1):
+            assert abs(sum(a[r] * krot[r][ch] for r in range(2 * m)) - k[0, e, ch]) <= 1e-5
+            assert abs(sum(a[r] * float(c['v'][0, rows[r], ch]) for r in range(2 * m)) - v[0, e, ch]) <= 1e-5
+        assert abs(sum(a[r] * float(c['u'][0, rows[r], 5]) for r in range(2 * m)) - u[0, e, 5]) <= 1e-5
+
+
+def test_rope_after_pool_reductions_and_complex_form():
+    D, dI = 128, 32
+    # m = 1: rotating before or after pooling one token is the same operation at the same position
+    c = _variant_case(76, 2, 8, D, dI, 1)
+    got = C.compress_variant('rope_after_pool', c['k'], c['v'], c['g'], np.zeros(1, np.float32), 40, raw_ik=c['u'])
+    ref = C.compress(c['k'], c['v'], c['g'], np.zeros(1, np.float32), 40, raw_ik=c['u'])
+    for a, b in zip(got, ref):
+        assert np.array_equal(a, b)
+    # m = 4: values and indexer keys as in the base reading; keys = e^{i theta p_last} x pooled pair
+    m, pos0 = 4, 1000
+    c = _variant_case(77, 2, 16, D, dI, m)
+    beta = np.random.default_rng(78).normal(0, 0.1, m).astype(np.float32)
+    k, v, u = C.compress_variant('rope_after_pool', c['k'], c['v'], c['g'], beta, pos0, raw_ik=c['u'])
+    kb, vb, ub = C.compress(c['k'], c['v'], c['g'], beta, pos0, raw_ik=c['u'])
+    assert np.array_equal(v, vb) and np.array_equal(u, ub)
+    alpha = C.gate_weights(c['g'], beta)
+    pooled = np.einsum('bem,bemc->bec', alpha, c['k'].astype(np.float64).reshape(2, 4, m, D))
+    z = pooled[..., 64::2] + 1j * pooled[..., 65::2]
+    theta = np.array([10000.0 ** (-(2 * j) / 64) for j in range(32)])
+    last = pos0 + m - 1 + m * np.arange(4)
+    zr = z * np.exp(1j * last[None, :, None] * theta[None, None, :])
+    assert np.allclose(k[..., 64::2], zr.real, atol=1e-5) and np.allclose(k[..., 65::2], zr.imag, atol=1e-5)
+    assert np.allclose(k[..., :64], pooled[..., :64], atol=1e-6)
+    assert not np.allclose(k, kb, atol=1e-3)       # the placements differ
+
+
+def test_channel_gate_reductions_one_hot_and_loop():
+    m, T, D, dI, pos0 = 4, 8, 128, 32, 12
+    c = _variant_case(79, 2, T, D, dI, m, channel=True)
+    Cc = 2 * D + dI
+    # equal gates in every channel: the base reading
+    gs = c['g'][..., 0]
+    beta = np.random.default_rng(80).normal(0, 0.1, m).astype(np.float32)
+    got = C.compress_variant('channel_gate', c['k'], c['v'], np.repeat(gs[..., None], Cc, -1),
+                             np.repeat(beta[:, None], Cc, -1), pos0, raw_ik=c['u'])
+    ref = C.compress(c['k'], c['v'], gs, beta, pos0, raw_ik=c['u'])
+    for a, b in zip(got, ref):
+        assert np.abs(a - b).max() <= 1e-6 * np.abs(b).max()
+    # one-hot per channel: channel ch of entry e takes token (ch % m) of its block
+    gate = np.zeros((2, T, Cc), np.float32)
+    for ch in range(Cc):
+        gate[:, np.arange(T // m) * m + ch % m, ch] = 60.0
+    k, v, u = C.compress_variant('channel_gate', c['k'], c['v'], gate, np.zeros((m, Cc), np.float32), pos0,
+                                 raw_ik=c['u'])
+    kr = R.apply(c['k'].astype(np.float64), (pos0 + np.arange(T))[None])
+    for ch in (0, 5, 64, 101, 127):
+        for e in range(T // m):
+            assert abs(k[1, e, ch] - kr[1, e * m + ch % m, ch]) <= 1e-5
+            assert abs(v[1, e, ch] - c['v'][1, e * m + (D + ch) % m, ch]) <= 1e-5
+    assert abs(u[0, 1, 7] - c['u'][0, m + (2 * D + 7) % m, 7]) <= 1e-5
+    # a plain loop on a few channels
+    bias = np.random.default_rng(81).normal(0, 0.5, (m, Cc)).astype(np.float32)
+    k, v, u = C.compress_variant('channel_gate', c['k'], c['v'], c['g'], bias, pos0, raw_ik=c['u'])
+    for e in range(T // m):
+        krot = [_rot_pair_loop([float(x) for x in c['k'][0, e * m + r]], pos0 + e * m + r, D) for r in range(m)]
+        for ch, src, out, off in ((3, None, k, 0), (70, None, k, 0), (9, c['v'], v, D), (2, c['u'], u, 2 * D)):
+            z = [float(c['g'][0, e * m + r, off + ch]) + float(bias[r, off + ch]) for r in range(m)]
+            ex = [math.exp(zz - max(z)) for zz in z]
+            vals = [krot[r][ch] for r in range(m)] if src is None else [float(src[0, e * m + r, ch]) for r in range(m)]
+            assert abs(sum(x * y for x, y in zip(ex, vals)) / sum(ex) - out[0, e, ch]) <= 1e-5
