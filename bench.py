@@ -241,6 +241,42 @@ def calibration_copy(torch):
     del src, dst
 
 
+def device_floors(torch):
+    """What this device sustains outside the library: a plain copy (torch, 256 MiB read and
+    256 MiB written) and the cost per kernel of back-to-back empty kernels (torch's spin
+    kernel with zero cycles) replayed from a HIP graph."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    src = torch.ones(CALIB_BYTES // 4, device='cuda')
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev[0].record()
+    for _ in range(20):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * CALIB_BYTES * 20 / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e9
+    del src, dst
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        torch.cuda._sleep(0)
+    with torch.cuda.graph(g, stream=s):
+        for _ in range(50):
+            torch.cuda._sleep(0)
+    g.replay()
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(10):
+        g.replay()
+    ev[1].record()
+    torch.cuda.synchronize()
+    empty_us = ev[0].elapsed_time(ev[1]) * 1e3 / 500
+    return {'copy_gbs': round(copy_gbs, 1), 'empty_kernel_us_in_graph': round(empty_us, 2),
+            'how': 'torch copy of 256 MiB (read + write bytes over time), 500 empty kernels (torch spin with '
+                   '0 cycles) replayed from a HIP graph'}
+
+
 def sleep_cycles_per_ms(torch):
     """Calibrate torch.cuda._sleep (a spin kernel) against HIP events."""
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -616,20 +652,24 @@ def stack_kinds(n):
     return ['win', 'win'] + ['csa' if i % 2 == 0 else 'hca' for i in range(n - 2)]
 
 
-def prepare_stack(v4, synth, torch, seed, n_layers, stream):
-    """Caches and prepared launches of every layer of the stack, bound to `stream`."""
+def prepare_stack(v4, synth, torch, seed, n_layers, stream, p0):
+    """Caches and prepared launches of every layer of the stack, bound to `stream`. The
+    decode position lives on the device (starting at p0) and advances by one per step;
+    every CSA and HCA layer has a raw ring of its last m tokens, from which its block is
+    compressed (block mode, at the device position) at the step that completes it."""
     kinds = stack_kinds(n_layers)
     n_csa = kinds.count('csa')
     # one copy of the caches per CSA layer and per HCA or window-only layer (no sharing)
     layers, inputs = build_layers(v4, synth, torch, max(n_csa, n_layers - n_csa), seed)
     dev = 'cuda'
-    pos = torch.full((B, 1), T - 1, dtype=torch.int64, device=dev)
+    pos = torch.full((B, 1), p0, dtype=torch.int64, device=dev)
     new_k = synth.gpu_normal(seed, 'stack/k', (B, 1, D), dtype=torch.bfloat16)
     new_v = synth.gpu_normal(seed, 'stack/v', (B, 1, D), dtype=torch.bfloat16)
-    blk_k4 = synth.gpu_normal(seed, 'stack/k4', (B, M_CSA, D), dtype=torch.bfloat16)
-    blk_v4 = synth.gpu_normal(seed, 'stack/v4', (B, M_CSA, D), dtype=torch.bfloat16)
-    blk_u4 = synth.gpu_normal(seed, 'stack/u4', (B, M_CSA, DI), dtype=torch.bfloat16)
-    g4 = synth.gpu_normal(seed, 'stack/g4', (B, M_CSA))
+    ring = {m: dict(k=synth.gpu_normal(seed, f'stack/ring_k{m}', (B, m, D), dtype=torch.bfloat16),
+                    v=synth.gpu_normal(seed, f'stack/ring_v{m}', (B, m, D), dtype=torch.bfloat16),
+                    g=synth.gpu_normal(seed, f'stack/ring_g{m}', (B, m)))
+            for m in (M_CSA, M_HCA)}
+    ring_u = synth.gpu_normal(seed, 'stack/ring_u', (B, M_CSA, DI), dtype=torch.bfloat16)
     idx = torch.zeros(B, 1, K, dtype=torch.int32, device=dev)
     outs, calls = [], []
     ws_i, ws_a = v4.Workspace(), v4.Workspace()
@@ -641,9 +681,11 @@ def prepare_stack(v4, synth, torch, seed, n_layers, stream):
             if kind == 'csa':
                 Ld = layers[ci]
                 ci += 1
+                r = ring[M_CSA]
                 calls.append(dict(
-                    block=v4.csa_compress(g4, inputs['bias4'], T - M_CSA, blk_k4, blk_v4, Ld['ek'], Ld['ev'], blk_u4,
-                                          Ld['ik'], prepare=True),
+                    kind=kind,
+                    block=v4.csa_compress(r['g'], inputs['bias4'], 0, r['k'], r['v'], Ld['ek'], Ld['ev'], ring_u,
+                                          Ld['ik'], prepare=True, block_end=pos.view(B)),
                     run=[v4.lightning_index_topk(pos, inputs['iq'], inputs['w'], Ld['ik'], K, M_CSA,
                                                  iq_scale=inputs['iq_scale'], out_idx=idx, workspace=ws_i,
                                                  prepare=True),
@@ -654,23 +696,29 @@ def prepare_stack(v4, synth, torch, seed, n_layers, stream):
                 Ld = layers[hi]
                 hi += 1
                 win = kind == 'win'
-                calls.append(dict(block=None, run=[v4.hca_attn(
-                    inputs['q_hca'], pos, None if win else Ld['hk'], None if win else Ld['hv'], M_HCA, Ld['hwk'],
-                    Ld['hwv'], W, n_entries_override=0 if win else -1, o=o, workspace=ws_a, prepare=True,
-                    append_k=new_k, append_v=new_v)]))
+                r = ring[M_HCA]
+                calls.append(dict(
+                    kind=kind,
+                    block=None if win else v4.csa_compress(r['g'], inputs['bias128'], 0, r['k'], r['v'], Ld['hk'],
+                                                           Ld['hv'], prepare=True, block_end=pos.view(B)),
+                    run=[v4.hca_attn(inputs['q_hca'], pos, None if win else Ld['hk'], None if win else Ld['hv'],
+                                     M_HCA, Ld['hwk'], Ld['hwv'], W, n_entries_override=0 if win else -1, o=o,
+                                     workspace=ws_a, prepare=True, append_k=new_k, append_v=new_v)]))
     torch.cuda.synchronize()
-    return calls, outs, (layers, inputs, pos, new_k, new_v, blk_k4, blk_v4, blk_u4, g4, idx, ws_i, ws_a)
+    return calls, outs, pos, (layers, inputs, new_k, new_v, ring, ring_u, idx, ws_i, ws_a)
 
 
-def run_stack(calls, step):
-    """One decode step through the stack: each CSA layer compresses its finished block
-    of four every fourth step (the HCA layers' block of 128 comes once per 128 steps
-    and is left out)."""
+def run_stack(calls, pos, t):
+    """One decode step at position t (pos holds t on the device when the step starts): each
+    CSA layer compresses its block of four when t completes it, each HCA layer its block of
+    128; every layer appends the token to its window; then the position advances."""
     for c in calls:
-        if c['block'] is not None and step % M_CSA == M_CSA - 1:
+        m = M_CSA if c['kind'] == 'csa' else M_HCA
+        if c['block'] is not None and (t + 1) % m == 0:
             c['block']()
         for f in c['run']:
             f()
+    pos.add_(1)
 
 
 def stack_main(a):
@@ -678,50 +726,69 @@ def stack_main(a):
     import long_context_attention_compress_amd as v4
     import synth
     n = a.stack_layers
+    reps = max(1, a.steps // M_CSA)
+    warm = max(a.warmup, M_CSA) // M_CSA * M_CSA
+    # the run's positions stay below the cached context; graphs start at multiples of 4
+    total = warm + 2 * reps * M_CSA + M_HCA
+    p0 = (T - total - M_HCA) // M_HCA * M_HCA
     print(f'[bench] building a {n}-layer stack (B={B}, context {T})', file=sys.stderr, flush=True)
     s = torch.cuda.Stream()
-    calls, outs, keep = prepare_stack(v4, synth, torch, a.seed, n, s)
+    calls, outs, pos, keep = prepare_stack(v4, synth, torch, a.seed, n, s, p0)
+    t = p0
     with torch.cuda.stream(s):
-        for i in range(max(a.warmup, M_CSA)):
-            run_stack(calls, i)
+        for _ in range(warm):
+            run_stack(calls, pos, t)
+            t += 1
     torch.cuda.synchronize()
-    # eager: four steps enqueued directly (host launch cost included)
+    # eager: the steps enqueued directly (host launch cost included)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    reps = max(1, a.steps // M_CSA)
     with torch.cuda.stream(s):
         ev[0].record()
-        for r in range(reps):
-            for i in range(M_CSA):
-                run_stack(calls, i)
+        for _ in range(reps * M_CSA):
+            run_stack(calls, pos, t)
+            t += 1
         ev[1].record()
     torch.cuda.synchronize()
     eager_ms = ev[0].elapsed_time(ev[1]) / (reps * M_CSA)
-    # one graph holds four steps (so each CSA layer's block compression appears once)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for i in range(M_CSA):
-            run_stack(calls, i)
-    g.replay()
+    # graphs of four steps starting at a multiple of 4 (CSA blocks at the fourth step);
+    # the one whose fourth step completes an HCA block of 128 has that compression too
+    assert t % M_CSA == 0
+    graphs = {}
+    for first in (0, M_HCA - M_CSA):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(M_CSA):
+                run_stack(calls, pos, first + i)
+        graphs[first] = g
+    # capturing ran nothing: put the position back where the step sequence is
+    pos.fill_(t)
     torch.cuda.synchronize()
+    n_hca_blocks = 0
     with torch.cuda.stream(s):
         ev[0].record()
         for r in range(reps):
-            g.replay()
+            hb = t % M_HCA == M_HCA - M_CSA
+            n_hca_blocks += hb
+            graphs[M_HCA - M_CSA if hb else 0].replay()
+            t += M_CSA
         ev[1].record()
     torch.cuda.synchronize()
+    assert int(pos[0, 0]) == t, 'the device position did not follow the replays'
     ms = ev[0].elapsed_time(ev[1]) / (reps * M_CSA)
     kinds = stack_kinds(n)
     rec = {
         'metric': STACK_METRIC, 'value': round(B / (ms * 1e-3), 1), 'unit': 'query-tokens/s', 'n_gpus': 1,
-        'steps': reps * M_CSA, 'warmup': max(a.warmup, M_CSA), 'ms_per_step': round(ms, 6),
+        'steps': reps * M_CSA, 'warmup': warm, 'ms_per_step': round(ms, 6),
         'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None, 'dtype': 'mxfp4+e4m3/bf16',
         'data': 'synthetic',
-        'config': {'workload': f'decode at 1,048,576-token context, batch 4, through {n} attention layers: '
-                               f'{kinds.count("win")} window-only, {kinds.count("csa")} CSA (m=4, top-1024, block '
-                               f'compression every 4th step), {kinds.count("hca")} HCA (m=128); every layer appends '
-                               'the new token to its window inside the attention launch; four steps captured in '
-                               'one HIP graph and replayed',
-                   'batch': B, 'context': T, 'layers': n, 'parallelism': 'single GPU'},
+        'config': {'workload': f'decode at about 1,048,576-token context, batch 4, through {n} attention layers: '
+                               f'{kinds.count("win")} window-only, {kinds.count("csa")} CSA (m=4, top-1024), '
+                               f'{kinds.count("hca")} HCA (m=128); the position advances every step on the device; '
+                               'each CSA layer compresses its block of 4 at the step that completes it, each HCA '
+                               'layer its block of 128 (block mode, device positions); every layer appends the new '
+                               'token to its window inside the attention launch; four steps per HIP graph, replayed',
+                   'batch': B, 'context': T, 'layers': n, 'first_position': p0,
+                   'hca_blocks_in_timed_steps': n_hca_blocks, 'parallelism': 'single GPU'},
         'eager_ms_per_step': round(eager_ms, 6),
         'roofline': None,
     }
@@ -768,6 +835,7 @@ def main():
         for s in range(warm):
             run_step(calls, s, L)
         torch.cuda.synchronize()
+        floors = device_floors(torch)
         print('[bench] timed (graph replay)', file=sys.stderr, flush=True)
         graph_ms = graph_timed(torch, calls, L, stream, warm, a.steps)
         print('[bench] timed (eager, instrumented)', file=sys.stderr, flush=True)
@@ -802,7 +870,8 @@ def main():
         'hbm_frac_step': round(step_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         'roofline': {'bound': 'hbm', 'kernel': 'lightning_index_topk', 'achieved': round(achieved, 1),
                      'peak': HBM_PEAK_GBS, 'unit': 'GB/s', 'frac': round(achieved / HBM_PEAK_GBS, 4),
-                     'traffic': traffic},
+                     'traffic': traffic, 'frac_of_measured_copy': round(achieved / floors['copy_gbs'], 4)},
+        'device_floors': floors,
         'roofline_calls': [line('lightning_index_topk', index_bytes(), idx_ms),
                            line('sparse_window_attn (with the fused window append)', sparse_bytes(), sparse_ms),
                            line('hca_attn (with the fused window append; HCA block compression amortised)',

@@ -84,6 +84,13 @@ typedef enum {
 typedef enum { V4A_KV_F32 = 0, V4A_KV_E4M3_BF16 = 1 } v4a_kv_format;
 typedef enum { V4A_IK_F32 = 0, V4A_IK_MXFP4 = 1 } v4a_ik_format;
 typedef enum { V4A_ACT_F32 = 0, V4A_ACT_BF16 = 1 } v4a_act_format;
+/* Compressor variants of csa_compress (readings of the pages; see csa_compress). */
+typedef enum {
+    V4A_POOL_BLOCK = 0,          /* blocks of m, keys rotated then pooled, one gate per token */
+    V4A_POOL_OVERLAP = 1,        /* windows of 2m: the block and the one before it */
+    V4A_POOL_ROPE_AFTER = 2,     /* keys pooled unrotated, rotated at the block's last position */
+    V4A_POOL_CHANNEL_GATE = 3    /* one gate logit per token and output channel */
+} v4a_pool_variant;
 
 /* One plane of a store: element (b, row, ...) starts at
  * ptr + b*batch_stride + row*row_stride (strides in BYTES). */
@@ -170,6 +177,42 @@ typedef struct {
  * t_new/m - 1, which must fit in the rows of linear stores. A ring store
  * (k_out/v_out with ring > 0, e.g. the window) receives only the last `ring`
  * of them, at row entry % ring.
+ *
+ *  block_end   NULL, or (block mode, decode) a DEVICE array [B] of positions:
+ *              for each batch element b the call compresses the one block of m
+ *              tokens ending at t = block_end[b] into entry (t+1)/m - 1, when
+ *              t + 1 is a positive multiple of m; otherwise (or when the entry
+ *              is past a linear store's rows) nothing is written for b. The
+ *              raw inputs are then rings of t_new rows per batch element (a
+ *              multiple of m): position p is row p % t_new of raw_k, raw_v and
+ *              raw_ik and element p % t_new of gate. pos0 must be 0. Positions
+ *              are read on the device, so the call can be captured once in a
+ *              HIP graph while the positions advance from replay to replay
+ *              (the block is written at the step it completes).
+ *              [chaosnode.de, "DeepSeek-V4: 1 Million Token Context endlich
+ *              nutzbar", section "Hybrid Attention: CSA und HCA": blocks of 4
+ *              (CSA) or 128 (HCA) consecutive tokens become one entry]
+ *  variant     a v4a_pool_variant (0 = V4A_POOL_BLOCK, the pooling above).
+ *              V4A_POOL_OVERLAP [webconsulting.at, section "Kompression und
+ *              Selektion": CSA lets information flow across group
+ *              boundaries]: entry e pools the 2m tokens (e-1)m .. (e+1)m - 1
+ *              with alpha = softmax over the 2m of (gate + pos_bias[offset]),
+ *              pos_bias [2m] (offsets below m: the block before); positions
+ *              below 0 do not take part. The raw inputs and gate then hold
+ *              t_new + m rows, positions pos0 - m .. pos0 + t_new - 1 (the
+ *              first m unread when pos0 = 0); in block mode the ring needs at
+ *              least 2m rows. m <= 512.
+ *              V4A_POOL_ROPE_AFTER [golem.de, same section as above: the last
+ *              64 values carry RoPE]: K = RoPE(sum_r alpha_r raw_k[r], p_last),
+ *              p_last the block's last position; V and U as above.
+ *              V4A_POOL_CHANNEL_GATE [chaosnode.de, same section: softmax
+ *              gating with a learned positional bias, per channel]: gate
+ *              [B][t_new][C] and pos_bias [m][C], C = 2 dim (when k_out is
+ *              given) + ik dim (when ik_out is given), channels ordered K, V, U;
+ *              channel c of an entry pools with its own softmax over r of
+ *              gate[.][r][c] + pos_bias[r][c].
+ *              Every variant keeps the store formats and the visibility rule,
+ *              so the attention calls read their entries unchanged.
  * ---------------------------------------------------------------------- */
 typedef struct {
     int32_t B;
@@ -186,6 +229,8 @@ typedef struct {
     const v4a_kv_store *k_out;
     const v4a_kv_store *v_out;
     const v4a_ik_store *ik_out;
+    const int64_t *block_end;
+    int32_t variant;
 } v4a_compress_args;
 
 int csa_compress(const v4a_compress_args *a, v4a_stream stream);

@@ -16,7 +16,8 @@ import ctypes
 import torch
 
 from . import _abi
-from ._abi import (ACT_BF16, ACT_F32, IK_F32, IK_MXFP4, KV_E4M3_BF16, KV_F32)
+from ._abi import (ACT_BF16, ACT_F32, IK_F32, IK_MXFP4, KV_E4M3_BF16, KV_F32, POOL_BLOCK, POOL_CHANNEL_GATE,
+                   POOL_OVERLAP, POOL_ROPE_AFTER)
 
 __all__ = ['KVStore', 'IKStore', 'Workspace', 'V4AError', 'Call', 'csa_compress', 'lightning_index_topk',
            'lightning_index_topk_noalloc', 'sparse_window_attn', 'hca_attn', 'lib', 'ROPE_DIM']
@@ -180,16 +181,31 @@ def _finish(fn, args, keep, prepare):
 
 
 def csa_compress(gate, pos_bias, pos0, raw_k=None, raw_v=None, k_out=None, v_out=None,
-                 raw_ik=None, ik_out=None, rope_base=10000.0, stream=None, prepare=False):
-    """Pool blocks of m = len(pos_bias) raw tokens into entries pos0/m ... of the stores.
+                 raw_ik=None, ik_out=None, rope_base=10000.0, stream=None, prepare=False, block_end=None,
+                 variant=POOL_BLOCK):
+    """Pool blocks of m raw tokens into entries pos0/m ... of the stores.
 
+    m = len(pos_bias) (POOL_BLOCK, POOL_ROPE_AFTER), len(pos_bias) / 2 (POOL_OVERLAP, whose raw
+    inputs and gate start m positions before pos0), pos_bias.shape[0] (POOL_CHANNEL_GATE, gate
+    [B, T, C] and pos_bias [m, C]).
+    block_end [B] int64 (device): block mode, the one block ending at each position (when it
+    completes a block), raw inputs being rings of gate.shape[1] rows indexed by position.
     With prepare=True nothing is launched; a Call that enqueues this operation is returned."""
     _need(gate, 'gate', torch.float32)
     _need(pos_bias, 'pos_bias', torch.float32)
     ref = raw_k if raw_k is not None else raw_ik
-    B, T = gate.shape
+    B, T = gate.shape[:2]
+    if variant == POOL_OVERLAP:
+        m = pos_bias.numel() // 2
+        if block_end is None:
+            T -= m          # the first m rows are the block before pos0
+    elif variant == POOL_CHANNEL_GATE:
+        m = pos_bias.shape[0]
+    else:
+        m = pos_bias.numel()
     a = _abi.CompressArgs()
-    a.B, a.t_new, a.pos0, a.m = B, T, int(pos0), pos_bias.numel()
+    a.B, a.t_new, a.pos0, a.m = B, T, int(pos0), m
+    a.variant = variant
     a.act_fmt = _act(ref)
     a.rope_base = rope_base
     if raw_k is not None:
@@ -202,7 +218,9 @@ def csa_compress(gate, pos_bias, pos0, raw_k=None, raw_v=None, k_out=None, v_out
         a.raw_ik = _ptr(raw_ik)
         a.ik_out = ik_out.c()
     a.gate, a.pos_bias = _ptr(gate), _ptr(pos_bias)
-    keep = (a, gate, pos_bias, raw_k, raw_v, k_out, v_out, raw_ik, ik_out)
+    if block_end is not None:
+        a.block_end = _ptr(_need(block_end, 'block_end', torch.int64))
+    keep = (a, gate, pos_bias, raw_k, raw_v, k_out, v_out, raw_ik, ik_out, block_end)
     return _finish(lib().csa_compress, (ctypes.byref(a), _stream(stream)), keep, prepare)
 
 

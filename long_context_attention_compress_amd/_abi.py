@@ -15,6 +15,7 @@ KV_F32, KV_E4M3_BF16 = 0, 1
 NOALLOC_SCRATCH_BYTES = 32 << 20   # V4A_NOALLOC_SCRATCH_BYTES
 IK_F32, IK_MXFP4 = 0, 1
 ACT_F32, ACT_BF16 = 0, 1
+POOL_BLOCK, POOL_OVERLAP, POOL_ROPE_AFTER, POOL_CHANNEL_GATE = 0, 1, 2, 3
 
 c_i32, c_i64, c_p, c_f, c_d = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.c_double
 
@@ -37,7 +38,7 @@ class CompressArgs(ctypes.Structure):
     _fields_ = [('B', c_i32), ('t_new', c_i32), ('pos0', c_i64), ('m', c_i32), ('act_fmt', c_i32),
                 ('rope_base', c_d), ('raw_k', c_p), ('raw_v', c_p), ('gate', c_p), ('pos_bias', c_p),
                 ('raw_ik', c_p), ('k_out', ctypes.POINTER(KvStoreC)), ('v_out', ctypes.POINTER(KvStoreC)),
-                ('ik_out', ctypes.POINTER(IkStoreC))]
+                ('ik_out', ctypes.POINTER(IkStoreC)), ('block_end', c_p), ('variant', c_i32)]
 
 
 class IndexArgs(ctypes.Structure):

@@ -354,6 +354,16 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
     if (a->m < 1 || a->m > 1024) return fail(V4A_EINVAL, "m must be in 1..1024 (got %d)", a->m);
     if (a->pos0 < 0 || a->pos0 % a->m || a->t_new % a->m)
         return fail(V4A_EINVAL, "pos0 and t_new must be non-negative multiples of m");
+    if (a->variant < V4A_POOL_BLOCK || a->variant > V4A_POOL_CHANNEL_GATE)
+        return fail(V4A_EFORMAT, "unknown compressor variant %d", a->variant);
+    const int span = a->variant == V4A_POOL_OVERLAP ? 2 * a->m : a->m;  // tokens one entry pools
+    if (a->variant == V4A_POOL_OVERLAP && a->m > 512) return fail(V4A_EINVAL, "overlapping windows need m <= 512");
+    if (a->block_end) {
+        if (a->pos0 != 0) return fail(V4A_EINVAL, "block mode (block_end given) needs pos0 == 0");
+        if (a->t_new < span)
+            return fail(V4A_EINVAL, "block mode: the raw ring (t_new rows) must hold the %d tokens an entry pools", span);
+        if (!aligned(a->block_end, 8)) return fail(V4A_EALIGN, "block_end must be 8-byte aligned");
+    }
     if (a->act_fmt != V4A_ACT_F32 && a->act_fmt != V4A_ACT_BF16) return fail(V4A_EFORMAT, "unknown activation format");
     if (a->t_new == 0) return V4A_OK;  // nothing to compress: no pointer is read, nothing is launched
     if (!a->gate || !a->pos_bias) return fail(V4A_ENULL, "gate and pos_bias are required");
@@ -369,6 +379,8 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
     P.pos0 = a->pos0;
     P.gate = a->gate;
     P.pos_bias = a->pos_bias;
+    P.block_end = a->block_end;
+    P.variant = a->variant;
     const int64_t e0 = a->pos0 / a->m, ne = a->t_new / a->m;
     const size_t esz = a->act_fmt == V4A_ACT_F32 ? 4 : 2;
     int r;
@@ -378,7 +390,7 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
         if (a->k_out->fmt != a->v_out->fmt || a->k_out->dim != a->v_out->dim || a->k_out->ring != a->v_out->ring)
             return fail(V4A_EFORMAT, "k_out and v_out must share format, dim and ring");
         for (const v4a_kv_store *s : {a->k_out, a->v_out}) {
-            if (s->ring == 0 && e0 + ne > s->rows)
+            if (!a->block_end && s->ring == 0 && e0 + ne > s->rows)
                 return fail(V4A_EINVAL, "entries %lld..%lld do not fit in %lld rows", (long long)e0,
                             (long long)(e0 + ne - 1), (long long)s->rows);
         }
@@ -390,13 +402,14 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
     }
     if (a->ik_out) {
         if ((r = check_ik(a->ik_out, "ik_out", &P.ik))) return r;
-        if (e0 + ne > a->ik_out->rows) return fail(V4A_EINVAL, "indexer entries do not fit in the store");
+        if (!a->block_end && e0 + ne > a->ik_out->rows) return fail(V4A_EINVAL, "indexer entries do not fit in the store");
         if (a->ik_out->fmt == V4A_IK_F32 && a->ik_out->dim % 4) return fail(V4A_EFORMAT, "bad indexer dim");
         if (!aligned(a->raw_ik, esz)) return fail(V4A_EALIGN, "raw_ik misaligned");
         P.has_ik = 1;
         P.dI = a->ik_out->dim;
         P.raw_ik = a->raw_ik;
     }
+    if (a->variant == V4A_POOL_CHANNEL_GATE) P.gate_c = (P.has_kv ? 2 * P.D : 0) + (P.has_ik ? P.dI : 0);
     fill_inv_freq(a->rope_base, P.inv_freq);
     if (a->t_new == 0) return V4A_OK;
     return hip_status(launch_compress(P, (hipStream_t)stream), "compress launch");

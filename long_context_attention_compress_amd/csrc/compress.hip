@@ -29,6 +29,37 @@ __device__ __forceinline__ double load_act(const void *base, int64_t i) {
 
 __device__ __forceinline__ int64_t kv_row(const KvView &s, int64_t e) { return s.ring > 0 ? e % s.ring : e; }
 
+// Where block j of batch element b comes from and goes to: `tok0` its first
+// raw row (relative to the batch element's rows of the raw inputs), `first`
+// the position of its first token, `entry` the entry it becomes. In block
+// mode the block ends at the device position block_end[b]; the raw rows are a
+// ring of t_new rows (a multiple of m), so the block's m rows are contiguous
+// from row first % t_new. `ok` is false when nothing is to be written.
+struct BlockGeo {
+    bool ok;
+    int64_t tok0, first, entry;
+};
+__device__ __forceinline__ BlockGeo block_geo(const CompressPlan &p, int j, int b, int m) {
+    BlockGeo g;
+    if (!p.block_end) {
+        g.ok = true;
+        g.tok0 = (int64_t)j * m;
+        g.first = p.pos0 + g.tok0;
+        g.entry = p.pos0 / m + j;
+        return g;
+    }
+    const int64_t t = p.block_end[b];
+    g.ok = t >= m - 1 && (t + 1) % m == 0;
+    g.first = g.ok ? t + 1 - m : 0;
+    g.tok0 = g.first % p.t_new;
+    g.entry = g.first / m;
+    // a linear store (or the indexer store) must hold the entry
+    if ((p.has_kv && p.k.ring == 0 && (g.entry >= p.k.rows || g.entry >= p.v.rows)) ||
+        (p.has_ik && g.entry >= p.ik.rows))
+        g.ok = false;
+    return g;
+}
+
 // Encode one float32 row held across the wave (nope dims lane + 64*i, rope
 // pair `lane` for lanes < 32) into a KV store row.
 __device__ void store_kv_row(const KvView &s, int b, int64_t row, const float *nope, int n_nope_it,
@@ -111,11 +142,12 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
     const int b = blockIdx.y;
     const int role = blockIdx.z;
     const int m = p.m;
-    const int64_t tok0 = (int64_t)j * m;                 // first raw token of the block (chunk-relative)
-    const int64_t entry = p.pos0 / m + j;
+    const BlockGeo geo = block_geo(p, j, b, m);
+    const int64_t tok0 = geo.tok0;                       // first raw row of the block
+    const int64_t entry = geo.entry;
     // A ring store keeps only the last `ring` entries written by one call.
     const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
-    if (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik) return;  // uniform per workgroup
+    if (!geo.ok || (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik)) return;  // uniform per workgroup
 
     // alpha_r = softmax_r(gate + pos_bias), float64
     double zmax = -__builtin_inf();
@@ -153,7 +185,7 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
                 *y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
                 if (role == 0) {
                     double sn, cs, xr, yr;
-                    rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                    rope_sincos((double)(geo.first + r) * f, &sn, &cs);
                     rope_rotate(*x, *y, sn, cs, &xr, &yr);
                     *x = xr;
                     *y = yr;
@@ -220,10 +252,11 @@ template <int ACT, int M>
 __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
     const int lane = lane_id(), role = threadIdx.x >> 6;
     const int j = blockIdx.x, b = blockIdx.y;
-    const int64_t tok0 = (int64_t)j * M;
-    const int64_t entry = p.pos0 / M + j;
+    const BlockGeo geo = block_geo(p, j, b, M);
+    const int64_t tok0 = geo.tok0;
+    const int64_t entry = geo.entry;
     const bool do_kv = p.has_kv && (p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring);
-    if (role < 2 ? !do_kv : !p.has_ik) return;  // uniform per wave
+    if (!geo.ok || (role < 2 ? !do_kv : !p.has_ik)) return;  // uniform per wave
     const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
     const int dI = p.dI;
     const int width = role < 2 ? D : dI;
@@ -283,7 +316,7 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
             if (rl) {
                 if (role == 0) {
                     double sn, cs, xr, yr;
-                    rope_sincos((double)(p.pos0 + tok0) * f, &sn, &cs);
+                    rope_sincos((double)geo.first * f, &sn, &cs);
                     rope_rotate((double)bits_val<ACT>(xa[0]), (double)bits_val<ACT>(xb[0]), sn, cs, &xr, &yr);
                     rx = (float)xr;
                     ry = (float)yr;
@@ -307,7 +340,7 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
                     double x = (double)bits_val<ACT>(xa[r]), y = (double)bits_val<ACT>(xb[r]);
                     if (role == 0) {
                         double sn, cs, xr, yr;
-                        rope_sincos((double)(p.pos0 + tok0 + r) * f, &sn, &cs);
+                        rope_sincos((double)(geo.first + r) * f, &sn, &cs);
                         rope_rotate(x, y, sn, cs, &xr, &yr);
                         x = xr;
                         y = yr;
@@ -341,6 +374,146 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
     }
 }
 
+// ------------------------------------------------------------ variants ----
+// The compressor variants of v4a_pool_variant: overlapping windows of 2m,
+// RoPE applied after pooling, one gate per token and channel. One wave per
+// (block, batch element, output), as compress_kernel, with the same float64
+// arithmetic and float32 rounding before encoding.
+
+constexpr int MAX_VAR_WINDOW = 1024;  // tokens one entry pools (2m for overlapping windows)
+
+// sum over window tokens r0 .. n-1 of w(r) * x(r) in float64, four partial sums
+template <class Wf, class Xf>
+__device__ __forceinline__ double pool_window(int r0, int n, Wf w, Xf x) {
+    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+    int r = r0;
+    for (; r + 4 <= n; r += 4) {
+        a0 += w(r) * x(r);
+        a1 += w(r + 1) * x(r + 1);
+        a2 += w(r + 2) * x(r + 2);
+        a3 += w(r + 3) * x(r + 3);
+    }
+    for (; r < n; ++r) a0 += w(r) * x(r);
+    return (a0 + a1) + (a2 + a3);
+}
+
+template <int ACT, int VAR>
+__global__ __launch_bounds__(64) void compress_var_kernel(CompressPlan p) {
+    __shared__ double alpha[MAX_VAR_WINDOW];
+    const int lane = lane_id();
+    const int j = blockIdx.x, b = blockIdx.y, role = blockIdx.z;
+    const int m = p.m;
+    const BlockGeo geo = block_geo(p, j, b, m);
+    const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
+    if (!geo.ok || (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik)) return;  // uniform per workgroup
+    const bool overlap = VAR == V4A_POOL_OVERLAP;
+    const int wm = overlap ? 2 * m : m;                          // tokens of the window
+    const int64_t wpos0 = overlap ? geo.first - m : geo.first;   // position of window token 0
+    const int r0 = wpos0 < 0 ? (int)-wpos0 : 0;                  // tokens before position 0 take no part
+    // raw rows of batch element b: a linear chunk (positions from pos0, or from pos0 - m for
+    // overlapping windows) or, in block mode, a ring of t_new rows indexed by position
+    const int64_t rows_b = p.block_end ? p.t_new : p.t_new + (overlap ? m : 0);
+    auto row = [&](int r) -> int64_t { return p.block_end ? (wpos0 + r) % p.t_new : (int64_t)j * m + r; };
+    const int C = p.gate_c;
+
+    if (VAR != V4A_POOL_CHANNEL_GATE) {
+        // alpha_r = softmax over the window of (gate + pos_bias[r]), float64
+        double zmax = -__builtin_inf();
+        for (int r = r0 + lane; r < wm; r += 64) {
+            const double z = (double)p.gate[(int64_t)b * rows_b + row(r)] + (double)p.pos_bias[r];
+            alpha[r] = z;
+            zmax = z > zmax ? z : zmax;
+        }
+        zmax = wave_max(zmax);
+        double zsum = 0.0;
+        for (int r = r0 + lane; r < wm; r += 64) {
+            const double e = exp(alpha[r] - zmax);
+            alpha[r] = e;
+            zsum += e;
+        }
+        zsum = wave_sum(zsum);
+        for (int r = r0 + lane; r < wm; r += 64) alpha[r] = alpha[r] / zsum;
+        __syncthreads();
+    }
+    // pooled value of channel c (gate column c) of the rows given by x(r)
+    auto pooled_ch = [&](int c, auto x) -> double {
+        if (VAR != V4A_POOL_CHANNEL_GATE) return pool_window(r0, wm, [&](int r) { return alpha[r]; }, x);
+        double zmax = -__builtin_inf();
+        for (int r = r0; r < wm; ++r) {
+            const double z = (double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c];
+            zmax = z > zmax ? z : zmax;
+        }
+        double zsum = 0.0;
+        for (int r = r0; r < wm; ++r)
+            zsum += exp((double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c] - zmax);
+        return pool_window(r0, wm, [&](int r) {
+            return exp((double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c] - zmax) / zsum;
+        }, x);
+    };
+
+    if (role < 2) {
+        const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
+        const void *src = role == 0 ? p.raw_k : p.raw_v;
+        const int cbase = role == 0 ? 0 : D;  // gate column of dim 0 of this output
+        float nope[4];
+        for (int i = 0; i < nit; ++i) {
+            const int d = lane + 64 * i;
+            nope[i] = (float)pooled_ch(cbase + d, [&](int r) { return load_act<ACT>(src, ((int64_t)b * rows_b + row(r)) * D + d); });
+        }
+        float rx = 0.0f, ry = 0.0f;
+        if (lane < ROPE_PAIRS) {
+            const double f = p.inv_freq[lane];
+            const bool rot_each = role == 0 && VAR != V4A_POOL_ROPE_AFTER;  // keys rotated at each token's position
+            auto pair = [&](int r, double *x, double *y) {
+                const int64_t base = ((int64_t)b * rows_b + row(r)) * D + Dn + 2 * lane;
+                *x = load_act<ACT>(src, base);
+                *y = load_act<ACT>(src, base + 1);
+                if (rot_each) {
+                    double sn, cs, xr, yr;
+                    rope_sincos((double)(wpos0 + r) * f, &sn, &cs);
+                    rope_rotate(*x, *y, sn, cs, &xr, &yr);
+                    *x = xr;
+                    *y = yr;
+                }
+            };
+            double px = pooled_ch(cbase + Dn + 2 * lane, [&](int r) { double x, y; pair(r, &x, &y); return x; });
+            double py = pooled_ch(cbase + Dn + 2 * lane + 1, [&](int r) { double x, y; pair(r, &x, &y); return y; });
+            if (role == 0 && VAR == V4A_POOL_ROPE_AFTER) {
+                // the pooled key rotated once, at the block's last position
+                double sn, cs, xr, yr;
+                rope_sincos((double)(geo.first + m - 1) * f, &sn, &cs);
+                rope_rotate(px, py, sn, cs, &xr, &yr);
+                px = xr;
+                py = yr;
+            }
+            rx = (float)px;
+            ry = (float)py;
+        }
+        const KvView &dst = role == 0 ? p.k : p.v;
+        store_kv_row(dst, b, kv_row(dst, geo.entry), nope, nit, rx, ry);
+    } else {
+        const int dI = p.dI, nit = dI / 64 + (dI % 64 ? 1 : 0);
+        const int cbase = p.has_kv ? 2 * p.D : 0;
+        for (int i = 0; i < nit; ++i) {
+            const int d = lane + 64 * i;
+            const bool on = d < dI;
+            const double acc = on ? pooled_ch(cbase + d, [&](int r) {
+                return load_act<ACT>(p.raw_ik, ((int64_t)b * rows_b + row(r)) * dI + d);
+            }) : 0.0;
+            store_ik_value(p.ik, b, geo.entry, d, on, (float)acc);
+        }
+    }
+}
+
+template <int ACT>
+static void launch_variant(const CompressPlan &p, dim3 g3, hipStream_t s) {
+    switch (p.variant) {
+        case V4A_POOL_OVERLAP: hipLaunchKernelGGL((compress_var_kernel<ACT, V4A_POOL_OVERLAP>), g3, dim3(64), 0, s, p); break;
+        case V4A_POOL_ROPE_AFTER: hipLaunchKernelGGL((compress_var_kernel<ACT, V4A_POOL_ROPE_AFTER>), g3, dim3(64), 0, s, p); break;
+        default: hipLaunchKernelGGL((compress_var_kernel<ACT, V4A_POOL_CHANNEL_GATE>), g3, dim3(64), 0, s, p); break;
+    }
+}
+
 template <int ACT>
 static void launch_small(const CompressPlan &p, dim3 grid, hipStream_t s) {
     switch (p.m) {
@@ -352,9 +525,13 @@ static void launch_small(const CompressPlan &p, dim3 grid, hipStream_t s) {
 }
 
 hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
-    dim3 grid(p.t_new / p.m, p.B);
+    dim3 grid(p.block_end ? 1 : p.t_new / p.m, p.B);  // block mode: one block per batch element
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
-    if (p.m <= SMALL_M) {
+    if (p.variant != V4A_POOL_BLOCK) {
+        const dim3 g3(grid.x, grid.y, 3);  // K, V, indexer key
+        if (p.act == 0) launch_variant<0>(p, g3, s);
+        else launch_variant<1>(p, g3, s);
+    } else if (p.m <= SMALL_M) {
         if (p.act == 0) launch_small<0>(p, grid, s);
         else launch_small<1>(p, grid, s);
     } else {

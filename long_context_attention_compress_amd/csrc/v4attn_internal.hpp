@@ -36,6 +36,11 @@ struct IkView {
 struct CompressPlan {
     int B, t_new, m, act;  // act: 0 f32, 1 bf16
     int64_t pos0;
+    // block mode: device positions [B] of the last token of the block to write
+    // (the raw inputs are rings of t_new rows); null: the chunk at pos0
+    const int64_t *block_end;
+    int variant;      // v4a_pool_variant
+    int gate_c;       // channel gates: logits per token (0 otherwise)
     int D, dI;
     int has_kv, has_ik;
     const void *raw_k, *raw_v, *raw_ik;

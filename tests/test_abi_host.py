@@ -249,3 +249,31 @@ def test_index_noalloc_rejections():
     assert lib.lightning_index_topk_workspace(ctypes.byref(big)) > _abi.NOALLOC_SCRATCH_BYTES
     r, msg = _status('lightning_index_topk_noalloc', ctypes.byref(big), None)
     assert r == _abi.V4A_EWORKSPACE and 'static scratch' in msg, (r, msg)
+
+
+def test_compress_block_mode_rejections():
+    """Block mode (device positions) needs pos0 == 0, a raw ring of at least m rows and an
+    8-byte aligned position array; a linear store's rows are checked on the device then."""
+    k, v = _kv(rows=16), _kv(rows=16)
+
+    def args(**kw):
+        a = _abi.CompressArgs()
+        a.B, a.t_new, a.pos0, a.m, a.act_fmt, a.rope_base = 2, 8, 0, 4, _abi.ACT_BF16, 1e4
+        a.raw_k = a.raw_v = a.gate = a.pos_bias = FAKE
+        a.k_out, a.v_out = ctypes.pointer(k), ctypes.pointer(v)
+        a.block_end = FAKE
+        for n, val in kw.items():
+            setattr(a, n, val)
+        return ctypes.byref(a)
+
+    for kw, want in [(dict(pos0=4), _abi.V4A_EINVAL), (dict(t_new=0), _abi.V4A_EINVAL), (dict(block_end=FAKE + 4),
+                     _abi.V4A_EALIGN)]:
+        r, msg = _status('csa_compress', args(**kw), None)
+        assert r == want, (kw, r, msg)
+    a = _abi.CompressArgs()
+    a.B, a.t_new, a.pos0, a.m, a.act_fmt, a.rope_base = 2, 4, 0, 8, _abi.ACT_BF16, 1e4
+    a.raw_k = a.raw_v = a.gate = a.pos_bias = FAKE
+    a.k_out, a.v_out = ctypes.pointer(k), ctypes.pointer(v)
+    a.block_end = FAKE
+    r, msg = _status('csa_compress', ctypes.byref(a), None)
+    assert r == _abi.V4A_EINVAL, (r, msg)      # t_new = 4 is not a multiple of m = 8

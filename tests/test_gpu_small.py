@@ -16,8 +16,8 @@ from oracle import compress as OC
 from oracle import formats as F
 from oracle import indexer as OI
 from oracle import model as OM
-from tests.helpers import (TOL_BF16, TOL_F32, assert_close_rms, assert_codes_e4m3, assert_topk, bf16_dev, dev,
-                           host_ik, host_kv, ik_store, kv_store, ring_rows)
+from tests.helpers import (TOL_BF16, TOL_F32, assert_close_rms, assert_codes_e4m3, assert_ik_rows, assert_kv_rows,
+                           assert_topk, bf16_dev, dev, host_ik, host_kv, ik_store, kv_planes, kv_store, ring_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -86,6 +86,134 @@ def test_compress_fp8_mxfp4(m, pos0, T):
     gi = host_ik(iks)
     assert np.array_equal(gi['e8m0'][:, e0:e0 + ne], scales)
     assert np.array_equal(gi['e2m1'][:, e0:e0 + ne], packed)
+
+
+@pytest.mark.parametrize('m', [1, 4, 128])
+def test_compress_block_mode_device_positions(m):
+    """Block mode: each batch element's block ends at a device position, raw inputs are a
+    ring of 2m rows indexed by position. b0's block sits in the ring's second half (a large
+    position), b1's position does not end a block (nothing written; for m = 1 every position
+    does), b2 writes entry 0. Bitwise equal to the linear-mode call on the same rows."""
+    B, D, dI = 3, 192, 128
+    R = 2 * m
+    raw = synth.raw_tokens(300 + m, B, R, D, m, dI if m == 4 else 0, bf16=True)
+    ends = np.array([m * 1002 - 1, m * 500 + m // 2, m - 1], np.int64)
+    ring = 128 if m == 1 else 0
+    rows = 128 if m == 1 else 1100
+
+    def stores():
+        st = [v4.KVStore.empty(B, rows, D, ring=ring) for _ in range(2)]
+        for x in st:
+            x.nope.fill_(0x5A)
+            x.rope.fill_(0x5A5A)
+            x.scale.fill_(-7.0)
+        ik = v4.IKStore.empty(B, rows, dI) if m == 4 else None
+        if ik is not None:
+            ik.e2m1.fill_(0xA5)
+            ik.e8m0.fill_(0x33)
+        return st[0], st[1], ik
+
+    rk, rv = bf16_dev(raw['raw_k']), bf16_dev(raw['raw_v'])
+    ru = bf16_dev(raw['raw_ik']) if m == 4 else None
+    gate, bias = dev(raw['gate']), dev(raw['pos_bias'])
+    k1, v1, i1 = stores()
+    print(f'compress block mode m={m}', flush=True)
+    v4.csa_compress(gate, bias, 0, rk, rv, k1, v1, ru, i1, block_end=dev(ends))
+    k2, v2, i2 = stores()
+    sl = lambda x, b: None if x is None else x[b:b + 1]
+    for b in range(B):
+        t = int(ends[b])
+        if (t + 1) % m:
+            continue
+        first = t + 1 - m
+        r0 = first % R
+        one = lambda st: None if st is None else (
+            v4.KVStore(st.fmt, st.dim, st.ring, nope=sl(st.nope, b), rope=sl(st.rope, b), scale=sl(st.scale, b))
+            if isinstance(st, v4.KVStore) else v4.IKStore(st.fmt, st.dim, e2m1=sl(st.e2m1, b), e8m0=sl(st.e8m0, b)))
+        v4.csa_compress(gate[b:b + 1, r0:r0 + m].contiguous(), bias, first, rk[b:b + 1, r0:r0 + m].contiguous(),
+                        rv[b:b + 1, r0:r0 + m].contiguous(), one(k2), one(v2),
+                        None if ru is None else ru[b:b + 1, r0:r0 + m].contiguous(), one(i2))
+    torch.cuda.synchronize()
+    for a, c in ((k1, k2), (v1, v2)):
+        assert torch.equal(a.nope, c.nope) and torch.equal(a.rope, c.rope)
+        assert torch.equal(a.scale.view(torch.int32), c.scale.view(torch.int32))
+    if m == 4:
+        assert torch.equal(i1.e2m1, i2.e2m1) and torch.equal(i1.e8m0, i2.e8m0)
+    if m > 1:
+        assert torch.all(k1.nope[1] == 0x5A), 'a position inside a block wrote an entry'
+
+
+VARIANT_CASES = [('overlap', 4, 0), ('overlap', 4, 1024), ('overlap', 128, 131072), ('rope_after_pool', 4, 1000),
+                 ('rope_after_pool', 128, 131072), ('channel_gate', 4, 1024), ('channel_gate', 128, 0)]
+
+
+@pytest.mark.parametrize('variant,m,pos0', VARIANT_CASES)
+def test_compress_variants(variant, m, pos0):
+    """Each compressor variant against the oracle's reading of it, every plane of K, V and
+    (for m = 4) the MXFP4 indexer key: overlapping windows (including the first entry, whose
+    block before does not exist), RoPE after pooling, per-channel gates."""
+    B, D, dI = 2, 192, 128
+    T = 8 * m
+    enum = {'overlap': v4.POOL_OVERLAP, 'rope_after_pool': v4.POOL_ROPE_AFTER, 'channel_gate': v4.POOL_CHANNEL_GATE}
+    with_ik = m == 4
+    extra = m if variant == 'overlap' else 0
+    raw = synth.raw_tokens(400 + m, B, T + extra, D, m, dI if with_ik else 0, bf16=True, prefix=f'var/{variant}')
+    C = 2 * D + (dI if with_ik else 0)
+    if variant == 'channel_gate':
+        gate = synth.normal(401, f'var/cg/{m}', (B, T, C))
+        bias = synth.normal(402, f'var/cb/{m}', (m, C), 0.1)
+    else:
+        gate = raw['gate']
+        bias = synth.normal(403, f'var/b/{variant}/{m}', (2 * m if variant == 'overlap' else m,), 0.1)
+    rows = (pos0 + T) // m
+    ks, vs = v4.KVStore.empty(B, rows, D), v4.KVStore.empty(B, rows, D)
+    iks = v4.IKStore.empty(B, rows, dI) if with_ik else None
+    print(f'compress variant {variant} m={m} pos0={pos0}', flush=True)
+    v4.csa_compress(dev(gate), dev(bias), pos0, bf16_dev(raw['raw_k']), bf16_dev(raw['raw_v']), ks, vs,
+                    bf16_dev(raw['raw_ik']) if with_ik else None, iks, variant=enum[variant])
+    torch.cuda.synchronize()
+    k32, v32, u32 = OC.compress_variant(variant, raw['raw_k'], raw['raw_v'], gate, bias, pos0,
+                                        raw_ik=raw['raw_ik'] if with_ik else None)
+    new = np.arange(pos0 // m, pos0 // m + T // m)
+    for b in range(B):
+        n = assert_kv_rows(*kv_planes(ks, b, new), k32[b], f'{variant} K b{b}')
+        n += assert_kv_rows(*kv_planes(vs, b, new), v32[b], f'{variant} V b{b}')
+        if with_ik:
+            n += assert_ik_rows(iks.e2m1[b, new[0]:].cpu().numpy(), iks.e8m0[b, new[0]:].cpu().numpy(), u32[b],
+                                f'{variant} indexer key b{b}')
+        print(f'[planes] {variant} m={m} b{b}: {n} boundary differences', flush=True)
+
+
+def test_compress_overlap_block_mode():
+    """Overlapping windows in block mode: a raw ring of 2m rows indexed by position, the
+    block ending at a device position; b0 at a large position, b1 the first entry (no
+    block before it), equal bitwise to the linear call on the same window."""
+    B, D, dI, m = 2, 192, 128, 4
+    R = 2 * m
+    raw = synth.raw_tokens(410, B, R, D, m, dI, bf16=True, prefix='var/ring')
+    bias = dev(synth.normal(411, 'var/ring/b', (2 * m,), 0.1))
+    ends = np.array([4 * 2501 - 1, m - 1], np.int64)
+    rows = 2600
+    st = lambda: (v4.KVStore.empty(B, rows, D), v4.KVStore.empty(B, rows, D), v4.IKStore.empty(B, rows, dI))
+    k1, v1, i1 = st()
+    rk, rv, ru, g = bf16_dev(raw['raw_k']), bf16_dev(raw['raw_v']), bf16_dev(raw['raw_ik']), dev(raw['gate'])
+    v4.csa_compress(g, bias, 0, rk, rv, k1, v1, ru, i1, block_end=dev(ends), variant=v4.POOL_OVERLAP)
+    k2, v2, i2 = st()
+    for b in range(B):
+        first = int(ends[b]) + 1 - m
+        order = [(first - m + r) % R for r in range(2 * m)]          # window rows by position
+        one = lambda x: x[b:b + 1]
+        sub = lambda t: t[b:b + 1][:, order].contiguous()
+        v4.csa_compress(sub(g), bias, first, sub(rk), sub(rv),
+                        v4.KVStore(k2.fmt, D, 0, nope=one(k2.nope), rope=one(k2.rope), scale=one(k2.scale)),
+                        v4.KVStore(v2.fmt, D, 0, nope=one(v2.nope), rope=one(v2.rope), scale=one(v2.scale)),
+                        sub(ru), v4.IKStore(i2.fmt, dI, e2m1=one(i2.e2m1), e8m0=one(i2.e8m0)),
+                        variant=v4.POOL_OVERLAP)
+    torch.cuda.synchronize()
+    for a, c in ((k1, k2), (v1, v2)):
+        assert torch.equal(a.nope, c.nope) and torch.equal(a.rope, c.rope)
+        assert torch.equal(a.scale.view(torch.int32), c.scale.view(torch.int32))
+    assert torch.equal(i1.e2m1, i2.e2m1) and torch.equal(i1.e8m0, i2.e8m0)
 
 
 # ---------------------------------------------------------------- index ----
@@ -623,87 +751,6 @@ def test_empty_inputs():
         ro, rl = _oracle_attn(a, 0, 1, np.arange(0))
         assert_close_rms(o[0, 1], ro, TOL_BF16, f'{name} t=0')
         assert np.allclose(l[0, 1], rl, atol=2e-2), name
-
-
-def test_layer_stack_graph_replays():
-    """A decode step through a small stack (window-only, CSA, HCA, CSA; B = 2, 8,192
-    tokens of context), four steps captured in one HIP graph: three replays, with eager
-    work and synchronisations between them, each give outputs bitwise equal to the
-    eager steps (the block compression and the window appends rewrite the same rows)."""
-    B, T, D, H, HI, DI, K, W = 2, 8192, 192, 64, 64, 128, 256, 128
-    g = torch.Generator(device='cuda').manual_seed(61)
-    rn = lambda *sh: torch.randn(*sh, generator=g, device='cuda')
-    z1 = torch.zeros(1, device='cuda')
-    pos = torch.full((B, 1), T - 1, dtype=torch.int64, device='cuda')
-    s = torch.cuda.Stream()
-
-    def caches(m, ik):
-        n = T // m
-        ek, ev = v4.KVStore.empty(B, n, D), v4.KVStore.empty(B, n, D)
-        iks = v4.IKStore.empty(B, n, DI) if ik else None
-        v4.csa_compress(rn(B, T), rn(m) * 0.1, 0, rn(B, T, D).bfloat16(), rn(B, T, D).bfloat16(), ek, ev,
-                        rn(B, T, DI).bfloat16() if ik else None, iks)
-        wk, wv = v4.KVStore.empty(B, W, D, ring=W), v4.KVStore.empty(B, W, D, ring=W)
-        v4.csa_compress(torch.zeros(B, W, device='cuda'), z1, T - W, rn(B, W, D).bfloat16(), rn(B, W, D).bfloat16(),
-                        wk, wv)
-        return ek, ev, iks, wk, wv
-
-    iq_store = v4.IKStore.empty(1, B * HI, DI)
-    v4.csa_compress(torch.zeros(1, B * HI, device='cuda'), z1, 0, raw_ik=rn(1, B * HI, DI), ik_out=iq_store)
-    iq, iqs = iq_store.e2m1.reshape(B, 1, HI, DI // 2), iq_store.e8m0.reshape(B, 1, HI, DI // 32)
-    w = torch.rand(B, 1, HI, generator=g, device='cuda')
-    q = rn(B, 1, H, D).bfloat16()
-    nk, nv = rn(B, 1, D).bfloat16(), rn(B, 1, D).bfloat16()
-    bk, bv, bu, bg = rn(B, 4, D).bfloat16(), rn(B, 4, D).bfloat16(), rn(B, 4, DI).bfloat16(), rn(B, 4)
-    b4 = rn(4) * 0.1
-    idx = torch.zeros(B, 1, K, dtype=torch.int32, device='cuda')
-    wsi, wsa = v4.Workspace(), v4.Workspace()
-    layers, outs = [], []
-    with torch.cuda.stream(s):
-        for kind in ('win', 'csa', 'hca', 'csa'):
-            o = torch.zeros(B, 1, H, D, device='cuda')
-            outs.append(o)
-            if kind == 'csa':
-                ek, ev, iks, wk, wv = caches(4, True)
-                layers.append((v4.csa_compress(bg, b4, T - 4, bk, bv, ek, ev, bu, iks, prepare=True),
-                               [v4.lightning_index_topk(pos, iq, w, iks, K, 4, iq_scale=iqs, out_idx=idx,
-                                                        workspace=wsi, prepare=True),
-                                v4.sparse_window_attn(q, pos, ek, ev, 4, wk, wv, W, idx, o=o, workspace=wsa,
-                                                      prepare=True, append_k=nk, append_v=nv)]))
-            else:
-                ek, ev, _, wk, wv = caches(128, False)
-                win = kind == 'win'
-                layers.append((None, [v4.hca_attn(q, pos, None if win else ek, None if win else ev, 128, wk, wv, W,
-                                                  n_entries_override=0 if win else -1, o=o, workspace=wsa,
-                                                  prepare=True, append_k=nk, append_v=nv)]))
-
-    def steps():
-        for i in range(4):
-            for blk, run in layers:
-                if blk is not None and i == 3:
-                    blk()
-                for f in run:
-                    f()
-    print('layer stack: eager', flush=True)
-    with torch.cuda.stream(s):
-        steps()
-        steps()
-    torch.cuda.synchronize()
-    ref = [o.clone() for o in outs]
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=s):
-        steps()
-    for r in range(3):
-        for o in outs:
-            o.fill_(float('nan'))
-        print(f'layer stack: replay {r}', flush=True)
-        graph.replay()
-        torch.cuda.synchronize()
-        assert all(torch.equal(o, e) for o, e in zip(outs, ref)), f'replay {r}'
-        with torch.cuda.stream(s):   # eager work between replays
-            steps()
-        torch.cuda.synchronize()
-        assert all(torch.equal(o, e) for o, e in zip(outs, ref)), f'eager after replay {r}'
 
 
 def test_attn_bf16_output():
