@@ -55,17 +55,21 @@ struct KeyInfo {
     int64_t n_list;  // entries in the list
     int64_t n_win;   // window rows
     int64_t t;
+    int64_t wrow0;   // window-store row of the window's first key (position t - n_win + 1)
 };
 
 __device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int64_t t) {
     KeyInfo ki;
     ki.t = t;
+    ki.wrow0 = 0;
     if (ki.t < 0) {
         ki.n_list = 0;
         ki.n_win = 0;
         return ki;
     }
     ki.n_win = ki.t + 1 < p.W ? ki.t + 1 : p.W;
+    const int64_t pos0 = ki.t - ki.n_win + 1;
+    ki.wrow0 = p.wk.ring > 0 ? pos0 % p.wk.ring : pos0;
     if (!p.has_ent) ki.n_list = 0;
     else if (p.sparse) ki.n_list = p.k;
     else {
@@ -90,6 +94,26 @@ __device__ __forceinline__ int64_t key_row(const AttnPlan &p, int q, const KeyIn
     int64_t pos = ki.t - ki.n_win + 1 + w;
     int64_t row = p.wk.ring > 0 ? pos % p.wk.ring : pos;
     return row < p.wk.rows ? row : -1;
+}
+
+constexpr int32_t WIN_BIT = 1 << 30;  // a row code with this bit set is a window-store row
+
+// Row code of key j of the list: the store row, WIN_BIT set for a window row,
+// -1 for a slot without a key. `id` is the selected id when j is a sparse
+// list entry (unused otherwise). The same function serves the per-split rows
+// table and the rows of the first two tiles, which are resolved per lane.
+__device__ __forceinline__ int32_t key_code(const AttnPlan &p, const KeyInfo &ki, int64_t j, int32_t id) {
+    if (j < ki.n_list) {
+        const int64_t e = p.sparse ? (j < p.k ? (int64_t)id : -1) : j;
+        return (e >= 0 && e < p.ek.rows) ? (int32_t)e : -1;
+    }
+    const int64_t w = j - ki.n_list;
+    if (w >= ki.n_win) return -1;
+    // position t - n_win + 1 + w; its ring row without a division: w < n_win
+    // <= ring, so one wrap at most
+    int64_t row = ki.wrow0 + w;
+    if (p.wk.ring > 0 && row >= p.wk.ring) row -= p.wk.ring;
+    return row < p.wk.rows ? (int32_t)row | WIN_BIT : -1;
 }
 
 // ------------------------------------------------------------------ F32 ----
@@ -262,8 +286,6 @@ struct MxSmem {
     AppRow app;
 };
 
-constexpr int32_t WIN_BIT = 1 << 30;
-
 // A tile in flight: the raw loads and which of them hold a key. Slots without
 // a key are zeroed only when the tile is staged, so that issuing the next
 // tile's loads never waits for this one's data.
@@ -333,19 +355,17 @@ __device__ __forceinline__ const char *row_addr(const char *base, uint32_t row, 
     return base + (uint64_t)row * stride;
 }
 
-// Issue the loads of one 32-key tile. Branch-free within the tile: a slot
-// without a key reads row 0 of the window store (always present) and is
-// zeroed afterwards, so the compiler keeps every load of the tile in flight
-// together. A tile wholly past the split's end loads nothing.
-__device__ __forceinline__ void load_tile(const LaneSrc &L, const int32_t *rows, int rel, int n_rel, TileRegs &R,
-                                          int tid) {
-    if (rel >= n_rel) {  // uniform: a tile past the split's end is never computed
-        R.ok = false;
-        R.sok = false;
-        return;
-    }
-    const int r = tid >> 3;
-    const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
+// Issue the loads of one 32-key tile. Branch-free: a slot without a key
+// (also every slot of a tile past the split's end) reads row 0 of the window
+// store (always present; the same line for the whole wave, so a cache hit)
+// and is zeroed when staged. Every call issues the same five loads, so the
+// wait before staging a tile counts exactly the loads issued after it and
+// leaves the next tile's loads in flight; with a branch around the loads the
+// compiler can only wait for all of them.
+// `code`: row code of the lane's row, `cs`: of the key whose scale the lane
+// loads (threads 0..31: K scale of key tid, 32..63: V scale of key tid - 32;
+// -1 for the other threads).
+__device__ __forceinline__ void load_tile_codes(const LaneSrc &L, int32_t code, int32_t cs, TileRegs &R) {
     const bool ok = code >= 0;
     const bool win = !ok || (code & WIN_BIT);
     const uint32_t row = ok ? (uint32_t)(code & (WIN_BIT - 1)) : 0u;
@@ -354,14 +374,20 @@ __device__ __forceinline__ void load_tile(const LaneSrc &L, const int32_t *rows,
     R.vn = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.vwn, L.ven), row, pick(win, L.vwn_s, L.ven_s)));
     R.vr = __builtin_nontemporal_load((const v4i *)row_addr(pick(win, L.vwr, L.ver), row, pick(win, L.vwr_s, L.ver_s)));
     R.ok = ok;
-    // scales: threads 0..31 -> K scale of key tid, 32..63 -> V scale of key tid-32
-    const int rs = tid & (TK - 1);
-    const int32_t cs = (tid < 2 * TK && rel + rs < n_rel) ? rows[rel + rs] : -1;
     const bool oks = cs >= 0;
     const bool wins = !oks || (cs & WIN_BIT);
     const uint32_t rows_ = oks ? (uint32_t)(cs & (WIN_BIT - 1)) : 0u;
     R.sc = *(const float *)row_addr(pick(wins, L.sw, L.se), rows_, pick(wins, L.srw, L.sre));
     R.sok = oks;
+}
+
+// The same from the split's rows table (LDS).
+__device__ __forceinline__ void load_tile(const LaneSrc &L, const int32_t *rows, int rel, int n_rel, TileRegs &R,
+                                          int tid) {
+    const int r = tid >> 3, rs = tid & (TK - 1);
+    const int32_t code = rel + r < n_rel ? rows[rel + r] : -1;
+    const int32_t cs = (tid < 2 * TK && rel + rs < n_rel) ? rows[rel + rs] : -1;
+    load_tile_codes(L, code, cs, R);
 }
 
 template <bool HI>
@@ -398,7 +424,13 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *row
     store_codes(&sm.vb[r * KB_LD + 16 * part], vn);
     *(v4i *)&sm.kb[r * KB_LD + MDN + 8 * part] = kr;
     *(v4i *)&sm.vb[r * KB_LD + MDN + 8 * part] = vr;
-    const float sc = R.sok ? R.sc : 0.f;
+    // The empty asm makes the loaded scale opaque here, at staging time:
+    // without it the compiler folds this select into the branch that issued
+    // the load and waits for the load there, before the next tile's loads
+    // are issued.
+    float sc = R.sc;
+    asm volatile("" : "+v"(sc));
+    sc = R.sok ? sc : 0.f;
     if (tid < TK) {
         sm.ksc[tid] = sc;
         sm.kbias[tid] = (rel + tid < n_rel && rows[rel + tid] >= 0) ? 0.f : -__builtin_inff();
@@ -488,12 +520,48 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const bool active = wave < NW;
     const int head = 16 * wave + col;
     touch_args(p);  // every line of the plan in one scalar round trip
-    // the position (a pointer, then the value: the longest scalar chain of the
-    // prologue) is asked for first, ahead of everything below
-    const int64_t t_pos = p.q_pos[q];
+    // The position (a pointer, then the value: the longest chain of the
+    // prologue) is asked for first, as a vector load whose address the
+    // compiler cannot prove uniform, and read into a scalar only where it is
+    // first needed: that wait then leaves every load issued after it in
+    // flight. (A load known to be uniform is read into a scalar at once, with
+    // a wait for it right there; a scalar load's wait is shared with every
+    // later scalar-cache and LDS wait.)
+    int opaque_zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(opaque_zero));
+    const int64_t t_lane = p.q_pos[q + opaque_zero];
     __builtin_amdgcn_sched_barrier(0);
+    constexpr int IDS = MAX_KS / (AT * NS);
+    const int64_t j0 = (int64_t)split * p.keys_per_split;
+    // Id loads without per-lane branches (which would wait for each load in
+    // turn): clamped positions, a dense call reading a valid dummy address; the
+    // values are masked where they are used.
+    const int32_t *ip = p.id_src + q * p.id_stride;
+    const int64_t jmax = p.id_jmax;
+    // The stream's first two tiles are loaded before the rows table exists:
+    // each lane resolves the keys it needs itself (its row of each tile and,
+    // threads 0..63, the key whose scale it loads) from ids asked for first,
+    // so the tile loads leave as soon as the position is known.
+    const int ra = TK * stream + (tids >> 3), rb = ra + TK * NS;
+    const int sa = TK * stream + (tids & (TK - 1)), sb = sa + TK * NS;
+    int32_t fid[4];
+    {
+        const int rr[4] = {ra, rb, sa, sb};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t j = j0 + rr[u];
+            fid[u] = ip[j < jmax ? j : jmax];
+        }
+    }
+    // the stores' planes and this lane's load sources (plan fields only)
+    TileSrc src;
+    src.wk = planes_of(p.wk, b);
+    src.wv = planes_of(p.wv, b);
+    src.ek = p.has_ent ? planes_of(p.ek, b) : src.wk;
+    src.ev = p.has_ent ? planes_of(p.ev, b) : src.wv;
+    const LaneSrc lsrc = lane_src(src, tids);
     // RoPE frequency of pair `lane & 31` (the table below is built by lanes
-    // 0..31 of the first wave), asked for now so that it has arrived by then
+    // 0..31 of the first wave)
     const double ifreq = p.inv_freq[lane & 31];
     // The query and (sparse) this split's selected ids do not depend on the
     // query position: their loads are issued before the position arrives.
@@ -503,23 +571,25 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     for (int c = 0; c < 4; ++c) qn[c] = ld16(qp + 32 * c + 8 * g);
 #pragma unroll
     for (int c = 0; c < 2; ++c) qraw[c] = ld16(qp + MDN + 32 * c + 8 * g);
-    constexpr int IDS = MAX_KS / (AT * NS);
-    const int64_t j0 = (int64_t)split * p.keys_per_split;
-    // Id loads without per-lane branches (which would wait for each load in
-    // turn): clamped positions, a dense call reading a valid dummy address; the
-    // values are masked where they are used.
-    const int32_t *ip = p.id_src + q * p.id_stride;
-    const int64_t jmax = p.id_jmax;
     int32_t ids[IDS];
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
         const int64_t j = j0 + tid + AT * NS * u;
         ids[u] = ip[j < jmax ? j : jmax];
     }
+    const int64_t t_pos = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(t_lane >> 32)) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readfirstlane((int)t_lane));
     const KeyInfo ki = key_info(p, t_pos);
     const int64_t n_keys = ki.n_list + ki.n_win;
     const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
     const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
+    TileRegs RA, RB;
+    {
+        auto first = [&](int rel, int32_t id) { return rel < n_rel ? key_code(p, ki, j0 + rel, id) : -1; };
+        const bool sl = tids < 2 * TK;  // threads 0..63 load the scales
+        load_tile_codes(lsrc, first(ra, fid[0]), sl ? first(sa, fid[2]) : -1, RA);
+        load_tile_codes(lsrc, first(rb, fid[1]), sl ? first(sb, fid[3]) : -1, RB);
+    }
     // Fused window append: the token's own key is the last of the list (the
     // window row at t). The workgroup whose split holds it reads the token's
     // raw K and V rows, one 32-bit word (two BF16 values) per lane of its last
@@ -534,22 +604,12 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         const uint32_t *rv = (const uint32_t *)(p.app_v + (size_t)q * MD);
         araw = aw == 0 ? rk[lane] : aw == 1 ? rv[lane] : lane < 32 ? rk[MDN / 2 + lane] : rv[MDN / 2 - 32 + lane];
     }
-    // resolve the split's keys to store rows once, and the RoPE table
+    // resolve the split's keys to store rows once (later tiles, the staging
+    // masks), and the RoPE table
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
         const int i = tid + AT * NS * u;
-        if (i < n_rel) {
-            const int64_t j = j0 + i;
-            int64_t row;
-            bool win = false;
-            if (j < ki.n_list) {
-                const int64_t e = p.sparse ? (j < p.k ? (int64_t)ids[u] : -1) : j;
-                row = (e >= 0 && e < p.ek.rows) ? e : -1;
-            } else {
-                row = key_row(p, q, ki, j, &win);
-            }
-            sm.rows[i] = row < 0 ? -1 : (int32_t)row | (win ? WIN_BIT : 0);
-        }
+        if (i < n_rel) sm.rows[i] = key_code(p, ki, j0 + i, ids[u]);
     }
     if (tid < ROPE_PAIRS) {
         double sn, cs;
@@ -593,14 +653,8 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
 
     // two-stage pipeline: tile t+2 is loaded while tile t is staged and computed
     const int n_tiles = (n_rel + TK - 1) / TK;
-    TileSrc src;
-    src.wk = planes_of(p.wk, b);
-    src.wv = planes_of(p.wv, b);
-    src.ek = p.has_ent ? planes_of(p.ek, b) : src.wk;
-    src.ev = p.has_ent ? planes_of(p.ev, b) : src.wv;
-    const LaneSrc lsrc = lane_src(src, tids);
-    // Every tile load is issued unconditionally (a tile past the end reads
-    // window row 0 and is never staged), and the loop is unrolled by two, so
+    // Two tiles' loads are in flight per stream (a tile past the split's end
+    // loads nothing and is staged empty), and the loop is unrolled by two, so
     // the wait before staging tile t only covers tile t's loads and tile t+1's
     // stay in flight.
     auto compute = [&](const TileBuf &tb) {
@@ -681,9 +735,6 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // stream s: tiles s + NS i; every stream runs the same number of rounds
     // (a round past its last tile stages an empty tile and skips the compute)
     const int n_rounds = (n_tiles + NS - 1) / NS;
-    TileRegs RA, RB;
-    load_tile(lsrc, sm.rows, TK * stream, n_rel, RA, tids);
-    load_tile(lsrc, sm.rows, TK * (stream + NS), n_rel, RB, tids);
     // The workgroup holding the appended key encodes the row while the first
     // tiles are in flight (the barrier before the first staging publishes it).
     int cur = -1;
@@ -737,18 +788,30 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     stage_tile(RA, sm.rows, b0, stream * TK, n_rel, tids, sm.app, cur);
     load_tile(lsrc, sm.rows, (stream + 2 * NS) * TK, n_rel, RA, tids);
     __syncthreads();
-    for (int i = 0; i < n_rounds; i += 2) {
+    // The loop runs whole pairs of rounds and has no exit but its own test:
+    // an exit from inside would join the loop's paths in one block, where the
+    // compiler has to assume that the tile staged first is the newest load
+    // and waits for every load in flight. The last one or two rounds follow.
+    int i = 0;
+    for (; i + 2 < n_rounds; i += 2) {
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         if (ta < n_tiles) compute(b0);
-        if (i + 1 >= n_rounds) break;
         stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur);
         load_tile(lsrc, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
         __syncthreads();
         if (tb_ < n_tiles) compute(b1);
-        if (i + 2 >= n_rounds) break;
         stage_tile(RA, sm.rows, b0, (ta + 2 * NS) * TK, n_rel, tids, sm.app, cur);
         load_tile(lsrc, sm.rows, (ta + 4 * NS) * TK, n_rel, RA, tids);
         __syncthreads();
+    }
+    if (i < n_rounds) {  // uniform
+        const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
+        if (ta < n_tiles) compute(b0);
+        if (i + 1 < n_rounds) {
+            stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur);
+            __syncthreads();
+            if (tb_ < n_tiles) compute(b1);
+        }
     }
     if (NS > 1) {
         // the other streams hand their (max, sum, O) to stream 0 through the tile buffers

@@ -546,20 +546,23 @@ def test_attn_many_query_head_pairs_combine():
                 assert_close_rms(o[b, i], ro, TOL_BF16, f'{name} b{b} i{i}')
 
 
-def test_attn_dense_two_streams():
-    """A key list long enough (>= 4096 with the window) for the two-stream
-    workgroups, with queries that see all entries, part of them, and almost
-    none (ragged and empty tiles in both streams)."""
-    B, Tq, rows, m = 1, 3, 6000, 4
+@pytest.mark.parametrize('Tq', [3, 70])
+def test_attn_dense_long_list(Tq):
+    """A key list of more than 4096 keys with the window (two key streams per
+    workgroup), with queries that see all entries, part of them, and almost none
+    (ragged and empty tiles in both streams); 3 queries (many splits each) and 70
+    (fewer splits per query)."""
+    B, rows, m = 1, 6000, 4
     H, D = 64, 192
-    q_pos = np.array([[rows * m - 1, 9001, 130]], np.int64)
+    base = [rows * m - 1, 9001, 130]
+    q_pos = np.array([[base[i % 3] - 7 * (i // 3) for i in range(Tq)]], np.int64)
     c = _attn_case(13, B, Tq, H, D, rows, q_pos, 'fp8')
     ek, ev, wk, wv = _stores(c)
-    print('attn dense two streams', flush=True)
+    print(f'attn dense long list, {Tq} queries', flush=True)
     o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, c['W'])
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
-    for i in range(Tq):
+    for i in sorted({0, 1, 2, Tq - 1, Tq // 2}):
         t = int(q_pos[0, i])
         n = min((t + 1) // m, rows)
         ro, _ = _oracle_attn(c, 0, i, np.arange(n))
