@@ -365,8 +365,9 @@ __device__ __forceinline__ void score_chunk(const IndexPlan &p, int q, int b, in
 // from the highest bit in which the chunk's keys differ, so the bins follow
 // the keys' actual range; the bin holding the s-th largest key is refined by
 // further digits only while the entries at or above its edge are more than a
-// merge thread group takes in registers (EMIT_SOFT). Entries are written in
-// index order with the threshold as the region's lower bound.
+// merge thread group takes in registers (EMIT_SOFT), or than twice s where s
+// exceeds that. Entries are written in index order with the threshold as the
+// region's lower bound.
 constexpr int EBITS = 11;
 constexpr int EBINS = 1 << EBITS;
 constexpr int EMIT_SOFT = 32;  // = GROUP * REG_CAND of the merge (static_assert there)
@@ -433,6 +434,12 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
         if (diff == 0u) {
             thr = mx;  // every valid key equal: all of them reach it
         } else {
+            // refine while more than `soft` would be emitted: EMIT_SOFT (what a
+            // merge thread group takes) or, where every chunk must emit more than
+            // that anyway (many chunks per query: chunked prefill), twice the
+            // share; never more than the region holds
+            uint32_t soft = 2u * (uint32_t)s_want > (uint32_t)EMIT_SOFT ? 2u * (uint32_t)s_want : (uint32_t)EMIT_SOFT;
+            soft = soft < (uint32_t)p.region_cap ? soft : (uint32_t)p.region_cap;
             int top = 31 - __builtin_clz(diff);  // highest differing bit; bits above it are common
             uint32_t prefix = (uint32_t)(((uint64_t)mx >> (top + 1)) << (top + 1));
             uint32_t need = (uint32_t)s_want, above_all = 0;
@@ -470,7 +477,7 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
                 prefix |= bin << sh;
                 above_all += above;
                 need -= above;
-                if (above_all + pop <= (uint32_t)EMIT_SOFT || sh == 0) break;
+                if (above_all + pop <= soft || sh == 0) break;
                 // refine inside the bin: clear it for the next digit
                 __syncthreads();  // every thread has read res and its bins
                 *(uint4 *)&em.hist[8 * tid] = make_uint4(0, 0, 0, 0);
