@@ -132,7 +132,10 @@ IndexLayout index_layout(const v4a_index_args *a) {
     IndexLayout L;
     const int64_t Q = (int64_t)a->B * a->Tq;
     const int64_t rows = a->keys->rows;
-    L.chunk = IDX_CHUNK;
+    // several queries per sequence over more than one sub-chunk (chunked
+    // prefill, drafts): a chunk of IDX_CPW sub-chunks per workgroup (MXFP4 keys)
+    const bool multi = a->keys->fmt != V4A_IK_F32 && a->Tq > 1 && rows > IDX_CHUNK;
+    L.chunk = multi ? IDX_CHUNK * IDX_CPW : IDX_CHUNK;
     L.n_chunks = (int)std::max<int64_t>(1, (rows + L.chunk - 1) / L.chunk);
     L.s_local = 2 * ((a->k + L.n_chunks - 1) / L.n_chunks) + 8;
     // a multiple of 4 slots and at least 32: the merge reads a region's first

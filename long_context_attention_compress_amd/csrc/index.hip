@@ -395,14 +395,22 @@ __device__ __forceinline__ uint32_t emit_scan(uint32_t v, EmitSmem &em, uint32_t
     return x - v + before;
 }
 
+// PER: entries per thread, in index order (the chunk holds IT x PER).
+template <int PER>
 __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
                            const uint32_t *skey, EmitSmem &em) {
+    static_assert(PER % 4 == 0, "whole 16-byte LDS reads per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t rid = (size_t)q * p.n_chunks + chunk;
-    constexpr int PER = IDX_CHUNK / IT;  // entries per thread, in index order
-    static_assert(PER == 4, "one 16-byte LDS read per thread");
-    const uint4 k4 = *(const uint4 *)&skey[PER * tid];
-    const uint32_t key[PER] = {k4.x, k4.y, k4.z, k4.w};
+    uint32_t key[PER];
+#pragma unroll
+    for (int v = 0; v < PER / 4; ++v) {
+        const uint4 k4 = *(const uint4 *)&skey[PER * tid + 4 * v];
+        key[4 * v] = k4.x;
+        key[4 * v + 1] = k4.y;
+        key[4 * v + 2] = k4.z;
+        key[4 * v + 3] = k4.w;
+    }
     bool valid[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) valid[j] = PER * tid + j < cnt;
@@ -533,8 +541,8 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
     for (int d = 3; d >= 0; --d) {
         for (int i = tid; i < 256; i += NT) sm.hist[i] = 0;
         __syncthreads();
-        for (int64_t c0 = 0; c0 < nvis; c0 += p.chunk) {
-            const int cnt = (int)((nvis - c0) < p.chunk ? (nvis - c0) : p.chunk);
+        for (int64_t c0 = 0; c0 < nvis; c0 += IDX_CHUNK) {
+            const int cnt = (int)((nvis - c0) < IDX_CHUNK ? (nvis - c0) : IDX_CHUNK);
             if (threadIdx.x < IT) score_chunk<MODE, IT, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
             __syncthreads();
             for (int i = tid; i < cnt; i += NT)
@@ -551,9 +559,9 @@ __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, i
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
     float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
     uint32_t written = 0, ties = 0;
-    const int per = (p.chunk + NT - 1) / NT;
-    for (int64_t c0 = 0; c0 < nvis; c0 += p.chunk) {
-        const int cnt = (int)((nvis - c0) < p.chunk ? (nvis - c0) : p.chunk);
+    const int per = (IDX_CHUNK + NT - 1) / NT;
+    for (int64_t c0 = 0; c0 < nvis; c0 += IDX_CHUNK) {
+        const int cnt = (int)((nvis - c0) < IDX_CHUNK ? (nvis - c0) : IDX_CHUNK);
         if (threadIdx.x < IT) score_chunk<MODE, IT, false>(p, q, b, c0, cnt, skey, sq);  // the first IT threads score
         __syncthreads();
         const int lo = threadIdx.x * per;
@@ -630,18 +638,20 @@ __global__ __launch_bounds__(IT) void index_score_kernel(IndexPlan p) {
     const int64_t spread = (kk + div - 1) / div;
     if (spread > s_want) s_want = (int)spread;
     if (s_want > cnt) s_want = cnt;
-    chunk_emit(p, q, chunk, c0, cnt, s_want, skey, em);
+    chunk_emit<IDX_CHUNK / IT>(p, q, chunk, c0, cnt, s_want, skey, em);
 }
 
 // ---------------------------------------- several chunks per workgroup ----
 
-// Chunked prefill: many queries, each with many chunks. A workgroup takes
-// IDX_CPW consecutive chunks of one query: the query's operands are loaded
-// once, and the next chunk's first two key batches are in flight while the
-// current chunk emits its candidates. Per chunk the tiles, head sums, score
-// keys and emission are those of score_chunk_mx and chunk_emit, so the
-// candidate regions are bitwise identical to the one-chunk kernel's.
-constexpr int IDX_CPW = 4;
+// Several queries per sequence over many entries (chunked prefill, drafts).
+// A chunk is IDX_CPW sub-chunks of IDX_CHUNK entries; the workgroup of
+// (chunk, query) loads the query's operands once, scores the sub-chunks one
+// after the other (the next one's first two key batches in flight while the
+// current one finishes) into one score buffer, and emits the chunk's
+// candidates once. Per sub-chunk the tiles, head sums and score keys are
+// those of score_chunk_mx, so every score is bitwise the one-chunk kernel's.
+// One emission per IDX_CPW sub-chunks: the emission's fixed VALU work, and
+// not the head sums, was what an emission per sub-chunk spent beyond them.
 
 struct ChunkGeo {
     const char *kbase, *sbase;
@@ -665,22 +675,25 @@ __global__ __launch_bounds__(IT, 4) void index_score_cpw_kernel(IndexPlan p) {
     static_assert(NB * 16 * STRIDE == IDX_CHUNK && NB % 2 == 0, "a chunk is an even number of batches");
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
     __shared__ EmitSmem em;
-    uint32_t *skey = dyn;  // [chunk], reused by each chunk of the workgroup
+    uint32_t *skey = dyn;  // [chunk]: sub-chunk i's scores from IDX_CHUNK i on
     const int q = blockIdx.y + p.q_base;
     const int b = q / p.Tq;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int ch0 = blockIdx.x * IDX_CPW;
-    const int ch_end = ch0 + IDX_CPW < p.n_chunks ? ch0 + IDX_CPW : p.n_chunks;
+    const int chunk = blockIdx.x;
+    const int64_t cbase = (int64_t)chunk * p.chunk;
     const int64_t nvis = visible_entries(p, q);
     const int64_t n_active = (nvis + p.chunk - 1) / p.chunk;
-    const int act_end = n_active < (int64_t)ch_end ? (int)n_active : ch_end;  // chunks ch0 .. act_end-1 score
-    for (int c = (act_end > ch0 ? act_end : ch0) + tid; c < ch_end; c += IT) {
-        uint32_t *meta = p.meta + ((size_t)q * p.n_chunks + c) * 2;
-        meta[0] = 0;
-        meta[1] = 0;
+    const int cnt_all = (int)(nvis - cbase <= 0 ? 0 : (nvis - cbase < p.chunk ? nvis - cbase : p.chunk));
+    if (cnt_all == 0) {
+        if (tid == 0) {
+            uint32_t *meta = p.meta + ((size_t)q * p.n_chunks + chunk) * 2;
+            meta[0] = 0;
+            meta[1] = 0;
+        }
+        return;
     }
-    if (act_end <= ch0) return;
+    const int n_sub = (cnt_all + IDX_CHUNK - 1) / IDX_CHUNK;  // sub-chunks with visible entries
 
     // the query's operands into LDS (read again for each chunk, so that they
     // hold no registers while the next chunk's keys fly during an emission)
@@ -725,11 +738,11 @@ __global__ __launch_bounds__(IT, 4) void index_score_cpw_kernel(IndexPlan p) {
             sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, svo, 0, 0);
         }
     };
-    auto chunk_cnt = [&](int c) {
-        const int64_t left = nvis - (int64_t)c * p.chunk;
-        return (int)(left < p.chunk ? left : p.chunk);
+    auto sub_cnt = [&](int sub) {
+        const int left = cnt_all - sub * IDX_CHUNK;
+        return left < IDX_CHUNK ? left : IDX_CHUNK;
     };
-    ChunkGeo geo = chunk_geo(p, b, (int64_t)ch0 * p.chunk, chunk_cnt(ch0));
+    ChunkGeo geo = chunk_geo(p, b, cbase, sub_cnt(0));
     issue(ka, sa, geo, 0);
     __builtin_amdgcn_sched_barrier(0);
     issue(kb, sb, geo, 1);
@@ -766,13 +779,13 @@ __global__ __launch_bounds__(IT, 4) void index_score_cpw_kernel(IndexPlan p) {
             sv[u] = (sv[u] >> (8 * grp)) & 0xFFu;
         }
     };
+    uint32_t *sk = skey;  // the current sub-chunk's scores
     auto finish = [&](const float (&part)[BATCH], int bi) {
         const float s = scatter_rows(part);
-        skey[(STRIDE * bi + wave + NW * grp) * 16 + col] = score_key(s);
+        sk[(STRIDE * bi + wave + NW * grp) * 16 + col] = score_key(s);
     };
-    for (int c = ch0; c < act_end; ++c) {
-        const int64_t c0 = (int64_t)c * p.chunk;
-        const int cnt = chunk_cnt(c);
+    for (int sub = 0; sub < n_sub; ++sub) {
+        sk = skey + sub * IDX_CHUNK;
         v8i A[4];
         float wv[4][4];
 #pragma unroll
@@ -817,17 +830,16 @@ __global__ __launch_bounds__(IT, 4) void index_score_cpw_kernel(IndexPlan p) {
                 finish(part, bi);
             }
         }
-        if (c + 1 < act_end) {  // the next chunk's first batches fly during this chunk's emission
-            geo = chunk_geo(p, b, c0 + p.chunk, chunk_cnt(c + 1));
+        if (sub + 1 < n_sub) {  // the next sub-chunk's first batches
+            geo = chunk_geo(p, b, cbase + (int64_t)(sub + 1) * IDX_CHUNK, sub_cnt(sub + 1));
             issue(ka, sa, geo, 0);
             __builtin_amdgcn_sched_barrier(0);
             issue(kb, sb, geo, 1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
-        // chunk_emit reads skey before its first barrier, so the next chunk may overwrite it afterwards
-        chunk_emit(p, q, c, c0, cnt, s_base < cnt ? s_base : cnt, skey, em);
     }
+    __syncthreads();
+    chunk_emit<IDX_CHUNK * IDX_CPW / IT>(p, q, chunk, cbase, cnt_all, s_base < cnt_all ? s_base : cnt_all, skey, em);
 }
 
 // ------------------------------------------------------ merge select ----
@@ -1246,16 +1258,15 @@ __global__ __launch_bounds__(MT) void index_merge_kernel(IndexPlan p) {
 template <int MODE>
 static void launch_mode(const IndexPlan &p, hipStream_t s) {
     const size_t q_lds = MODE == 0 ? (size_t)p.H * p.dI * 4 : 0;
-    // several queries per sequence with several chunks each (chunked prefill):
-    // a workgroup takes IDX_CPW chunks of one query
-    const bool cpw = MODE != 0 && p.Tq > 1 && p.n_chunks > 1;
+    // several queries per sequence over many entries (chunked prefill): the
+    // layout's chunks are IDX_CPW sub-chunks, one workgroup each
+    const bool cpw = p.chunk > IDX_CHUNK;
     for (int q0 = 0; q0 < p.Q; q0 += MAX_GRID_Y) {
         IndexPlan ps = p;
         ps.q_base = q0;
         const int nq = p.Q - q0 < MAX_GRID_Y ? p.Q - q0 : MAX_GRID_Y;
         if (cpw)
-            hipLaunchKernelGGL(index_score_cpw_kernel<MODE == 0 ? 1 : MODE>,
-                               dim3((p.n_chunks + IDX_CPW - 1) / IDX_CPW, nq), dim3(IT),
+            hipLaunchKernelGGL(index_score_cpw_kernel<MODE == 0 ? 1 : MODE>, dim3(p.n_chunks, nq), dim3(IT),
                                (size_t)p.chunk * 4 + (size_t)p.H * 72, s, ps);
         else
             hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, nq), dim3(IT), (size_t)p.chunk * 4 + q_lds, s,

@@ -50,9 +50,13 @@ struct CompressPlan {
     double inv_freq[ROPE_PAIRS];
 };
 
-// Entries scored by one indexer workgroup. A compile-time constant: the
-// scoring loop over a chunk is fully unrolled.
+// Entries scored by one indexer workgroup in one unrolled pass (a sub-chunk).
+// A compile-time constant: the scoring loop over it is fully unrolled.
 constexpr int IDX_CHUNK = 1024;
+// With several queries per sequence over more than IDX_CHUNK entries (chunked
+// prefill, drafts) a chunk is IDX_CPW sub-chunks: one workgroup scores them
+// and keeps one candidate set for all of them.
+constexpr int IDX_CPW = 4;
 
 // Launches put queries on grid y, whose extent is at most 65535: larger
 // query counts run as several launches, each with its first query in q_base.
@@ -61,7 +65,7 @@ constexpr int MAX_GRID_Y = 65535;
 struct IndexPlan {
     int Q, Tq, H, dI, k, m;
     int q_base;      // first query of this launch (score kernel)
-    int chunk;       // entries scored per workgroup (IDX_CHUNK)
+    int chunk;       // entries per chunk: IDX_CHUNK, or IDX_CHUNK x IDX_CPW (several queries per sequence)
     int n_chunks;    // workgroups per query
     int s_local;     // candidates a chunk keeps at least (its local top-s)
     int region_cap;  // candidate slots per chunk in the workspace
