@@ -415,8 +415,10 @@ __device__ __forceinline__ void store_codes(__bf16 *dst, const v4i &c) {
 // that stage its slot then overwrite it with the encoded row from LDS (the
 // same threads, so the later store wins), in place of the loaded (previous)
 // store contents.
+// `ksc_mul` multiplies the K row scales as they are staged (the softmax scale
+// in log2 units, so that a score is one fma).
 __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *rows, TileBuf &sm, int rel, int n_rel,
-                                           int tid, const AppRow &app, int cur) {
+                                           int tid, const AppRow &app, int cur, float ksc_mul) {
     const int r = tid >> 3, part = tid & 7;
     const v4i z = {0, 0, 0, 0};
     const v4i kn = R.ok ? R.kn : z, vn = R.ok ? R.vn : z, kr = R.ok ? R.kr : z, vr = R.ok ? R.vr : z;
@@ -432,7 +434,7 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *row
     asm volatile("" : "+v"(sc));
     sc = R.sok ? sc : 0.f;
     if (tid < TK) {
-        sm.ksc[tid] = sc;
+        sm.ksc[tid] = sc * ksc_mul;
         sm.kbias[tid] = (rel + tid < n_rel && rows[rel + tid] >= 0) ? 0.f : -__builtin_inff();
     } else if (tid < 2 * TK) {
         sm.vsc[tid - TK] = sc;
@@ -445,7 +447,7 @@ __device__ __forceinline__ void stage_tile(const TileRegs &R, const int32_t *row
             *(v4i *)&sm.kb[ra * KB_LD + MDN + 8 * part] = *(const v4i *)&app.kr[16 * part];
             *(v4i *)&sm.vb[ra * KB_LD + MDN + 8 * part] = *(const v4i *)&app.vr[16 * part];
         }
-        if (tid == ra) sm.ksc[ra] = app.ksc;
+        if (tid == ra) sm.ksc[ra] = app.ksc * ksc_mul;
         if (tid == TK + ra) sm.vsc[ra] = app.vsc;
     }
 }
@@ -620,6 +622,11 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     }
     __syncthreads();
 
+    // Scores are kept in log2 units: the softmax scale times log2(e) multiplies
+    // the K row scales as they are staged and the rotated RoPE query here, and
+    // the RoPE product's accumulator starts at the key's bias (0, or -inf for
+    // an empty slot), so a score is one fma of the two products.
+    const float sc2 = p.sm_scale * 1.4426950408889634f;
     // query operands (B of S^T = K Q^T): head `col` of this wave, dims 32c + 8g .. +8
     bf16x8 qrh[2], qrl[2];
 #pragma unroll
@@ -633,7 +640,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
             const int pr = (32 * c + 8 * g + i) >> 1;
             const float2 t = sm.rsc[pr];
             const float x = (float)raw[i], y = (float)raw[i + 1];
-            const float rx = x * t.y - y * t.x, ry = x * t.x + y * t.y;
+            const float rx = (x * t.y - y * t.x) * sc2, ry = (x * t.x + y * t.y) * sc2;
             hi[i] = (__bf16)rx;
             hi[i + 1] = (__bf16)ry;
             lo[i] = (__bf16)(rx - (float)hi[i]);
@@ -642,7 +649,6 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         qrh[c] = hi;
         qrl[c] = lo;
     }
-    const float sc2 = p.sm_scale * 1.4426950408889634f;
     // The running max starts at a finite floor far below any logit, so that
     // exp2(s - mrun) is 0 for an empty slot (s = -inf) with no test.
     float mrun = -1e30f, lrun = 0.f;
@@ -668,7 +674,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
             vs[st] = *(const v4f *)&tb.vsc[16 * st + 4 * g];
         }
         // the two key halves as independent MFMA chains
-        v4f an[2] = {zero, zero}, ar[2] = {zero, zero};
+        v4f an[2] = {zero, zero}, ar[2] = {kb[0], kb[1]};
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -683,12 +689,12 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
                 ar[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrh[c], ar[st], 0, 0, 0);
                 ar[st] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qrl[c], ar[st], 0, 0, 0);
             }
-        // an empty slot has a zero K row and bias -inf
+        // an empty slot has a zero K row, a zero scale and bias -inf
         float s[2][4];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[st][j] = (an[st][j] * ks[st][j] + ar[st][j]) * sc2 + kb[st][j];
+            for (int j = 0; j < 4; ++j) s[st][j] = __builtin_fmaf(an[st][j], ks[st][j], ar[st][j]);
         float mx = s[0][0];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -785,7 +791,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // tile r + 2 into the register set that staging freed.
     TileBuf &b0 = sm.tb[stream][0], &b1 = sm.tb[stream][1];
     __syncthreads();  // the resolved rows and the appended row are published
-    stage_tile(RA, sm.rows, b0, stream * TK, n_rel, tids, sm.app, cur);
+    stage_tile(RA, sm.rows, b0, stream * TK, n_rel, tids, sm.app, cur, sc2);
     load_tile(lsrc, sm.rows, (stream + 2 * NS) * TK, n_rel, RA, tids);
     __syncthreads();
     // The loop runs whole pairs of rounds and has no exit but its own test:
@@ -796,11 +802,11 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     for (; i + 2 < n_rounds; i += 2) {
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         if (ta < n_tiles) compute(b0);
-        stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur);
+        stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur, sc2);
         load_tile(lsrc, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
         __syncthreads();
         if (tb_ < n_tiles) compute(b1);
-        stage_tile(RA, sm.rows, b0, (ta + 2 * NS) * TK, n_rel, tids, sm.app, cur);
+        stage_tile(RA, sm.rows, b0, (ta + 2 * NS) * TK, n_rel, tids, sm.app, cur, sc2);
         load_tile(lsrc, sm.rows, (ta + 4 * NS) * TK, n_rel, RA, tids);
         __syncthreads();
     }
@@ -808,7 +814,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         if (ta < n_tiles) compute(b0);
         if (i + 1 < n_rounds) {
-            stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur);
+            stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur, sc2);
             __syncthreads();
             if (tb_ < n_tiles) compute(b1);
         }
