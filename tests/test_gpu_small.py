@@ -280,6 +280,28 @@ def test_index_mxfp4_shapes_and_edges():
     _check_index(c, idx, score, c['dkeys'], c['diq'])
 
 
+@pytest.mark.parametrize('rows,k', [(1025, 512), (4096, 1024), (4097, 2048), (8193, 1024)])
+def test_index_mxfp4_multi_query_chunk_boundaries(rows, k):
+    """Several queries per sequence over more than 1,024 entries: the layout's chunk is four
+    1,024-entry sub-chunks with one candidate emission each (one workgroup per chunk). Entry
+    counts just past a sub-chunk, at and just past a chunk, and past two chunks; queries that
+    see every entry, part of a chunk, or almost nothing; k up to 2,048, where a chunk's share
+    is capped by its region. Checked against the oracle, and bitwise against one call per
+    query (the one-chunk scorer)."""
+    n = rows * 4
+    q_pos = np.array([[n - 1, (rows // 2) * 4 + 1, 4 * 3 - 1],
+                      [(rows - 1) * 4 - 1, 4 * 1030 - 1, -1]], np.int64)
+    c = _index_case_mx(43 + rows, 2, rows, q_pos, k)
+    print(f'index mxfp4, 3 queries per sequence over {rows} entries, k {k}', flush=True)
+    idx, score = _run_index(c)
+    _check_index(c, idx, score, c['dkeys'], c['diq'])
+    for i in range(q_pos.shape[1]):
+        ci = dict(c, q_pos=c['q_pos'][:, i:i + 1], ip=c['ip'][:, i:i + 1], isc=c['isc'][:, i:i + 1],
+                  w=c['w'][:, i:i + 1])
+        idx1, score1 = _run_index(ci)
+        assert np.array_equal(idx1[:, 0], idx[:, i]) and _same_bits(score1[:, 0], score[:, i]), f'query {i}'
+
+
 def test_index_mxfp4_clustered_winners_and_ties():
     q_pos = np.array([[40000 * 4 - 1], [20000]], np.int64)
     c = _index_case_mx(2, 2, 40000, q_pos, 1024, cluster=(0, 3000, 1500), ties=True)
