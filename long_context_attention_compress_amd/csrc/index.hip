@@ -65,22 +65,49 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
     return x;
 }
 
+// Values that are the same in every lane (the wave's index, an LDS word that
+// every lane reads) are read into scalars, so that selections and loops on
+// them are scalar compares and branches instead of per-lane masks.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+
+// Per-wave values arr[0 .. NW) in LDS (NW <= 16): the sum over the waves
+// before `wave` and over all of them, as scalars. Lane w < NW reads arr[w];
+// a 16-lane inclusive scan (DPP row shifts) leaves the prefix sums in lanes
+// 0 .. NW-1, which are read out with readlane.
+template <int NW>
+__device__ __forceinline__ void wave_prefix(const uint32_t *arr, int wave, uint32_t *before, uint32_t *all) {
+    static_assert(NW >= 1 && NW <= 16, "the per-wave values fit one 16-lane row");
+    const int lane = threadIdx.x & 63;
+    uint32_t x = arr[lane < NW ? lane : 0];
+    x = lane < NW ? x : 0u;
+    if (NW > 1) x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    if (NW > 2) x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    if (NW > 4) x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    if (NW > 8) x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    *all = (uint32_t)__builtin_amdgcn_readlane((int)x, NW - 1);
+    *before = wave > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)x, wave - 1) : 0u;
+}
+
+// Unsigned max of arr[0 .. NW) in LDS (NW <= 64), as a scalar.
+template <int NW>
+__device__ __forceinline__ uint32_t lds_max_u32(const uint32_t *arr) {
+    const int lane = threadIdx.x & 63;
+    return uniform_u32(wave_max_u32(arr[lane < NW ? lane : 0]));
+}
+
 // Inclusive prefix sum over the workgroup (NT threads) in thread order; *total gets the sum.
 template <int NT>
 __device__ uint32_t block_scan(uint32_t v, IdxSmem &sm, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_index();
     const uint32_t x = wave_inclusive_scan(v);
-    (void)lane;
     __syncthreads();
     if (lane == 63) sm.scan[wave] = x;
     __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-        uint32_t t = sm.scan[w];
-        before += (w < wave) ? t : 0u;
-        all += t;
-    }
+    uint32_t before, all;
+    wave_prefix<NT / 64>(sm.scan, wave, &before, &all);
     *total = all;
     return x + before;
 }
@@ -99,8 +126,8 @@ __device__ int find_bin(IdxSmem &sm, uint32_t need, uint32_t *above) {
         sm.misc[1] = (int)excl;
     }
     __syncthreads();
-    int b = sm.misc[0];
-    *above = (uint32_t)sm.misc[1];
+    int b = (int)uniform_u32((uint32_t)sm.misc[0]);
+    *above = uniform_u32((uint32_t)sm.misc[1]);
     __syncthreads();
     return b;
 }
@@ -380,17 +407,12 @@ struct EmitSmem {
 
 // Exclusive prefix sum over the IT threads in thread order; *total gets the sum.
 __device__ __forceinline__ uint32_t emit_scan(uint32_t v, EmitSmem &em, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_index();
     const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) em.scan[wave] = x;
     __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < IT / 64; ++w) {
-        const uint32_t t = em.scan[w];
-        before += (w < wave) ? t : 0u;
-        all += t;
-    }
+    uint32_t before, all;
+    wave_prefix<IT / 64>(em.scan, wave, &before, &all);
     *total = all;
     return x - v + before;
 }
@@ -400,7 +422,7 @@ template <int PER>
 __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
                            const uint32_t *skey, EmitSmem &em) {
     static_assert(PER % 4 == 0, "whole 16-byte LDS reads per thread");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const size_t rid = (size_t)q * p.n_chunks + chunk;
     uint32_t key[PER];
 #pragma unroll
@@ -433,11 +455,8 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
             em.red[1][wave] = nmn;
         }
         __syncthreads();
-#pragma unroll
-        for (int w = 0; w < IT / 64; ++w) {
-            mx = em.red[0][w] > mx ? em.red[0][w] : mx;
-            nmn = em.red[1][w] > nmn ? em.red[1][w] : nmn;
-        }
+        mx = lds_max_u32<IT / 64>(em.red[0]);
+        nmn = lds_max_u32<IT / 64>(em.red[1]);
         const uint32_t diff = mx ^ ~nmn;
         if (diff == 0u) {
             thr = mx;  // every valid key equal: all of them reach it
@@ -481,7 +500,8 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
                     }
                 }
                 __syncthreads();
-                const uint32_t bin = em.res[0], above = em.res[1], pop = em.res[2];
+                const uint32_t bin = uniform_u32(em.res[0]), above = uniform_u32(em.res[1]),
+                               pop = uniform_u32(em.res[2]);
                 prefix |= bin << sh;
                 above_all += above;
                 need -= above;
@@ -865,17 +885,12 @@ struct __attribute__((aligned(16))) MergeSmem {
 // Inclusive prefix sum over the workgroup. Consecutive calls must alternate
 // `buf`; the barrier of one call then protects the other buffer.
 __device__ __forceinline__ uint32_t scan_buf(uint32_t v, MergeSmem &sm, int buf, uint32_t *total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = wave_index();
     const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) sm.part[buf][wave] = x;
     __syncthreads();
-    uint32_t before = 0, all = 0;
-#pragma unroll
-    for (int w = 0; w < MT / 64; ++w) {
-        const uint32_t t = sm.part[buf][w];
-        before += (w < wave) ? t : 0u;
-        all += t;
-    }
+    uint32_t before, all;
+    wave_prefix<MT / 64>(sm.part[buf], wave, &before, &all);
     *total = all;
     return x + before;
 }
@@ -907,9 +922,9 @@ __device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf
     }
     *(uint4 *)&sm.hist[b0] = make_uint4(0, 0, 0, 0);
     __syncthreads();
-    *bin = sm.misc[0];
-    *above = sm.misc[1];
-    *in_bin = sm.misc[2];
+    *bin = uniform_u32(sm.misc[0]);
+    *above = uniform_u32(sm.misc[1]);
+    *in_bin = uniform_u32(sm.misc[2]);
 }
 
 
@@ -942,7 +957,7 @@ __device__ __forceinline__ void fence_keys(uint32_t (&k)[REG_CAND]) {
 __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, uint32_t *pre, IdxSmem &sm,
                                              MergeSmem &ms) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = wave_index();
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
     float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
     const uint32_t *meta = p.meta + (size_t)q * p.n_chunks * 2;
@@ -991,12 +1006,12 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
         ms.red[2][wave] = (w_over ? 1u : 0u) | (w_big ? 2u : 0u);
     }
     __syncthreads();
-    uint32_t flags = 0;
-#pragma unroll
-    for (int w = 0; w < MT / 64; ++w) {
-        kmax = ms.red[0][w] > kmax ? ms.red[0][w] : kmax;
-        t_lo = ms.red[1][w] > t_lo ? ms.red[1][w] : t_lo;
-        flags |= ms.red[2][w];
+    kmax = lds_max_u32<MT / 64>(ms.red[0]);
+    t_lo = lds_max_u32<MT / 64>(ms.red[1]);
+    uint32_t flags;
+    {
+        const uint32_t f = ms.red[2][lane < MT / 64 ? lane : 0];
+        flags = (__ballot(f & 1u) != 0 ? 1u : 0u) | (__ballot(f & 2u) != 0 ? 2u : 0u);
     }
     if (flags & 1u) {
         return false;
@@ -1063,13 +1078,8 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
             ms.red[1][wave] = tl;
         }
         __syncthreads();
-        kmax = 0u;
-        t_lo = 1u;
-#pragma unroll
-        for (int w = 0; w < MT / 64; ++w) {
-            kmax = ms.red[0][w] > kmax ? ms.red[0][w] : kmax;
-            t_lo = ms.red[1][w] > t_lo ? ms.red[1][w] : t_lo;
-        }
+        kmax = lds_max_u32<MT / 64>(ms.red[0]);
+        t_lo = lds_max_u32<MT / 64>(ms.red[1]);
     }
     if (kmax < t_lo) return false;  // no candidate at or above T_lo
     // candidates below T_lo never decide anything: empty their slots
@@ -1170,8 +1180,8 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
                 ms.misc[1] = need - gt;
             }
             __syncthreads();
-            kth = ms.misc[0];
-            need_ties = ms.misc[1];
+            kth = uniform_u32(ms.misc[0]);
+            need_ties = uniform_u32(ms.misc[1]);
             break;
         }
     }
