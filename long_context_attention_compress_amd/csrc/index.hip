@@ -961,6 +961,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
     float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
     const uint32_t *meta = p.meta + (size_t)q * p.n_chunks * 2;
+    if (tid == 0) ms.misc[3] = 0u;  // the gather's slot counter (read after later barriers)
 
     uint32_t keys[REG_CAND];
     int32_t ids[REG_CAND];
@@ -1138,15 +1139,19 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
             break;
         }
         if (in_bin <= (uint32_t)RESOLVE_MAX) {
-            // gather the bin into LDS (slots by a workgroup prefix sum) ...
+            // gather the bin into LDS: a wave takes its slots with one
+            // addition to an LDS counter (the ranking does not depend on
+            // the list's order) ...
             fence_keys(keys);
             const uint32_t m2 = 0xFFFFFFFFu << top;
             uint32_t n = 0;
 #pragma unroll
             for (int i = 0; i < REG_CAND; ++i) n += (keys[i] & m2) == hi_bits && keys[i] != 0u;
-            uint32_t tot;
-            uint32_t slot = scan_buf(n, ms, buf, &tot) - n;
-            buf ^= 1;
+            const uint32_t x = wave_inclusive_scan(n);
+            const uint32_t w_n = (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
+            uint32_t base = 0;
+            if (w_n != 0u && lane == 0) base = atomicAdd(&ms.misc[3], w_n);
+            uint32_t slot = (uint32_t)__builtin_amdgcn_readlane((int)base, 0) + x - n;
             fence_keys(keys);
 #pragma unroll
             for (int i = 0; i < REG_CAND; ++i) {
@@ -1155,29 +1160,33 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
                 slot += in;
             }
             __syncthreads();
-            // ... and rank it: PARTS threads share an element, each comparing
-            // it with RESOLVE_MAX / PARTS list entries
+            // ... and rank it: PARTS threads share an element, part p comparing
+            // it with list entries p, p + PARTS, ...; waves whose elements all
+            // lie past the bin's end skip the ranking
             constexpr int PARTS = MT / RESOLVE_MAX;
-            const int e = tid / PARTS, part = tid % PARTS;
-            const uint32_t mk = ms.list[e];
-            uint32_t gt = 0, ge = 0;
+            constexpr int EPW = 64 / PARTS;  // elements per wave
+            if ((uint32_t)(wave * EPW) < in_bin) {
+                const int e = tid / PARTS, part = tid % PARTS;
+                const uint32_t mk = ms.list[e];
+                const int n_j = (int)((in_bin + PARTS - 1) / PARTS);
+                uint32_t gt = 0, ge = 0;
+                for (int j = 0; j < n_j; ++j) {
+                    const int o = j * PARTS + part;
+                    const uint32_t ok = ms.list[o];
+                    const bool in = (uint32_t)o < in_bin;
+                    gt += in && ok > mk;
+                    ge += in && ok >= mk;
+                }
 #pragma unroll
-            for (int j = 0; j < RESOLVE_MAX / PARTS; ++j) {
-                const int o = part * (RESOLVE_MAX / PARTS) + j;
-                const uint32_t ok = ms.list[o];
-                const bool in = (uint32_t)o < in_bin;
-                gt += in && ok > mk;
-                ge += in && ok >= mk;
-            }
-#pragma unroll
-            for (int off = 1; off < PARTS; off <<= 1) {
-                gt += __shfl_xor(gt, off, 64);
-                ge += __shfl_xor(ge, off, 64);
-            }
-            // every element equal to the k-th key writes the same pair
-            if (part == 0 && (uint32_t)e < in_bin && gt < need && need <= ge) {
-                ms.misc[0] = mk;
-                ms.misc[1] = need - gt;
+                for (int off = 1; off < PARTS; off <<= 1) {
+                    gt += __shfl_xor(gt, off, 64);
+                    ge += __shfl_xor(ge, off, 64);
+                }
+                // every element equal to the k-th key writes the same pair
+                if (part == 0 && (uint32_t)e < in_bin && gt < need && need <= ge) {
+                    ms.misc[0] = mk;
+                    ms.misc[1] = need - gt;
+                }
             }
             __syncthreads();
             kth = uniform_u32(ms.misc[0]);
@@ -1213,7 +1222,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
             tb += eq;
             const uint32_t a = take ? pos : STAGE_MAX + lane;
             st_id[a] = (uint32_t)ids[i];
-            ms.stage_key[a] = keys[i];
+            if (osc) ms.stage_key[a] = keys[i];  // scores are optional
             pos += take;
         }
     } else {
