@@ -975,6 +975,58 @@ __global__ __launch_bounds__(G * 192) void attn_combine_kernel(AttnPlan p) {
         p.lse[(size_t)q * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -__builtin_inff();
 }
 
+// Merge of at most 64 splits: thread d of a (query, head) workgroup sums
+// output dim d over the splits itself, and every wave reduces the splits'
+// (max, sum) pairs on its own (lane j holds split j), so the merge needs no
+// LDS and no barrier. NS: splits loaded per thread, a multiple of 16 at or
+// above the split count (the surplus loads repeat the last split and get
+// weight zero, so that every load and product is unconditional). The
+// splits are added in split order (deterministic).
+template <int OUT_BF16, int NS>
+__global__ __launch_bounds__(192) void attn_combine_w_kernel(AttnPlan p) {
+    static_assert(NS % 16 == 0 && NS <= 64, "one lane per split");
+    const int q = blockIdx.x, h = blockIdx.y, d = threadIdx.x, lane = d & 63;
+    const int D = p.D, H = p.H, S = p.n_split;
+    const size_t base = (size_t)q * S * H;
+    const size_t stride = (size_t)H * D;
+    const bool own = d < D;
+    const int dd = own ? d : 0;
+    // every load in one batch: the partials of dim d (split i's row is a
+    // scalar address stepped by stride), then lane j's (max, sum) pair
+    const float *row = p.part_o + (base + h) * D;
+    float v[NS];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        v[i] = row[dd];
+        row += i + 1 < S ? stride : 0;
+    }
+    const int j = lane < S ? lane : S - 1;
+    const float2 ml = *(const float2 *)&p.part_ml[((base + (size_t)j * H) + h) * 2];
+    __builtin_amdgcn_sched_barrier(0);
+    const float mj = lane < S ? __builtin_fmaxf(-__builtin_inff(), ml.x) : -__builtin_inff();
+    const float M = wave_max_dpp(mj);
+    const float wj = (lane < S && M != -__builtin_inff()) ? __builtin_amdgcn_exp2f(ml.x - M) : 0.f;
+    const float L = wave_sum_dpp(wj * (lane < S ? ml.y : 0.f));
+    // splits past S repeat split S - 1's partial with weight zero (a finite
+    // partial adds zero; a NaN one makes the output NaN either way)
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) acc = __builtin_fmaf(v[i], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), i)), acc);
+    if (own) {
+        const float o = L > 0.f ? acc / L : 0.f;
+        if (OUT_BF16) ((__bf16 *)p.o)[((size_t)q * H + h) * D + d] = (__bf16)o;
+        else ((float *)p.o)[((size_t)q * H + h) * D + d] = o;
+    }
+    if (d == 0 && p.lse)
+        p.lse[(size_t)q * H + h] = L > 0.f ? (M + log2f(L)) * 0.6931471805599453f : -__builtin_inff();
+}
+
+template <int NS>
+static void launch_combine_w(const AttnPlan &p, hipStream_t s) {
+    if (p.o_bf16) hipLaunchKernelGGL((attn_combine_w_kernel<1, NS>), dim3(p.Q, p.H), dim3(192), 0, s, p);
+    else hipLaunchKernelGGL((attn_combine_w_kernel<0, NS>), dim3(p.Q, p.H), dim3(192), 0, s, p);
+}
+
 static void launch_attn_slice(const AttnPlan &p, int nq, hipStream_t s) {
     const dim3 grid(p.n_split, nq);
     if (p.ek.fmt == 0 && p.wk.fmt == 0) {
@@ -1010,6 +1062,15 @@ hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
     // many query-head pairs (several tokens per sequence): one thread per output dim
     // sums every split; few pairs (one decode token): CMB_G threads share a dim
     const bool many = (int64_t)p.Q * p.H >= CMB_MANY;
+    if (!many && p.n_split <= 64) {
+        switch ((p.n_split + 15) / 16) {
+            case 1: launch_combine_w<16>(p, s); break;
+            case 2: launch_combine_w<32>(p, s); break;
+            case 3: launch_combine_w<48>(p, s); break;
+            default: launch_combine_w<64>(p, s); break;
+        }
+        return hipGetLastError();
+    }
     if (p.o_bf16) {
         if (many) hipLaunchKernelGGL((attn_combine_kernel<1, 1>), dim3(p.Q, p.H), dim3(192), 0, s, p);
         else hipLaunchKernelGGL((attn_combine_kernel<1, CMB_G>), dim3(p.Q, p.H), dim3(CMB_G * 192), 0, s, p);

@@ -95,6 +95,36 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
     auto c = __builtin_amdgcn_permlane32_swap(x, x, false, false);
     return c[0] > c[1] ? c[0] : c[1];
 }
+// Float max and sum over the wave on the VALU (DPP row rotations, then the
+// lane swaps), with the result in every lane. Each step combines a lane's
+// value with one that its partner combines in the other order, so every lane
+// ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float row_rot(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max_dpp(float x) {
+    float y;
+    y = row_rot<0x128>(x); x = y > x ? y : x;  // row_ror:8
+    y = row_rot<0x124>(x); x = y > x ? y : x;  // row_ror:4
+    y = row_rot<0x122>(x); x = y > x ? y : x;  // row_ror:2
+    y = row_rot<0x121>(x); x = y > x ? y : x;  // row_ror:1
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) > __uint_as_float(a[1]) ? __uint_as_float(a[0]) : __uint_as_float(a[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) > __uint_as_float(c[1]) ? __uint_as_float(c[0]) : __uint_as_float(c[1]);
+}
+__device__ __forceinline__ float wave_sum_dpp(float x) {
+    x += row_rot<0x128>(x);
+    x += row_rot<0x124>(x);
+    x += row_rot<0x122>(x);
+    x += row_rot<0x121>(x);
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Magnitude maxima (inputs are |x| or a NaN with the sign cleared; as bits
 // they order like the magnitudes, a NaN above infinity, so a NaN propagates).
 __device__ __forceinline__ float wave_amax_bits(float a) { return __uint_as_float(wave_max_u32(__float_as_uint(a))); }
