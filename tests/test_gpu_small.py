@@ -568,6 +568,35 @@ def test_attn_many_query_head_pairs_combine():
                 assert_close_rms(o[b, i], ro, TOL_BF16, f'{name} b{b} i{i}')
 
 
+@pytest.mark.parametrize('n_split', [16, 17, 48, 49, 64, 65])
+def test_attn_combine_split_counts(n_split):
+    """Sparse calls whose key list (k id slots + W window rows = 32 n keys, one tile per
+    split) gives n splits: the one-thread-per-dim combine at each of its load counts
+    (16, 32, 48, 64 splits: 16 and 17, 48 and 49, 64) and the grouped combine above 64
+    splits. The last 64 id slots are empty, so whole splits have no key (max -inf, sum 0);
+    outputs and log-sum-exps against the oracle."""
+    B, Tq, rows, m, H, D, W = 2, 1, 3000, 4, 64, 192, 128
+    k = 32 * n_split - W
+    q_pos = np.array([[rows * m - 1], [rows * m - 1 - 9]], np.int64)
+    c = _attn_case(81 + n_split, B, Tq, H, D, rows, q_pos, 'fp8', W=W)
+    ek, ev, wk, wv = _stores(c)
+    g = np.random.default_rng(82 + n_split)
+    idx = np.full((B, Tq, k), -1, np.int32)
+    for b in range(B):
+        idx[b, 0, :k - 64] = np.sort(g.choice(rows, k - 64, replace=False))
+    lse = torch.zeros(B, Tq, H, dtype=torch.float32, device='cuda')
+    print(f'combine over {n_split} splits', flush=True)
+    o = v4.sparse_window_attn(_qdev(c), dev(q_pos), ek, ev, m, wk, wv, W, dev(idx), lse=lse)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    for b in range(B):
+        ids = idx[b, 0][idx[b, 0] >= 0]
+        ro, rl = _oracle_attn(c, b, 0, ids)
+        assert_close_rms(o[b, 0], ro, TOL_BF16, f'o b{b}')
+        assert np.allclose(lse[b, 0], rl, atol=2e-2), f'lse b{b}'
+
+
 @pytest.mark.parametrize('Tq', [3, 70])
 def test_attn_dense_long_list(Tq):
     """A key list of more than 4096 keys with the window (two key streams per
