@@ -106,7 +106,8 @@ typedef struct {
  *                         plane rope  [rows][64] bfloat16 bits,
  *                         plane scale [rows][(dim-64)/128] float32;
  *                         value of nope element i = E4M3(code) * scale[i/128].
- *  rows  rows per batch element.
+ *  rows  rows per batch element (below 2^30 for the attention calls, which
+ *        reject larger stores with V4A_EINVAL).
  *  ring  0: entry/position n is row n (n < rows);
  *        > 0: entry/position n is row n % ring (ring <= rows), for a window
  *        kept as a ring buffer.

@@ -256,6 +256,10 @@ int check_attn(const v4a_attn_args *a, AttnPlan *P) {
     if ((r = check_kv(a->win_k, "win_k", &P->wk)) || (r = check_kv(a->win_v, "win_v", &P->wv))) return r;
     if (a->ent_k && ((r = check_kv(a->ent_k, "ent_k", &P->ek)) || (r = check_kv(a->ent_v, "ent_v", &P->ev)))) return r;
     if (a->ent_k && (a->ent_k->ring != 0 || a->ent_v->ring != 0)) return fail(V4A_EINVAL, "entry stores cannot be rings");
+    // rows are addressed as 30-bit codes (bit 30 marks a window-store row)
+    for (auto *s : {a->win_k, a->win_v, a->ent_k, a->ent_v})
+        if (s && s->rows >= ((int64_t)1 << 30))
+            return fail(V4A_EINVAL, "a store of %lld rows exceeds the 2^30 rows attention addresses", (long long)s->rows);
     const int fmt = a->win_k->fmt;
     const v4a_kv_store *all[4] = {a->win_k, a->win_v, a->ent_k, a->ent_v};
     for (auto *s : all)

@@ -51,12 +51,25 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
 
+// The key list of one query at position t. Counts and rows fit 32 bits: a
+// list holds at most MAX_KEY_LIST keys and the stores fewer than 2^30 rows
+// (the host checks both), so the per-key arithmetic below is 32-bit.
 struct KeyInfo {
-    int64_t n_list;  // entries in the list
-    int64_t n_win;   // window rows
+    int32_t n_list;  // entries in the list
+    int32_t n_win;   // window rows
     int64_t t;
-    int64_t wrow0;   // window-store row of the window's first key (position t - n_win + 1)
+    int32_t wrow0;   // window-store row of the window's first key (position t - n_win + 1);
+                     // a linear store's row count when that position lies past it
 };
+
+// (t + 1) / m and pos % ring in 32 bits where the operands fit (every
+// position below 2^32); the 64-bit forms otherwise.
+__device__ __forceinline__ int64_t div_pos(int64_t x, int64_t d) {
+    return (uint64_t)x < (1ull << 32) ? (int64_t)((uint32_t)x / (uint32_t)d) : x / d;
+}
+__device__ __forceinline__ int64_t mod_pos(int64_t x, int64_t d) {
+    return (uint64_t)x < (1ull << 32) ? (int64_t)((uint32_t)x % (uint32_t)d) : x % d;
+}
 
 __device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int64_t t) {
     KeyInfo ki;
@@ -67,16 +80,17 @@ __device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int64_t t) {
         ki.n_win = 0;
         return ki;
     }
-    ki.n_win = ki.t + 1 < p.W ? ki.t + 1 : p.W;
+    ki.n_win = (int32_t)(ki.t + 1 < p.W ? ki.t + 1 : p.W);
     const int64_t pos0 = ki.t - ki.n_win + 1;
-    ki.wrow0 = p.wk.ring > 0 ? pos0 % p.wk.ring : pos0;
+    const int64_t wrow0 = p.wk.ring > 0 ? mod_pos(pos0, p.wk.ring) : pos0;
+    ki.wrow0 = (int32_t)(wrow0 < p.wk.rows ? wrow0 : p.wk.rows);
     if (!p.has_ent) ki.n_list = 0;
     else if (p.sparse) ki.n_list = p.k;
     else {
-        int64_t n = (ki.t + 1) / p.m;
+        int64_t n = div_pos(ki.t + 1, p.m);
         if (n > p.ek.rows) n = p.ek.rows;
         if (p.n_override >= 0 && n > p.n_override) n = p.n_override;
-        ki.n_list = n;
+        ki.n_list = (int32_t)n;
     }
     return ki;
 }
@@ -102,18 +116,19 @@ constexpr int32_t WIN_BIT = 1 << 30;  // a row code with this bit set is a windo
 // -1 for a slot without a key. `id` is the selected id when j is a sparse
 // list entry (unused otherwise). The same function serves the per-split rows
 // table and the rows of the first two tiles, which are resolved per lane.
-__device__ __forceinline__ int32_t key_code(const AttnPlan &p, const KeyInfo &ki, int64_t j, int32_t id) {
+__device__ __forceinline__ int32_t key_code(const AttnPlan &p, const KeyInfo &ki, int32_t j, int32_t id) {
     if (j < ki.n_list) {
-        const int64_t e = p.sparse ? (j < p.k ? (int64_t)id : -1) : j;
-        return (e >= 0 && e < p.ek.rows) ? (int32_t)e : -1;
+        const int32_t e = p.sparse ? (j < p.k ? id : -1) : j;
+        return (e >= 0 && e < (int32_t)p.ek.rows) ? e : -1;
     }
-    const int64_t w = j - ki.n_list;
+    const int32_t w = j - ki.n_list;
     if (w >= ki.n_win) return -1;
     // position t - n_win + 1 + w; its ring row without a division: w < n_win
     // <= ring, so one wrap at most
-    int64_t row = ki.wrow0 + w;
-    if (p.wk.ring > 0 && row >= p.wk.ring) row -= p.wk.ring;
-    return row < p.wk.rows ? (int32_t)row | WIN_BIT : -1;
+    int32_t row = ki.wrow0 + w;
+    const int32_t ring = (int32_t)p.wk.ring;
+    if (ring > 0 && row >= ring) row -= ring;
+    return row < (int32_t)p.wk.rows ? row | WIN_BIT : -1;
 }
 
 // ------------------------------------------------------------------ F32 ----
@@ -587,7 +602,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
     TileRegs RA, RB;
     {
-        auto first = [&](int rel, int32_t id) { return rel < n_rel ? key_code(p, ki, j0 + rel, id) : -1; };
+        auto first = [&](int rel, int32_t id) { return rel < n_rel ? key_code(p, ki, (int32_t)j0 + rel, id) : -1; };
         const bool sl = tids < 2 * TK;  // threads 0..63 load the scales
         load_tile_codes(lsrc, first(ra, fid[0]), sl ? first(sa, fid[2]) : -1, RA);
         load_tile_codes(lsrc, first(rb, fid[1]), sl ? first(sb, fid[3]) : -1, RB);
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
         const int i = tid + AT * NS * u;
-        if (i < n_rel) sm.rows[i] = key_code(p, ki, j0 + i, ids[u]);
+        if (i < n_rel) sm.rows[i] = key_code(p, ki, (int32_t)j0 + i, ids[u]);
     }
     if (tid < ROPE_PAIRS) {
         double sn, cs;

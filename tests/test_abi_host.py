@@ -185,8 +185,9 @@ def test_attention_rejections():
 
 
 def test_attention_key_list_and_ring_limits():
-    """A key list longer than the splits can resolve, and a window ring shorter than the
-    window, are rejected before any launch (and their workspace size is 0)."""
+    """A key list longer than the splits can resolve, a window ring shorter than the
+    window and a store of 2^30 rows or more are rejected before any launch (and their
+    workspace size is 0)."""
     lib = _abi.load()
     big = 1024 * 2048   # splits per query x keys a split resolves
 
@@ -222,6 +223,12 @@ def test_attention_key_list_and_ring_limits():
     assert r == _abi.V4A_EINVAL and 'ring' in msg, (r, msg)
     assert lib.hca_attn_workspace(ctypes.byref(args(ring=128, W=128)), -1) > 0
     assert lib.hca_attn_workspace(ctypes.byref(args(ring=100, W=100)), -1) > 0
+    # store rows are addressed by 30-bit codes: 2^30 rows or more are rejected
+    huge = args(ek_rows=1 << 30)
+    assert lib.hca_attn_workspace(ctypes.byref(huge), 1000) == 0
+    r, msg = _status('hca_attn', ctypes.byref(huge), 1000, FAKE, 1 << 40, None)
+    assert r == _abi.V4A_EINVAL and '2^30' in msg, (r, msg)
+    assert lib.hca_attn_workspace(ctypes.byref(args(ek_rows=(1 << 30) - 1)), 1000) > 0
 
 
 def test_index_noalloc_rejections():
