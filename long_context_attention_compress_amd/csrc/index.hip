@@ -32,7 +32,7 @@
 namespace v4a {
 
 constexpr int IT = 256;   // threads of a scoring workgroup (4 waves)
-constexpr int MT = 1024;  // threads of the merge workgroup (16 waves)
+constexpr int MT = 1024;  // threads of the largest merge workgroup (16 waves)
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -397,7 +397,7 @@ __device__ __forceinline__ void score_chunk(const IndexPlan &p, int q, int b, in
 // region's lower bound.
 constexpr int EBITS = 11;
 constexpr int EBINS = 1 << EBITS;
-constexpr int EMIT_SOFT = 32;  // = GROUP * REG_CAND of the merge (static_assert there)
+constexpr int EMIT_SOFT = 32;  // = merge_group * merge_rc of the merge (static_assert there)
 struct EmitSmem {
     uint32_t hist[EBINS] __attribute__((aligned(16)));
     uint32_t red[2][IT / 64];
@@ -548,9 +548,14 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
 
 // ------------------------------------------------------------- merge ----
 
-constexpr int REG_CAND = 8;  // candidates a merge thread holds in registers
-constexpr int GROUP = 4;     // merge threads sharing one chunk's region (32 slots)
-static_assert(GROUP * REG_CAND == EMIT_SOFT, "a chunk emits at most what one thread group holds");
+// The merge workgroup holds MERGE_SLOTS candidates in registers: NT threads
+// of merge_rc<NT>() each, merge_group<NT>() threads sharing one chunk's region.
+constexpr int MERGE_SLOTS = 8192;
+constexpr int MERGE_WIDE_Q = 512;  // from this many queries per call the merge takes 512 threads per query
+template <int NT> constexpr int merge_rc() { return MERGE_SLOTS / NT; }
+template <int NT> constexpr int merge_group() { return EMIT_SOFT / merge_rc<NT>(); }
+static_assert(merge_group<1024>() * merge_rc<1024>() == EMIT_SOFT && merge_group<512>() * merge_rc<512>() == EMIT_SOFT,
+              "a chunk emits at most what one thread group holds");
 
 template <int MODE, int NT>
 __device__ void exact_fallback(const IndexPlan &p, int q, int b, int64_t nvis, int kk, uint32_t *skey,
@@ -867,16 +872,15 @@ __global__ __launch_bounds__(IT, 4) void index_score_cpw_kernel(IndexPlan p) {
 constexpr int MBITS = 12;                 // radix digit of the merge select
 constexpr int MBINS = 1 << MBITS;
 constexpr int RESOLVE_MAX = 128;          // a boundary bin this small is gathered and ranked directly
-constexpr int BPT = MBINS / MT;           // histogram bins per merge thread
-static_assert(BPT == 4, "each merge thread scans four bins (one 16-byte word)");
 constexpr int STAGE_MAX = 2048;           // selections staged in LDS for coalesced output
 
 // Per-key loops are kept free of branches: a key that does not count goes
 // to a dummy slot of its lane (the arrays carry 64 extra slots).
+template <int NT>
 struct __attribute__((aligned(16))) MergeSmem {
     uint32_t hist[MBINS + 64];
-    uint32_t part[2][MT / 64];  // wave totals of block scans (two buffers, used in turn)
-    uint32_t red[3][MT / 64];
+    uint32_t part[2][NT / 64];  // wave totals of block scans (two buffers, used in turn)
+    uint32_t red[3][NT / 64];
     uint32_t list[RESOLVE_MAX + 64] __attribute__((aligned(16)));
     uint32_t misc[4];
     uint32_t stage_key[STAGE_MAX + 64];  // selected keys, staged for coalesced output
@@ -884,13 +888,14 @@ struct __attribute__((aligned(16))) MergeSmem {
 
 // Inclusive prefix sum over the workgroup. Consecutive calls must alternate
 // `buf`; the barrier of one call then protects the other buffer.
-__device__ __forceinline__ uint32_t scan_buf(uint32_t v, MergeSmem &sm, int buf, uint32_t *total) {
+template <int NT>
+__device__ __forceinline__ uint32_t scan_buf(uint32_t v, MergeSmem<NT> &sm, int buf, uint32_t *total) {
     const int lane = threadIdx.x & 63, wave = wave_index();
     const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) sm.part[buf][wave] = x;
     __syncthreads();
     uint32_t before, all;
-    wave_prefix<MT / 64>(sm.part[buf], wave, &before, &all);
+    wave_prefix<NT / 64>(sm.part[buf], wave, &before, &all);
     *total = all;
     return x + before;
 }
@@ -898,15 +903,25 @@ __device__ __forceinline__ uint32_t scan_buf(uint32_t v, MergeSmem &sm, int buf,
 // Highest bin whose suffix count reaches `need`: its index, the count above
 // it, its own count and the count over all bins. Thread t covers bins
 // [MBINS - BPT(t+1), MBINS - BPT t) and zeroes them for the next pass.
-__device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf, uint32_t *bin, uint32_t *above,
+template <int NT>
+__device__ __forceinline__ void merge_find(MergeSmem<NT> &sm, uint32_t need, int buf, uint32_t *bin, uint32_t *above,
                                            uint32_t *in_bin, uint32_t *total) {
+    constexpr int BPT = MBINS / NT;  // bins per thread, read as 16-byte words
+    static_assert(BPT % 4 == 0, "whole 16-byte words of bins per thread");
     const int b0 = MBINS - BPT * (threadIdx.x + 1);
-    const uint4 h0 = *(const uint4 *)&sm.hist[b0];
-    const uint32_t h[BPT] = {h0.x, h0.y, h0.z, h0.w};
+    uint32_t h[BPT];
+#pragma unroll
+    for (int v = 0; v < BPT / 4; ++v) {
+        const uint4 x = *(const uint4 *)&sm.hist[b0 + 4 * v];
+        h[4 * v] = x.x;
+        h[4 * v + 1] = x.y;
+        h[4 * v + 2] = x.z;
+        h[4 * v + 3] = x.w;
+    }
     uint32_t local = 0;
 #pragma unroll
     for (int j = 0; j < BPT; ++j) local += h[j];
-    const uint32_t incl = scan_buf(local, sm, buf, total);
+    const uint32_t incl = scan_buf<NT>(local, sm, buf, total);
     uint32_t acc = incl - local;
     if (acc < need && incl >= need) {
 #pragma unroll
@@ -920,7 +935,8 @@ __device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf
             acc += h[j];
         }
     }
-    *(uint4 *)&sm.hist[b0] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < BPT / 4; ++v) *(uint4 *)&sm.hist[b0 + 4 * v] = make_uint4(0, 0, 0, 0);
     __syncthreads();
     *bin = uniform_u32(sm.misc[0]);
     *above = uniform_u32(sm.misc[1]);
@@ -930,9 +946,10 @@ __device__ __forceinline__ void merge_find(MergeSmem &sm, uint32_t need, int buf
 
 // Marks the key registers as rewritten (no instruction is emitted), so that
 // per-key tests are not hoisted out of the select loop into 32 live masks.
-__device__ __forceinline__ void fence_keys(uint32_t (&k)[REG_CAND]) {
+template <int RC>
+__device__ __forceinline__ void fence_keys(uint32_t (&k)[RC]) {
 #pragma unroll
-    for (int i = 0; i < REG_CAND; ++i) asm volatile("" : "+v"(k[i]));
+    for (int i = 0; i < RC; ++i) asm volatile("" : "+v"(k[i]));
 }
 
 // One workgroup per query. Each thread holds a contiguous run of the chunks'
@@ -954,8 +971,10 @@ __device__ __forceinline__ void fence_keys(uint32_t (&k)[REG_CAND]) {
 //
 // merge_select is the candidate select; false when the exact fallback has to
 // decide instead.
+template <int NT>
 __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, uint32_t *pre, IdxSmem &sm,
-                                             MergeSmem &ms) {
+                                             MergeSmem<NT> &ms) {
+    constexpr int REG_CAND = merge_rc<NT>(), GROUP = merge_group<NT>();
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = wave_index();
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
@@ -968,7 +987,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
     int mine = 0;
     uint32_t t_lo = 1;  // largest chunk lower bound (+1) seen by this thread
     int over = 0, big = 1;
-    if (p.n_chunks * GROUP <= MT) {
+    if (p.n_chunks * GROUP <= NT) {
         // region mode: the region load is issued together with the count
         const int c = tid / GROUP, sub = tid % GROUP;
         uint32_t cnt = 0;
@@ -1007,11 +1026,11 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
         ms.red[2][wave] = (w_over ? 1u : 0u) | (w_big ? 2u : 0u);
     }
     __syncthreads();
-    kmax = lds_max_u32<MT / 64>(ms.red[0]);
-    t_lo = lds_max_u32<MT / 64>(ms.red[1]);
+    kmax = lds_max_u32<NT / 64>(ms.red[0]);
+    t_lo = lds_max_u32<NT / 64>(ms.red[1]);
     uint32_t flags;
     {
-        const uint32_t f = ms.red[2][lane < MT / 64 ? lane : 0];
+        const uint32_t f = ms.red[2][lane < NT / 64 ? lane : 0];
         flags = (__ballot(f & 1u) != 0 ? 1u : 0u) | (__ballot(f & 2u) != 0 ? 2u : 0u);
     }
     if (flags & 1u) {
@@ -1021,7 +1040,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
         // general mode: exclusive prefix of candidate counts, then equal runs
         int bad = 0;
         uint32_t carry = 0, tl = 1;
-        for (int c0 = 0; c0 < p.n_chunks; c0 += MT) {
+        for (int c0 = 0; c0 < p.n_chunks; c0 += NT) {
             const int c = c0 + tid;
             uint32_t n = 0;
             if (c < p.n_chunks) {
@@ -1034,14 +1053,14 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
                 n = 0;
             }
             uint32_t tot;
-            const uint32_t inc = block_scan<MT>(n, sm, &tot);
+            const uint32_t inc = block_scan<NT>(n, sm, &tot);
             if (c < p.n_chunks) pre[c] = carry + inc - n;
             carry += tot;
             __syncthreads();
         }
         if (tid == 0) pre[p.n_chunks] = carry;
         const uint32_t total = carry;
-        const uint32_t per = (total + MT - 1) / MT;
+        const uint32_t per = (total + NT - 1) / NT;
         __syncthreads();
         if (__syncthreads_or(bad) || per > REG_CAND) {
             return false;
@@ -1079,8 +1098,8 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
             ms.red[1][wave] = tl;
         }
         __syncthreads();
-        kmax = lds_max_u32<MT / 64>(ms.red[0]);
-        t_lo = lds_max_u32<MT / 64>(ms.red[1]);
+        kmax = lds_max_u32<NT / 64>(ms.red[0]);
+        t_lo = lds_max_u32<NT / 64>(ms.red[1]);
     }
     if (kmax < t_lo) return false;  // no candidate at or above T_lo
     // candidates below T_lo never decide anything: empty their slots
@@ -1102,7 +1121,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
 #pragma unroll
                 for (int i = 0; i < REG_CAND; ++i) n += keys[i] == kmax;
                 uint32_t tot;
-                scan_buf(n, ms, buf, &tot);
+                scan_buf<NT>(n, ms, buf, &tot);
                 if (tot < need) {
                     return false;
                 }
@@ -1124,7 +1143,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
         }
         __syncthreads();
         uint32_t bin, above, in_bin, total;
-        merge_find(ms, need, buf, &bin, &above, &in_bin, &total);
+        merge_find<NT>(ms, need, buf, &bin, &above, &in_bin, &total);
         buf ^= 1;
         if (first && total < need) {  // the k-th key lies below T_lo
             return false;
@@ -1163,7 +1182,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
             // ... and rank it: PARTS threads share an element, part p comparing
             // it with list entries p, p + PARTS, ...; waves whose elements all
             // lie past the bin's end skip the ranking
-            constexpr int PARTS = MT / RESOLVE_MAX;
+            constexpr int PARTS = NT / RESOLVE_MAX;
             constexpr int EPW = 64 / PARTS;  // elements per wave
             if ((uint32_t)(wave * EPW) < in_bin) {
                 const int e = tid / PARTS, part = tid % PARTS;
@@ -1206,7 +1225,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
     }
     const uint32_t packed = (ngt << 16) | neq;
     uint32_t tot;
-    const uint32_t ex = scan_buf(packed, ms, buf, &tot) - packed;
+    const uint32_t ex = scan_buf<NT>(packed, ms, buf, &tot) - packed;
     fence_keys(keys);
     uint32_t tb = ex & 0xFFFFu;
     uint32_t pos = (ex >> 16) + (tb < need_ties ? tb : need_ties);
@@ -1239,7 +1258,7 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
     }
     if (stage) {
         __syncthreads();
-        for (int i = tid; i < kk; i += MT) {
+        for (int i = tid; i < kk; i += NT) {
             oidx[i] = (int32_t)st_id[i];
             if (osc) osc[i] = key_score(ms.stage_key[i] - 1u);
         }
@@ -1247,31 +1266,32 @@ __device__ __forceinline__ bool merge_select(const IndexPlan &p, int q, int kk, 
     return true;
 }
 
-template <int MODE>
-__global__ __launch_bounds__(MT) void index_merge_kernel(IndexPlan p) {
+template <int MODE, int NT>
+__global__ __launch_bounds__(NT) void index_merge_kernel(IndexPlan p) {
     extern __shared__ uint32_t dyn[];
     __shared__ IdxSmem sm;
-    __shared__ MergeSmem ms;
+    __shared__ MergeSmem<NT> ms;
     const int q = blockIdx.x, tid = threadIdx.x;
     const int b = q / p.Tq;
     uint32_t *pre = dyn;                                  // [n_chunks + 1] candidate offsets
     uint32_t *skey = dyn + p.n_chunks + 1;                // [chunk] (exact fallback)
     float *sq = (float *)(skey + p.chunk);                // f32 mode query
-    *(uint4 *)&ms.hist[BPT * tid] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int v = 0; v < MBINS / NT / 4; ++v) *(uint4 *)&ms.hist[MBINS / NT * tid + 4 * v] = make_uint4(0, 0, 0, 0);
     if (MODE == 0) {
         const float *iq = (const float *)p.iq + (size_t)q * p.H * p.dI;
-        for (int i = tid; i < p.H * p.dI; i += MT) sq[i] = iq[i];
+        for (int i = tid; i < p.H * p.dI; i += NT) sq[i] = iq[i];
     }
     const int64_t nvis = visible_entries(p, q);
     const int kk = (int)(nvis < p.k ? nvis : p.k);
     int32_t *oidx = p.out_idx + (size_t)q * p.k;
     float *osc = p.out_score ? p.out_score + (size_t)q * p.k : nullptr;
-    for (int i = kk + tid; i < p.k; i += MT) {
+    for (int i = kk + tid; i < p.k; i += NT) {
         oidx[i] = -1;
         if (osc) osc[i] = 0.f;
     }
     if (kk == 0) return;
-    if (!merge_select(p, q, kk, pre, sm, ms)) exact_fallback<MODE, MT>(p, q, b, nvis, kk, skey, sq, sm);
+    if (!merge_select<NT>(p, q, kk, pre, sm, ms)) exact_fallback<MODE, NT>(p, q, b, nvis, kk, skey, sq, sm);
 }
 
 template <int MODE>
@@ -1291,8 +1311,12 @@ static void launch_mode(const IndexPlan &p, hipStream_t s) {
             hipLaunchKernelGGL(index_score_kernel<MODE>, dim3(p.n_chunks, nq), dim3(IT), (size_t)p.chunk * 4 + q_lds, s,
                                ps);
     }
-    hipLaunchKernelGGL(index_merge_kernel<MODE>, dim3(p.Q), dim3(MT),
-                       (size_t)(p.n_chunks + 1 + p.chunk) * 4 + q_lds, s, p);
+    // Few queries (decode): 1,024 threads per query, whose sixteen waves hide
+    // a lone workgroup's latencies; many (chunked prefill): 512, so that two
+    // workgroups share a compute unit.
+    const size_t m_lds = (size_t)(p.n_chunks + 1 + p.chunk) * 4 + q_lds;
+    if (p.Q >= MERGE_WIDE_Q) hipLaunchKernelGGL((index_merge_kernel<MODE, 512>), dim3(p.Q), dim3(512), m_lds, s, p);
+    else hipLaunchKernelGGL((index_merge_kernel<MODE, 1024>), dim3(p.Q), dim3(1024), m_lds, s, p);
 }
 
 hipError_t launch_index(const IndexPlan &p, hipStream_t s) {

@@ -302,6 +302,25 @@ def test_index_mxfp4_multi_query_chunk_boundaries(rows, k):
         assert np.array_equal(idx1[:, 0], idx[:, i]) and _same_bits(score1[:, 0], score[:, i]), f'query {i}'
 
 
+@pytest.mark.parametrize('k', [64, 1024])
+def test_index_mxfp4_merge_widths(k):
+    """The merge runs 512 threads per query from 512 queries per call and 1,024 below:
+    600 queries made of 6 patterns (same query rows and positions) against a call with
+    the 6 alone, bitwise (ids and scores), and the 6 against the oracle."""
+    rows, P, R = 20000, 6, 100
+    q_pos = np.array([[rows * 4 - 1, 70001, 40003, 9000, 4095, 130]], np.int64)
+    c = _index_case_mx(61 + k, 1, rows, q_pos, k)
+    print(f'index merge widths, k {k}', flush=True)
+    idx6, score6 = _run_index(c)
+    _check_index(c, idx6, score6, c['dkeys'], c['diq'])
+    pat = np.arange(P * R) % P
+    cw = dict(c, q_pos=c['q_pos'][:, pat], ip=c['ip'][:, pat], isc=c['isc'][:, pat], w=c['w'][:, pat])
+    idx, score = _run_index(cw)
+    for j in range(P * R):
+        assert np.array_equal(idx[0, j], idx6[0, pat[j]]), f'ids of query {j}'
+        assert _same_bits(score[0, j], score6[0, pat[j]]), f'scores of query {j}'
+
+
 def test_index_mxfp4_clustered_winners_and_ties():
     q_pos = np.array([[40000 * 4 - 1], [20000]], np.int64)
     c = _index_case_mx(2, 2, 40000, q_pos, 1024, cluster=(0, 3000, 1500), ties=True)
