@@ -418,9 +418,10 @@ __device__ __forceinline__ uint32_t emit_scan(uint32_t v, EmitSmem &em, uint32_t
 }
 
 // PER: entries per thread, in index order (the chunk holds IT x PER).
-template <int PER>
-__device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
-                           const uint32_t *skey, EmitSmem &em) {
+// FULL: the chunk holds IT * PER entries (every slot valid).
+template <int PER, bool FULL>
+__device__ void chunk_emit_impl(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
+                                const uint32_t *skey, EmitSmem &em) {
     static_assert(PER % 4 == 0, "whole 16-byte LDS reads per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
     const size_t rid = (size_t)q * p.n_chunks + chunk;
@@ -435,19 +436,18 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
     }
     bool valid[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) valid[j] = PER * tid + j < cnt;
+    for (int j = 0; j < PER; ++j) valid[j] = FULL || PER * tid + j < cnt;
     uint32_t thr = 0;  // emit valid keys >= thr
     if (cnt > s_want) {
         // range of the valid keys; the histogram is cleared in the same round
-        uint32_t mx = 0u, nmn = 0u;  // max and ~min
+        uint32_t mx = 0u, mn = 0xFFFFFFFFu;
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (valid[j]) {
-                mx = key[j] > mx ? key[j] : mx;
-                nmn = ~key[j] > nmn ? ~key[j] : nmn;
-            }
+        for (int j = 0; j < PER; ++j) {
+            mx = __builtin_elementwise_max(mx, valid[j] ? key[j] : 0u);
+            mn = __builtin_elementwise_min(mn, valid[j] ? key[j] : 0xFFFFFFFFu);
+        }
         mx = wave_max_u32(mx);
-        nmn = wave_max_u32(nmn);
+        uint32_t nmn = wave_max_u32(~mn);
         *(uint4 *)&em.hist[8 * tid] = make_uint4(0, 0, 0, 0);
         *(uint4 *)&em.hist[8 * tid + 4] = make_uint4(0, 0, 0, 0);
         if (lane == 0) {
@@ -470,13 +470,20 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
             int top = 31 - __builtin_clz(diff);  // highest differing bit; bits above it are common
             uint32_t prefix = (uint32_t)(((uint64_t)mx >> (top + 1)) << (top + 1));
             uint32_t need = (uint32_t)s_want, above_all = 0;
+            bool refining = false;  // the first digit: every valid key shares the bits above top
             while (true) {
                 const int sh = top + 1 - EBITS > 0 ? top + 1 - EBITS : 0;
                 const uint32_t dmask = (2u << (top - sh)) - 1u;
+                if (!refining) {
 #pragma unroll
-                for (int j = 0; j < PER; ++j)
-                    if (valid[j] && ((uint64_t)key[j] >> (top + 1)) == ((uint64_t)prefix >> (top + 1)))
-                        atomicAdd(&em.hist[(key[j] >> sh) & dmask], 1u);
+                    for (int j = 0; j < PER; ++j)
+                        if (valid[j]) atomicAdd(&em.hist[(key[j] >> sh) & dmask], 1u);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < PER; ++j)
+                        if (valid[j] && ((uint64_t)key[j] >> (top + 1)) == ((uint64_t)prefix >> (top + 1)))
+                            atomicAdd(&em.hist[(key[j] >> sh) & dmask], 1u);
+                }
                 __syncthreads();
                 // thread t owns bins EBINS-8(t+1) .. EBINS-8t-1, highest first
                 const uint4 h1 = *(const uint4 *)&em.hist[EBINS - 8 * tid - 4];
@@ -512,6 +519,7 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
                 *(uint4 *)&em.hist[8 * tid + 4] = make_uint4(0, 0, 0, 0);
                 __syncthreads();
                 top = sh - 1;
+                refining = true;
             }
             thr = prefix;
         }
@@ -544,6 +552,13 @@ __device__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int
         meta[0] = total;
         meta[1] = thr;
     }
+}
+
+template <int PER>
+__device__ __forceinline__ void chunk_emit(const IndexPlan &p, int q, int chunk, int64_t c0, int cnt, int s_want,
+                                           const uint32_t *skey, EmitSmem &em) {
+    if (cnt == IT * PER) chunk_emit_impl<PER, true>(p, q, chunk, c0, cnt, s_want, skey, em);
+    else chunk_emit_impl<PER, false>(p, q, chunk, c0, cnt, s_want, skey, em);
 }
 
 // ------------------------------------------------------------- merge ----
