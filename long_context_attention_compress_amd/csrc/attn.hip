@@ -299,6 +299,7 @@ struct MxSmem {
     int32_t rows[MAX_KS];       // row of each key of the split; bit 30 marks a window row; -1: no key
     float xml[NS > 1 ? 2 * AT : 1];
     AppRow app;
+    uint32_t sync[NS];         // per-stream round counters (two streams)
 };
 
 // A tile in flight: the raw loads and which of them hold a key. Slots without
@@ -635,6 +636,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         sm.rcos[tid] = cs;
         sm.rsc[tid] = make_float2((float)sn, (float)cs);
     }
+    if (NS > 1 && tid < NS) sm.sync[tid] = 0u;
     __syncthreads();
 
     // Scores are kept in log2 units: the softmax scale times log2(e) multiplies
@@ -805,10 +807,31 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     // other (whose loads were issued a round earlier), and issues the loads of
     // tile r + 2 into the register set that staging freed.
     TileBuf &b0 = sm.tb[stream][0], &b1 = sm.tb[stream][1];
+    // With two streams each round synchronises the stream's own four waves
+    // (its tiles and buffers are its own): an LDS counter per stream that
+    // every wave adds one to once its LDS stores are done, then waits for
+    // (a bounded wait: every wave leaves it), so that one stream's late tile
+    // does not hold the other back.
+    uint32_t sync_gen = 0;
+    auto round_sync = [&]() {
+        if (NS == 1) {
+            __syncthreads();
+            return;
+        }
+        sync_gen += AT / 64;
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS stores are done
+        asm volatile("" ::: "memory");
+        if (lane == 0) __hip_atomic_fetch_add(&sm.sync[stream], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int spin = 0; spin < (1 << 16); ++spin) {
+            if (__hip_atomic_load(&sm.sync[stream], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= sync_gen) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    };
     __syncthreads();  // the resolved rows and the appended row are published
     stage_tile(RA, sm.rows, b0, stream * TK, n_rel, tids, sm.app, cur, sc2);
     load_tile(lsrc, sm.rows, (stream + 2 * NS) * TK, n_rel, RA, tids);
-    __syncthreads();
+    round_sync();
     // The loop runs whole pairs of rounds and has no exit but its own test:
     // an exit from inside would join the loop's paths in one block, where the
     // compiler has to assume that the tile staged first is the newest load
@@ -819,18 +842,18 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         if (ta < n_tiles) compute(b0);
         stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur, sc2);
         load_tile(lsrc, sm.rows, (tb_ + 2 * NS) * TK, n_rel, RB, tids);
-        __syncthreads();
+        round_sync();
         if (tb_ < n_tiles) compute(b1);
         stage_tile(RA, sm.rows, b0, (ta + 2 * NS) * TK, n_rel, tids, sm.app, cur, sc2);
         load_tile(lsrc, sm.rows, (ta + 4 * NS) * TK, n_rel, RA, tids);
-        __syncthreads();
+        round_sync();
     }
     if (i < n_rounds) {  // uniform
         const int ta = stream + NS * i, tb_ = stream + NS * (i + 1);
         if (ta < n_tiles) compute(b0);
         if (i + 1 < n_rounds) {
             stage_tile(RB, sm.rows, b1, tb_ * TK, n_rel, tids, sm.app, cur, sc2);
-            __syncthreads();
+            round_sync();
             if (tb_ < n_tiles) compute(b1);
         }
     }
