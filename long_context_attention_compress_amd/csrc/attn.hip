@@ -62,16 +62,25 @@ struct KeyInfo {
                      // a linear store's row count when that position lies past it
 };
 
-// (t + 1) / m and pos % ring in 32 bits where the operands fit (every
-// position below 2^32); the 64-bit forms otherwise.
-__device__ __forceinline__ int64_t div_pos(int64_t x, int64_t d) {
-    return (uint64_t)x < (1ull << 32) ? (int64_t)((uint32_t)x / (uint32_t)d) : x / d;
-}
-__device__ __forceinline__ int64_t mod_pos(int64_t x, int64_t d) {
-    return (uint64_t)x < (1ull << 32) ? (int64_t)((uint32_t)x % (uint32_t)d) : x % d;
+// Division of a position by a divisor fixed for the call (m, the ring):
+// below 2^31 a multiply and a shift with host-made constants (the quotient
+// is exact: the constant is 2^s' / d rounded up, with s' = 31 + ceil(log2 d),
+// and its error times x stays below 2^s' / d), the 64-bit division otherwise.
+__device__ __forceinline__ int64_t div_fixed(int64_t x, int64_t d, uint32_t mul, uint32_t sh) {
+    return (uint64_t)x < (1ull << 31) ? (int64_t)(((uint64_t)x * mul) >> sh) : x / d;
 }
 
-__device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int64_t t) {
+// Host side: the multiplier and shift of div_fixed for 1 <= d < 2^31.
+inline void div_consts(int64_t d, uint32_t *mul, uint32_t *sh) {
+    int s = 0;
+    while (((int64_t)1 << s) < d) ++s;
+    const int k = 31 + s;
+    const unsigned __int128 num = (unsigned __int128)1 << k;
+    *mul = (uint32_t)((num + (unsigned __int128)d - 1) / (unsigned __int128)d);
+    *sh = (uint32_t)k;
+}
+
+__device__ __forceinline__ KeyInfo key_info(const KeyConsts &kc, int64_t t) {
     KeyInfo ki;
     ki.t = t;
     ki.wrow0 = 0;
@@ -80,17 +89,15 @@ __device__ __forceinline__ KeyInfo key_info(const AttnPlan &p, int64_t t) {
         ki.n_win = 0;
         return ki;
     }
-    ki.n_win = (int32_t)(ki.t + 1 < p.W ? ki.t + 1 : p.W);
+    ki.n_win = (int32_t)(ki.t + 1 < kc.W ? ki.t + 1 : kc.W);
     const int64_t pos0 = ki.t - ki.n_win + 1;
-    const int64_t wrow0 = p.wk.ring > 0 ? mod_pos(pos0, p.wk.ring) : pos0;
-    ki.wrow0 = (int32_t)(wrow0 < p.wk.rows ? wrow0 : p.wk.rows);
-    if (!p.has_ent) ki.n_list = 0;
-    else if (p.sparse) ki.n_list = p.k;
+    int64_t wrow0 = pos0;
+    if (kc.ring > 0) wrow0 = pos0 - div_fixed(pos0, kc.ring, kc.r_mul, (kc.misc >> 16) & 0xff) * kc.ring;
+    ki.wrow0 = (int32_t)(wrow0 < kc.wrows ? wrow0 : kc.wrows);
+    if (kc.misc & 1u) ki.n_list = kc.cap;
     else {
-        int64_t n = div_pos(ki.t + 1, p.m);
-        if (n > p.ek.rows) n = p.ek.rows;
-        if (p.n_override >= 0 && n > p.n_override) n = p.n_override;
-        ki.n_list = (int32_t)n;
+        const int64_t n = div_fixed(ki.t + 1, kc.m, kc.m_mul, (kc.misc >> 8) & 0xff);
+        ki.n_list = (int32_t)(n < kc.cap ? n : kc.cap);
     }
     return ki;
 }
@@ -116,19 +123,17 @@ constexpr int32_t WIN_BIT = 1 << 30;  // a row code with this bit set is a windo
 // -1 for a slot without a key. `id` is the selected id when j is a sparse
 // list entry (unused otherwise). The same function serves the per-split rows
 // table and the rows of the first two tiles, which are resolved per lane.
-__device__ __forceinline__ int32_t key_code(const AttnPlan &p, const KeyInfo &ki, int32_t j, int32_t id) {
-    if (j < ki.n_list) {
-        const int32_t e = p.sparse ? (j < p.k ? id : -1) : j;
-        return (e >= 0 && e < (int32_t)p.ek.rows) ? e : -1;
-    }
+// Both candidates are formed and one is selected (no per-lane branches).
+__device__ __forceinline__ int32_t key_code(const KeyConsts &kc, const KeyInfo &ki, int32_t j, int32_t id) {
+    const int32_t e = (kc.misc & 1u) ? id : j;
+    const int32_t ec = (uint32_t)e < (uint32_t)kc.erows ? e : -1;
+    // window key w at position t - n_win + 1 + w; its ring row without a
+    // division: w < n_win <= ring, so one wrap at most
     const int32_t w = j - ki.n_list;
-    if (w >= ki.n_win) return -1;
-    // position t - n_win + 1 + w; its ring row without a division: w < n_win
-    // <= ring, so one wrap at most
     int32_t row = ki.wrow0 + w;
-    const int32_t ring = (int32_t)p.wk.ring;
-    if (ring > 0 && row >= ring) row -= ring;
-    return row < (int32_t)p.wk.rows ? row | WIN_BIT : -1;
+    row = (kc.ring > 0 && row >= kc.ring) ? row - kc.ring : row;
+    const int32_t wc = ((uint32_t)w < (uint32_t)ki.n_win && row < kc.wrows) ? (row | WIN_BIT) : -1;
+    return j < ki.n_list ? ec : wc;
 }
 
 // ------------------------------------------------------------------ F32 ----
@@ -149,7 +154,7 @@ __global__ __launch_bounds__(AT) void attn_f32_kernel(AttnPlan p) {
     const int tid = threadIdx.x;
     const int q = blockIdx.y + p.q_base, split = blockIdx.x;
     const int b = q / p.Tq;
-    const KeyInfo ki = key_info(p, p.q_pos[q]);
+    const KeyInfo ki = key_info(p.kc, p.q_pos[q]);
     const float *qin = (const float *)p.q + (size_t)q * H * D;
     const int Dn = D - ROPE_DIM;
     for (int i = tid; i < H * D; i += AT) {
@@ -537,7 +542,13 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     const int H = p.H;
     const bool active = wave < NW;
     const int head = 16 * wave + col;
+    // The key-list constants are read with the plan's lines and pinned in
+    // scalar registers (the empty asm keeps the compiler from loading them
+    // again where they are used, one wait per load, after the position).
+    KeyConsts kc = p.kc;
     touch_args(p);  // every line of the plan in one scalar round trip
+    asm volatile("" : "+s"(kc.W), "+s"(kc.ring), "+s"(kc.wrows), "+s"(kc.erows), "+s"(kc.cap), "+s"(kc.misc),
+                 "+s"(kc.m_mul), "+s"(kc.r_mul), "+s"(kc.m));
     // The position (a pointer, then the value: the longest chain of the
     // prologue) is asked for first, as a vector load whose address the
     // compiler cannot prove uniform, and read into a scalar only where it is
@@ -597,13 +608,13 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
     }
     const int64_t t_pos = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(t_lane >> 32)) << 32) |
                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)t_lane));
-    const KeyInfo ki = key_info(p, t_pos);
+    const KeyInfo ki = key_info(kc, t_pos);
     const int64_t n_keys = ki.n_list + ki.n_win;
     const int64_t j1 = j0 + p.keys_per_split < n_keys ? j0 + p.keys_per_split : n_keys;
     const int n_rel = j1 > j0 ? (int)(j1 - j0) : 0;
     TileRegs RA, RB;
     {
-        auto first = [&](int rel, int32_t id) { return rel < n_rel ? key_code(p, ki, (int32_t)j0 + rel, id) : -1; };
+        auto first = [&](int rel, int32_t id) { return rel < n_rel ? key_code(kc, ki, (int32_t)j0 + rel, id) : -1; };
         const bool sl = tids < 2 * TK;  // threads 0..63 load the scales
         load_tile_codes(lsrc, first(ra, fid[0]), sl ? first(sa, fid[2]) : -1, RA);
         load_tile_codes(lsrc, first(rb, fid[1]), sl ? first(sb, fid[3]) : -1, RB);
@@ -627,7 +638,7 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
 #pragma unroll
     for (int u = 0; u < IDS; ++u) {
         const int i = tid + AT * NS * u;
-        if (i < n_rel) sm.rows[i] = key_code(p, ki, (int32_t)j0 + i, ids[u]);
+        if (i < n_rel) sm.rows[i] = key_code(kc, ki, (int32_t)j0 + i, ids[u]);
     }
     if (tid < ROPE_PAIRS) {
         double sn, cs;
@@ -1089,7 +1100,25 @@ static void launch_attn_slice(const AttnPlan &p, int nq, hipStream_t s) {
     }
 }
 
-hipError_t launch_attn(const AttnPlan &p, hipStream_t s) {
+hipError_t launch_attn(const AttnPlan &plan, hipStream_t s) {
+    AttnPlan p = plan;
+    KeyConsts &kc = p.kc;
+    kc.W = p.W;
+    kc.ring = (int32_t)p.wk.ring;
+    kc.wrows = (int32_t)p.wk.rows;
+    kc.erows = p.has_ent ? (int32_t)p.ek.rows : 0;
+    int64_t cap = 0;
+    if (p.has_ent) {
+        cap = p.sparse ? p.k : p.ek.rows;
+        if (!p.sparse && p.n_override >= 0 && p.n_override < cap) cap = p.n_override;
+    }
+    kc.cap = (int32_t)cap;
+    uint32_t m_sh = 0, r_sh = 0;
+    div_consts(p.m, &kc.m_mul, &m_sh);
+    kc.r_mul = 0;
+    if (kc.ring > 0) div_consts(kc.ring, &kc.r_mul, &r_sh);
+    kc.misc = (p.sparse ? 1u : 0u) | (m_sh << 8) | (r_sh << 16);
+    kc.m = p.m;
     for (int q0 = 0; q0 < p.Q; q0 += MAX_GRID_Y) {
         AttnPlan ps = p;
         ps.q_base = q0;

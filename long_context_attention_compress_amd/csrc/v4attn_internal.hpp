@@ -81,7 +81,24 @@ struct IndexPlan {
     int32_t *reg_idx;    // [Q][n_chunks][region_cap]
 };
 
+// What a query's key list needs besides the query position, in one
+// block at the start of the plan, so that the first scalar loads bring it in
+// before the position arrives (launch_attn fills it from the plan's other
+// fields). Rows and counts are below 2^30 (the host checks).
+struct KeyConsts {
+    int32_t W;       // window length
+    int32_t ring;    // window stores' ring (0: linear)
+    int32_t wrows;   // window store rows
+    int32_t erows;   // entry store rows (0 without entries)
+    int32_t cap;     // list length bound: k (sparse), else the entry rows capped by the override; 0 without entries
+    uint32_t misc;   // bit 0: sparse; bits 8..15: m_sh; bits 16..23: r_sh
+    uint32_t m_mul;  // x / m == (x * m_mul) >> m_sh for 0 <= x < 2^31 (x as 64-bit product)
+    uint32_t r_mul;  // x / ring == (x * r_mul) >> r_sh likewise (ring > 0)
+    int32_t m;       // positions per entry (1 without entries)
+};
+
 struct AttnPlan {
+    KeyConsts kc;
     int Q, Tq, H, D, W, m;
     int q_base;        // first query of this launch (attention kernels)
     int sparse;        // 1: key list is idx[q][0..k); 0: entries 0..n_ent-1
