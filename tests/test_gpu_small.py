@@ -522,6 +522,39 @@ def test_attn_dense(fmt, override):
             assert_close_rms(o[b, i], ro, tol, f'o b{b} i{i}')
 
 
+# Positions past 2^31 take the 64-bit divisions of the key-list geometry (the
+# entry count (t + 1) // m and the window's ring slot); a large m keeps the
+# entry store small while the division still decides the count: with
+# m = 8,388,617, t + 1 = 256 m is the first position past 2^31 that sees 256
+# entries, and t + 1 = 255 m (below 2^31) a boundary of the fast path.
+BIG_M = 8388617
+
+
+@pytest.mark.parametrize('q_pos', [[256 * BIG_M - 2, 256 * BIG_M - 1], [255 * BIG_M - 2, 255 * BIG_M - 1]])
+def test_attn_positions_past_2_31(q_pos):
+    B, Tq, H, D, rows = 1, 2, 64, 192, 300
+    q_pos = np.array([q_pos], np.int64)
+    c = _attn_case(15, B, Tq, H, D, rows, q_pos, 'fp8', ring=200)
+    ek, ev, wk, wv = _stores(c)
+    print(f'attn positions {q_pos.tolist()}', flush=True)
+    o = v4.hca_attn(_qdev(c), dev(q_pos), ek, ev, BIG_M, wk, wv, c['W'])
+    g = np.random.default_rng(16)
+    k = 64
+    idx = np.stack([np.sort(g.choice(rows, k, replace=False)) for _ in range(Tq)])[None].astype(np.int32)
+    os_ = v4.sparse_window_attn(_qdev(c), dev(q_pos), ek, ev, 4, wk, wv, c['W'], dev(idx))
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    os_ = os_.float().cpu().numpy()
+    for i in range(Tq):
+        t = int(q_pos[0, i])
+        n = min((t + 1) // BIG_M, rows)
+        assert n in (254, 255, 256)
+        ro, _ = _oracle_attn(c, 0, i, np.arange(n))
+        assert_close_rms(o[0, i], ro, TOL_BF16, f'dense o i{i}')
+        ro, _ = _oracle_attn(c, 0, i, idx[0, i])
+        assert_close_rms(os_[0, i], ro, TOL_BF16, f'sparse o i{i}')
+
+
 def test_more_queries_than_one_launch_row():
     """70,000 queries in one call, more than one launch takes along the query axis, so
     the library splits it: the index and dense attention, with query rows drawn from 64
