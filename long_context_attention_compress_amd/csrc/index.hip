@@ -200,12 +200,13 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
     constexpr int NW = IT / 64, BATCH = 4;
     constexpr int STRIDE = NW * BATCH;               // tiles per batch over the NW waves
     constexpr int NB = IDX_CHUNK / (16 * STRIDE);    // batches per wave
-    static_assert(NB * 16 * STRIDE == IDX_CHUNK && NB % 2 == 0, "a chunk is an even number of batches");
+    constexpr int DEPTH = 3;                         // batches in flight per wave
+    static_assert(NB * 16 * STRIDE == IDX_CHUNK && NB >= DEPTH, "a chunk is at least DEPTH batches");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
 
-    // Issue order: the query's raw operands, then key batches 0 and 1; the
-    // query is first used after both batches are issued. The memory clobbers
+    // Issue order: the query's raw operands, then the first DEPTH key batches;
+    // the query is first used after they are all issued. The memory clobbers
     // pin that order in the IR, the scheduling barriers in the machine
     // scheduler, and the register fences keep every use of the query values
     // (even their unpacking) behind the key loads.
@@ -235,8 +236,8 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
     const uint32_t kbytes = (uint32_t)(cnt - 1) * krs + 64u, sbytes = (uint32_t)(cnt - 1) * srs + 4u;
     const uint32_t kvo = (uint32_t)(wave * 16 + col) * krs + 16u * grp;  // this lane's quarter in tile `wave`
     const uint32_t svo = (uint32_t)(wave * 16 + col) * srs;              // the row's four exponents (one word)
-    v4i ka[BATCH], kb[BATCH];
-    uint32_t sa[BATCH], sb[BATCH];
+    v4i kbuf[DEPTH][BATCH];
+    uint32_t sbuf[DEPTH][BATCH];
     auto issue = [&](v4i (&kv)[BATCH], uint32_t (&sv)[BATCH], int bi) {
 #pragma unroll
         for (int u = 0; u < BATCH; ++u) {
@@ -252,9 +253,12 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
             sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, svo, 0, 2);
         }
     };
-    issue(ka, sa, 0);
-    __builtin_amdgcn_sched_barrier(0);  // batch 0 (keys and exponents) wholly ahead of batch 1
-    issue(kb, sb, 1);
+    // each batch (keys and exponents) wholly ahead of the next
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+        issue(kbuf[i], sbuf[i], i);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -312,18 +316,15 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
         finish(part, bi);
     };
     if (FASTOK) {
-        // two batches in flight: batch bi + 2 is issued as soon as bi is consumed
-        // (scheduling barriers around each issue keep the next batch's work from
-        // being hoisted above it, which would wait for that batch's data first)
+        // DEPTH batches in flight: batch bi + DEPTH is issued into the registers
+        // of batch bi as soon as bi is consumed (scheduling barriers around each
+        // issue keep the next batch's work from being hoisted above it, which
+        // would wait for that batch's data first)
 #pragma unroll
-        for (int bi = 0; bi < NB; bi += 2) {
-            consume(ka, sa, bi);
+        for (int bi = 0; bi < NB; ++bi) {
+            consume(kbuf[bi % DEPTH], sbuf[bi % DEPTH], bi);
             __builtin_amdgcn_sched_barrier(0);
-            if (bi + 2 < NB) issue(ka, sa, bi + 2);
-            __builtin_amdgcn_sched_barrier(0);
-            consume(kb, sb, bi + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            if (bi + 3 < NB) issue(kb, sb, bi + 3);
+            if (bi + DEPTH < NB) issue(kbuf[bi % DEPTH], sbuf[bi % DEPTH], bi + DEPTH);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -332,11 +333,11 @@ __device__ void score_chunk_mx(const IndexPlan &p, int q, int b, int64_t c0, int
     // separate loop so that its registers never add to the fast pass's
     if (redo) {
         for (int bi = 0; bi < NB; ++bi) {
-            issue(ka, sa, bi);
-            unpack(sa);
+            issue(kbuf[0], sbuf[0], bi);
+            unpack(sbuf[0]);
             float part[BATCH];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) part[u] = head_sum<NT, false>(A, sA, ka[u], sa[u], wv);
+            for (int u = 0; u < BATCH; ++u) part[u] = head_sum<NT, false>(A, sA, kbuf[0][u], sbuf[0][u], wv);
             finish(part, bi);
         }
     }
