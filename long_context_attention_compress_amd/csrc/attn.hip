@@ -63,9 +63,11 @@ struct KeyInfo {
 };
 
 // Division of a position by a divisor fixed for the call (m, the ring):
-// below 2^31 a multiply and a shift with host-made constants (the quotient
-// is exact: the constant is 2^s' / d rounded up, with s' = 31 + ceil(log2 d),
-// and its error times x stays below 2^s' / d), the 64-bit division otherwise.
+// below 2^31 a multiply and a shift with host-made constants, the 64-bit
+// division otherwise. The quotient is exact: with s' = 31 + ceil(log2 d) and
+// M = ceil(2^s' / d), x M / 2^s' exceeds x / d by x (M d - 2^s') / (d 2^s'),
+// which is below 1 / d (x < 2^31 and M d - 2^s' < d <= 2^(s' - 31)), too
+// little to reach the next integer.
 __device__ __forceinline__ int64_t div_fixed(int64_t x, int64_t d, uint32_t mul, uint32_t sh) {
     return (uint64_t)x < (1ull << 31) ? (int64_t)(((uint64_t)x * mul) >> sh) : x / d;
 }
