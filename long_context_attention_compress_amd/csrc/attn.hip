@@ -920,13 +920,18 @@ __global__ __launch_bounds__(AT * NS, 2) void attn_mx_kernel(AttnPlan p) {
         if (g == 0 && p.lse)
             p.lse[(size_t)q * H + head] = lrun > 0.f ? (mrun + log2f(lrun)) * 0.6931471805599453f : -__builtin_inff();
     } else {
+        // Non-temporal stores: the partials of all splits (7-10 MB per decode
+        // launch) are read once, by the combine, mostly on other XCDs. Written
+        // as ordinary lines they made the decode step about 1.5 us slower
+        // (measured; the likely cause is their write-back from this XCD's L2
+        // at the kernel's end).
         const size_t base = ((size_t)q * p.n_split + split) * H + head;
         float *po = p.part_o + base * MD;
 #pragma unroll
-        for (int dt = 0; dt < 12; ++dt) *(v4f *)(po + 16 * dt + 4 * g) = O[dt];
+        for (int dt = 0; dt < 12; ++dt) __builtin_nontemporal_store(O[dt], (v4f *)(po + 16 * dt + 4 * g));
         if (g == 0) {
-            p.part_ml[base * 2] = mrun;
-            p.part_ml[base * 2 + 1] = lrun;
+            __builtin_nontemporal_store(mrun, &p.part_ml[base * 2]);
+            __builtin_nontemporal_store(lrun, &p.part_ml[base * 2 + 1]);
         }
     }
 }
