@@ -492,6 +492,15 @@ __device__ __forceinline__ bf16x8 ld16(const __bf16 *p) { return *(const bf16x8 
 // Two floats as hi + lo BF16 terms (hi = RNE(x), lo = RNE(x - hi)) into
 // elements e, e+1 of hi and lo, one conversion instruction per pair.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// The combines read the split partials once, with non-temporal loads: with
+// ordinary loads the 7-10 MB of a decode call's partials stayed in the L2s,
+// and the decode step took 2.6 us longer (the combine itself and the next
+// kernels, measured).
+__device__ __forceinline__ float2 ld_ml(const float *a) {
+    const f32x2 v = __builtin_nontemporal_load((const f32x2 *)a);
+    return make_float2(v[0], v[1]);
+}
 __device__ __forceinline__ void split_bf16x2(float a, float b, bf16x8 &hi, bf16x8 &lo, int e) {
     const bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);
     const bf16x2 l = __builtin_convertvector((f32x2){a - (float)h[0], b - (float)h[1]}, bf16x2);
@@ -980,15 +989,14 @@ __global__ __launch_bounds__(G * 192) void attn_combine_kernel(AttnPlan p) {
 #pragma unroll
     for (int i = 0; i < CMB_CHUNK; ++i) {
         const int sp = gi + G * i;
-        v[i] = (own && sp < S) ? po[(size_t)sp * stride] : 0.f;
+        v[i] = (own && sp < S) ? __builtin_nontemporal_load(&po[(size_t)sp * stride]) : 0.f;
     }
     float2 ml[NK];
     float mloc = -__builtin_inff();
 #pragma unroll
     for (int k = 0; k < NK; ++k) {
         const int sp = tid + CMB_T * k;
-        ml[k] = sp < S ? *(const float2 *)&p.part_ml[((base + (size_t)sp * H) + h) * 2]
-                       : make_float2(-__builtin_inff(), 0.f);
+        ml[k] = sp < S ? ld_ml(&p.part_ml[((base + (size_t)sp * H) + h) * 2]) : make_float2(-__builtin_inff(), 0.f);
         mloc = __builtin_fmaxf(mloc, ml[k].x);
     }
     mloc = wave_max(mloc);
@@ -1023,7 +1031,7 @@ __global__ __launch_bounds__(G * 192) void attn_combine_kernel(AttnPlan p) {
 #pragma unroll
         for (int i = 0; i < CMB_CHUNK; ++i) {
             const int sp = s0 + gi + G * i;
-            v[i] = (own && sp < S) ? po[(size_t)sp * stride] : 0.f;
+            v[i] = (own && sp < S) ? __builtin_nontemporal_load(&po[(size_t)sp * stride]) : 0.f;
         }
 #pragma unroll
         for (int i = 0; i < CMB_CHUNK; ++i) {
@@ -1066,11 +1074,11 @@ __global__ __launch_bounds__(192) void attn_combine_w_kernel(AttnPlan p) {
     float v[NS];
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-        v[i] = row[dd];
+        v[i] = __builtin_nontemporal_load(&row[dd]);
         row += i + 1 < S ? stride : 0;
     }
     const int j = lane < S ? lane : S - 1;
-    const float2 ml = *(const float2 *)&p.part_ml[((base + (size_t)j * H) + h) * 2];
+    const float2 ml = ld_ml(&p.part_ml[((base + (size_t)j * H) + h) * 2]);
     __builtin_amdgcn_sched_barrier(0);
     const float mj = lane < S ? __builtin_fmaxf(-__builtin_inff(), ml.x) : -__builtin_inff();
     const float M = wave_max_dpp(mj);
