@@ -7,8 +7,9 @@
 // große Wirkung", section "Komprimierte Erinnerung für längere Kontexte"]: the
 // last 64 values carry RoPE and stay BF16, the rest is FP8.
 //
-// One wave per (entry, batch element, output) for long blocks, three waves
-// (one per output) in one workgroup for blocks of up to four tokens. The gate weights, the RoPE rotation and the
+// Four waves per (entry, batch element, output) for long blocks (a quarter
+// of the tokens each), three waves (one per output) in one workgroup for
+// blocks of up to four tokens. The gate weights, the RoPE rotation and the
 // weighted sum are evaluated in float64 and the entry is rounded to float32
 // before it is encoded, so every encoding decision (FP8 scale and codes, BF16
 // rounding, MX exponent and E2M1 codes) is taken on a float32 value.
@@ -116,28 +117,38 @@ __device__ __forceinline__ void store_ik_value(const IkView &s, int b, int64_t e
         ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[d >> 5] = nbad ? 0xFF : (uint8_t)(E + 127);
 }
 
-// sum_r alpha[r] * x(r) over r < m in float64, as four interleaved partial
-// sums (independent FMA chains) added pairwise at the end.
+// sum_r alpha[r] * x(r) over r0 <= r < r1 in float64, as four interleaved
+// partial sums (independent FMA chains) added pairwise at the end.
 template <class F>
-__device__ __forceinline__ double pooled(const double *alpha, int m, F x) {
+__device__ __forceinline__ double pooled(const double *alpha, int r0, int r1, F x) {
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int r = 0;
-    for (; r + 4 <= m; r += 4) {
+    int r = r0;
+    for (; r + 4 <= r1; r += 4) {
         a0 += alpha[r] * x(r);
         a1 += alpha[r + 1] * x(r + 1);
         a2 += alpha[r + 2] * x(r + 2);
         a3 += alpha[r + 3] * x(r + 3);
     }
-    for (; r < m; ++r) a0 += alpha[r] * x(r);
+    for (; r < r1; ++r) a0 += alpha[r] * x(r);
     return (a0 + a1) + (a2 + a3);
 }
 
-// One wave per (block, batch element, output): blockIdx.z = 0 the K entry,
-// 1 the V entry, 2 the indexer key; each evaluates the gate softmax itself.
+// Waves per (block, batch element, output) of the general kernel: wave w
+// pools the w-th quarter of the block's tokens, and wave 0 adds the four
+// float64 partial sums in a fixed order ((w0 + w1) + (w2 + w3)) before the
+// entry is rounded to float32 and encoded. (With one wave per output the
+// m = 128 blocks of a chunked prefill ran as 128 waves on the whole device,
+// each through 128 tokens and their float64 sin/cos: 120 us per call.)
+constexpr int CW = 4;
+
+// One workgroup per (block, batch element, output): blockIdx.z = 0 the K
+// entry, 1 the V entry, 2 the indexer key.
 template <int ACT>
-__global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
+__global__ __launch_bounds__(64 * CW) void compress_kernel(CompressPlan p) {
     __shared__ double alpha[MAX_M];
+    __shared__ double part[CW][6][64];  // per wave: up to four pooled dims per lane, then the RoPE pair
     const int lane = lane_id();
+    const int wave = (int)(threadIdx.x >> 6);
     const int j = blockIdx.x;  // block within the chunk
     const int b = blockIdx.y;
     const int role = blockIdx.z;
@@ -149,35 +160,39 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
     const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
     if (!geo.ok || (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik)) return;  // uniform per workgroup
 
-    // alpha_r = softmax_r(gate + pos_bias), float64
-    double zmax = -__builtin_inf();
-    for (int r = lane; r < m; r += 64) {
-        double z = (double)p.gate[(int64_t)b * p.t_new + tok0 + r] + (double)p.pos_bias[r];
-        alpha[r] = z;
-        zmax = z > zmax ? z : zmax;
+    // alpha_r = softmax_r(gate + pos_bias), float64, by wave 0
+    if (wave == 0) {
+        double zmax = -__builtin_inf();
+        for (int r = lane; r < m; r += 64) {
+            double z = (double)p.gate[(int64_t)b * p.t_new + tok0 + r] + (double)p.pos_bias[r];
+            alpha[r] = z;
+            zmax = z > zmax ? z : zmax;
+        }
+        zmax = wave_max(zmax);
+        double zsum = 0.0;
+        for (int r = lane; r < m; r += 64) {
+            double e = exp(alpha[r] - zmax);
+            alpha[r] = e;
+            zsum += e;
+        }
+        zsum = wave_sum(zsum);
+        for (int r = lane; r < m; r += 64) alpha[r] = alpha[r] / zsum;
     }
-    zmax = wave_max(zmax);
-    double zsum = 0.0;
-    for (int r = lane; r < m; r += 64) {
-        double e = exp(alpha[r] - zmax);
-        alpha[r] = e;
-        zsum += e;
-    }
-    zsum = wave_sum(zsum);
-    for (int r = lane; r < m; r += 64) alpha[r] = alpha[r] / zsum;
     __syncthreads();
+    // this wave's tokens
+    const int chunk = (m + CW - 1) / CW;
+    const int r0 = wave * chunk < m ? wave * chunk : m;
+    const int r1 = r0 + chunk < m ? r0 + chunk : m;
 
     if (role < 2) {
         // values (never rotated) and keys (rotated at each token's position)
         const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
         const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * D;
         const void *src = role == 0 ? p.raw_k : p.raw_v;
-        float nope[4];
         for (int i = 0; i < nit; ++i)
-            nope[i] = (float)pooled(alpha, m, [&](int r) {
+            part[wave][i][lane] = pooled(alpha, r0, r1, [&](int r) {
                 return load_act<ACT>(src, rowbase + (int64_t)r * D + lane + 64 * i);
             });
-        float rx = 0.0f, ry = 0.0f;
         if (lane < ROPE_PAIRS) {
             const double f = p.inv_freq[lane];
             auto pair = [&](int r, double *x, double *y) {
@@ -192,8 +207,8 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
                 }
             };
             double ax[4] = {0.0, 0.0, 0.0, 0.0}, ay[4] = {0.0, 0.0, 0.0, 0.0};
-            int r = 0;
-            for (; r + 4 <= m; r += 4)
+            int r = r0;
+            for (; r + 4 <= r1; r += 4)
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     double x, y;
@@ -201,28 +216,44 @@ __global__ __launch_bounds__(64) void compress_kernel(CompressPlan p) {
                     ax[u] += alpha[r + u] * x;
                     ay[u] += alpha[r + u] * y;
                 }
-            for (; r < m; ++r) {
+            for (; r < r1; ++r) {
                 double x, y;
                 pair(r, &x, &y);
                 ax[0] += alpha[r] * x;
                 ay[0] += alpha[r] * y;
             }
-            rx = (float)((ax[0] + ax[1]) + (ax[2] + ax[3]));
-            ry = (float)((ay[0] + ay[1]) + (ay[2] + ay[3]));
+            part[wave][4][lane] = (ax[0] + ax[1]) + (ax[2] + ax[3]);
+            part[wave][5][lane] = (ay[0] + ay[1]) + (ay[2] + ay[3]);
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        auto total = [&](int k) {
+            return (part[0][k][lane] + part[1][k][lane]) + (part[2][k][lane] + part[3][k][lane]);
+        };
+        float nope[4];
+        for (int i = 0; i < nit; ++i) nope[i] = (float)total(i);
+        float rx = 0.0f, ry = 0.0f;
+        if (lane < ROPE_PAIRS) {
+            rx = (float)total(4);
+            ry = (float)total(5);
         }
         const KvView &dst = role == 0 ? p.k : p.v;
         store_kv_row(dst, b, kv_row(dst, entry), nope, nit, rx, ry);
     } else {
         const int dI = p.dI, nit = dI / 64 + (dI % 64 ? 1 : 0);
         const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * dI;
-        const IkView &s = p.ik;
         for (int i = 0; i < nit; ++i) {
             const int d = lane + 64 * i;
-            const bool on = d < dI;
-            const double acc = on ? pooled(alpha, m, [&](int r) {
+            part[wave][i][lane] = d < dI ? pooled(alpha, r0, r1, [&](int r) {
                 return load_act<ACT>(p.raw_ik, rowbase + (int64_t)r * dI + d);
             }) : 0.0;
-            store_ik_value(s, b, entry, d, on, (float)acc);
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        for (int i = 0; i < nit; ++i) {
+            const int d = lane + 64 * i;
+            const double acc = (part[0][i][lane] + part[1][i][lane]) + (part[2][i][lane] + part[3][i][lane]);
+            store_ik_value(p.ik, b, entry, d, d < dI, (float)acc);
         }
     }
 }
@@ -536,8 +567,8 @@ hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
         else launch_small<1>(p, grid, s);
     } else {
         const dim3 g3(grid.x, grid.y, 3);  // K, V, indexer key
-        if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, g3, dim3(64), 0, s, p);
-        else hipLaunchKernelGGL(compress_kernel<1>, g3, dim3(64), 0, s, p);
+        if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, g3, dim3(64 * CW), 0, s, p);
+        else hipLaunchKernelGGL(compress_kernel<1>, g3, dim3(64 * CW), 0, s, p);
     }
     return hipGetLastError();
 }
