@@ -16,10 +16,12 @@
 //     scales ride in the instruction. Each lane loads one 16-byte quarter of
 //     one key row, so a wave reads 1 KB of contiguous key bytes per tile.
 //     The ReLU-weighted head sum is taken in the accumulator lanes.
-//  2. The chunk keeps its local top-s candidates: a two-pass LDS radix
-//     histogram (top 16 bits of the order-preserving score key) finds a
-//     threshold; every entry at or above it is written, in index order, to the
-//     chunk's candidate region with the threshold as the region's lower bound.
+//  2. The chunk keeps its local top-s candidates: an LDS radix histogram of
+//     11-bit digits of the order-preserving score key, taken from the highest
+//     bit in which the chunk's keys differ and refined only while too many
+//     entries reach the chosen bin, finds a threshold; every entry at or above
+//     it is written, in index order, to the chunk's candidate region with the
+//     threshold as the region's lower bound.
 //  3. A merge kernel (one workgroup per query) radix-selects the k-th key over
 //     the candidates held in registers, checks that no chunk could have
 //     withheld an entry at or above it (lower bound > k-th key), and writes the
