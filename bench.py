@@ -800,6 +800,135 @@ def stack_main(a):
     print(json.dumps(rec), flush=True)
 
 
+# ------------------------------------------------------------------ compression ----
+
+CP_B, CP_T = 4, 65536                 # sequences, new raw tokens per sequence
+CP_POS0 = T - CP_T                    # the chunk ending at the 1M-th token
+CP_METRIC = 'compressed raw tokens/s (CSA m=4: K, V and MXFP4 indexer key; 4 x 65,536 tokens at 1M positions)'
+
+
+def compress_bytes(m, variant, ik):
+    """Algorithmic HBM bytes of one csa_compress call over CP_B x CP_T tokens: every raw row
+    read once (the overlapping windows also read the m rows before the chunk), the gate
+    logits, and every entry row written once."""
+    rows = CP_T + (m if variant == 'overlap' else 0)
+    width = 2 * D + (DI if ik else 0)                       # raw BF16 values per token
+    gate_w = width if variant == 'channel_gate' else 1      # float32 gate logits per token
+    n_e = CP_T // m
+    per_seq = rows * (2 * width + 4 * gate_w) + n_e * (2 * ROW_KV + (ROW_IK if ik else 0))
+    return CP_B * per_seq
+
+
+def cpu_baseline_compress(seed):
+    """The oracle's m = 4 compression (K rotated then pooled, V, indexer key; float64 numpy,
+    encoding included) on blocks of the same shapes, repeated for about CPU_SAMPLE_S seconds."""
+    sys.path.insert(0, ROOT)
+    import numpy as np
+    import synth
+    from oracle import compress as OC
+    threads = int(os.environ.get('OMP_NUM_THREADS', 0)) or len(os.sched_getaffinity(0))
+    n_tok = 4096
+    raw = synth.raw_tokens(seed, 1, n_tok, D, M_CSA, DI, bf16=True, prefix='cpu_cp')
+    n, el = 0, 0.0
+    while el < CPU_SAMPLE_S:
+        t0 = time.perf_counter()
+        k, v, u = OC.compress(raw['raw_k'], raw['raw_v'], raw['gate'], raw['pos_bias'], CP_POS0, raw_ik=raw['raw_ik'])
+        OC.encode_kv(k, 'e4m3_bf16'), OC.encode_kv(v, 'e4m3_bf16'), OC.encode_ik(u, 'mxfp4')
+        el += time.perf_counter() - t0
+        n += 1
+    return {'value': round(n * n_tok / el, 1), 'unit': 'tokens/s', 'cores': int(threads), 'cpu_model': cpu_model(),
+            'kind': 'oracle',
+            'sample': f'{n} passes over {n_tok} raw tokens (m = 4: K, V and indexer key, pooled and encoded), '
+                      f'{el:.1f} s; float64 numpy'}
+
+
+def compress_main(a):
+    """Every compressor form over one chunk of CP_T new raw tokens for each of CP_B sequences at
+    positions just below 1M: CSA m = 4 (K, V, indexer key), HCA m = 128 (K, V), window rows
+    (m = 1, into a ring), and the three variants at m = 4. Each call is timed with HIP events
+    over --steps repetitions after --warmup; its roofline line is its algorithmic bytes over
+    that time against the HBM peak."""
+    import torch
+    import long_context_attention_compress_amd as v4
+    import synth
+    dev = 'cuda'
+    Bc, Tc, p0 = CP_B, CP_T, CP_POS0
+    print(f'[bench] compression inputs ({Bc} x {Tc} raw tokens at positions {p0}..{p0 + Tc - 1})', file=sys.stderr,
+          flush=True)
+    ext = 128                                # rows before the chunk (the overlapping windows read m of them)
+    g = lambda name, shape, std=1.0: synth.gpu_normal(a.seed, f'cp/{name}', shape, std)
+    rk = g('k', (Bc, ext + Tc, D)).to(torch.bfloat16)
+    rv = g('v', (Bc, ext + Tc, D)).to(torch.bfloat16)
+    ru = g('u', (Bc, ext + Tc, DI)).to(torch.bfloat16)
+    gate = g('gate', (Bc, ext + Tc))
+    body = lambda x: x[:, ext:].contiguous()
+    with_prev = lambda x, m: x[:, ext - m:].contiguous()
+    k_c, v_c, u_c, g_c = body(rk), body(rv), body(ru), body(gate)
+    k_o, v_o, u_o, g_o = (with_prev(x, M_CSA) for x in (rk, rv, ru, gate))
+    del rk, rv, ru, gate
+    C = 2 * D + DI
+    g_ch = g('gate_ch', (Bc, Tc, C))
+    b4, b128 = g('b4', (M_CSA,), 0.1), g('b128', (M_HCA,), 0.1)
+    b_ov, b_ch = g('b_ov', (2 * M_CSA,), 0.1), g('b_ch', (M_CSA, C), 0.1)
+    n4, n128 = (p0 + Tc) // M_CSA, (p0 + Tc) // M_HCA
+    ek4, ev4, ik4 = v4.KVStore.empty(Bc, n4, D), v4.KVStore.empty(Bc, n4, D), v4.IKStore.empty(Bc, n4, DI)
+    ek128, ev128 = v4.KVStore.empty(Bc, n128, D), v4.KVStore.empty(Bc, n128, D)
+    wk, wv = v4.KVStore.empty(Bc, Tc, D, ring=Tc), v4.KVStore.empty(Bc, Tc, D, ring=Tc)
+    z1 = torch.zeros(1, device=dev)
+    cases = [
+        ('csa_compress m=4 (K, V, indexer key)', 4, 'block', True,
+         v4.csa_compress(g_c, b4, p0, k_c, v_c, ek4, ev4, u_c, ik4, prepare=True)),
+        ('csa_compress m=128 (K, V)', 128, 'block', False,
+         v4.csa_compress(g_c, b128, p0, k_c, v_c, ek128, ev128, prepare=True)),
+        ('csa_compress m=1 (window rows into a ring)', 1, 'block', False,
+         v4.csa_compress(g_c, z1, p0, k_c, v_c, wk, wv, prepare=True)),
+        ('csa_compress m=4 overlapping windows of 2m', 4, 'overlap', True,
+         v4.csa_compress(g_o, b_ov, p0, k_o, v_o, ek4, ev4, u_o, ik4, prepare=True, variant=v4.POOL_OVERLAP)),
+        ('csa_compress m=4 RoPE after pooling', 4, 'rope_after_pool', True,
+         v4.csa_compress(g_c, b4, p0, k_c, v_c, ek4, ev4, u_c, ik4, prepare=True, variant=v4.POOL_ROPE_AFTER)),
+        ('csa_compress m=4 per-channel gates', 4, 'channel_gate', True,
+         v4.csa_compress(g_ch, b_ch, p0, k_c, v_c, ek4, ev4, u_c, ik4, prepare=True,
+                         variant=v4.POOL_CHANNEL_GATE)),
+    ]
+    torch.cuda.synchronize()
+    lines = []
+    for name, m, variant, ik, call in cases:
+        print(f'[bench] {name}', file=sys.stderr, flush=True)
+        for _ in range(a.warmup):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * a.steps)]
+        for i in range(a.steps):
+            ev[2 * i].record()
+            call()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        t_ms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(a.steps)) / a.steps
+        nbytes = compress_bytes(m, variant, ik)
+        gbs = nbytes / (t_ms * 1e-3) / 1e9
+        lines.append({'bound': 'hbm', 'kernel': name, 'achieved': round(gbs, 1), 'peak': HBM_PEAK_GBS, 'unit': 'GB/s',
+                      'frac': round(gbs / HBM_PEAK_GBS, 4), 'us_per_call': round(t_ms * 1e3, 2),
+                      'bytes_per_call': nbytes, 'tokens_per_s': round(Bc * Tc / (t_ms * 1e-3), 1)})
+    head = lines[0]
+    rec = {
+        'metric': CP_METRIC, 'value': head['tokens_per_s'], 'unit': 'tokens/s', 'n_gpus': 1,
+        'steps': a.steps, 'warmup': a.warmup, 'ms_per_step': round(head['us_per_call'] * 1e-3, 6),
+        'higher_is_better': True, 'scaling': 'weak', 'vs_baseline': None, 'dtype': 'bf16->e4m3/bf16+mxfp4',
+        'data': 'synthetic',
+        'config': {'workload': f'compression of {Tc:,} new raw tokens (BF16, K and V of dim 192, indexer key of '
+                               f'dim 128) for each of {Bc} sequences at positions {p0:,}..{p0 + Tc - 1:,}: CSA '
+                               f'blocks of 4, HCA blocks of 128, window rows, and the three compressor variants '
+                               f'at m = 4',
+                   'batch': Bc, 'new_tokens': Tc, 'parallelism': 'single GPU'},
+        'timing': 'HIP events around each call, averaged over the timed repetitions',
+        'roofline': {k: head[k] for k in ('bound', 'kernel', 'achieved', 'peak', 'unit', 'frac')} | {'traffic': None},
+        'roofline_calls': lines,
+    }
+    if not a.no_cpu_baseline:
+        print('[bench] cpu baseline (oracle)', file=sys.stderr, flush=True)
+        rec['cpu_baseline'] = cpu_baseline_compress(a.seed)
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split('\n')[0])
     ap.add_argument('--gpus', type=int, default=1)
@@ -808,7 +937,7 @@ def main():
     ap.add_argument('--layers', type=int, default=16)
     ap.add_argument('--seed', type=int, default=7)
     ap.add_argument('--no-cpu-baseline', action='store_true')
-    ap.add_argument('--workload', choices=('decode', 'prefill', 'stack', 'drafts'), default='decode')
+    ap.add_argument('--workload', choices=('decode', 'prefill', 'stack', 'drafts', 'compress'), default='decode')
     ap.add_argument('--tokens', type=int, default=4, help='tokens per sequence (--workload drafts)')
     ap.add_argument('--stack-layers', type=int, default=STACK_LAYERS)
     a = ap.parse_args()
@@ -823,6 +952,8 @@ def main():
         return stack_main(a)
     if a.workload == 'drafts':
         return drafts_main(a)
+    if a.workload == 'compress':
+        return compress_main(a)
     import torch
     import long_context_attention_compress_amd as v4
     import synth

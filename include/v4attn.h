@@ -168,7 +168,9 @@ typedef struct {
  *  act_fmt     format of raw_k, raw_v, raw_ik (float32 or bfloat16).
  *  rope_base   RoPE base (e.g. 10000).
  *  raw_k/raw_v [B][t_new][dim of k_out/v_out], contiguous; may be NULL
- *              together with k_out/v_out.
+ *              together with k_out/v_out. raw_k, raw_v and raw_ik are read as
+ *              pairs of elements: 8-byte aligned (float32) or 4-byte aligned
+ *              (bfloat16), else V4A_EALIGN.
  *  gate        [B][t_new] float32 gate logits.
  *  pos_bias    [m] float32 positional bias.
  *  raw_ik      [B][t_new][ik_out->dim] or NULL (then ik_out must be NULL).

@@ -401,7 +401,9 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
                 return fail(V4A_EINVAL, "entries %lld..%lld do not fit in %lld rows", (long long)e0,
                             (long long)(e0 + ne - 1), (long long)s->rows);
         }
-        if (!aligned(a->raw_k, esz) || !aligned(a->raw_v, esz)) return fail(V4A_EALIGN, "raw_k/raw_v misaligned");
+        // the compressors read raw rows as pairs of elements
+        if (!aligned(a->raw_k, 2 * esz) || !aligned(a->raw_v, 2 * esz))
+            return fail(V4A_EALIGN, "raw_k/raw_v must be aligned to two elements");
         P.has_kv = 1;
         P.D = a->k_out->dim;
         P.raw_k = a->raw_k;
@@ -411,7 +413,7 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
         if ((r = check_ik(a->ik_out, "ik_out", &P.ik))) return r;
         if (!a->block_end && e0 + ne > a->ik_out->rows) return fail(V4A_EINVAL, "indexer entries do not fit in the store");
         if (a->ik_out->fmt == V4A_IK_F32 && a->ik_out->dim % 4) return fail(V4A_EFORMAT, "bad indexer dim");
-        if (!aligned(a->raw_ik, esz)) return fail(V4A_EALIGN, "raw_ik misaligned");
+        if (!aligned(a->raw_ik, 2 * esz)) return fail(V4A_EALIGN, "raw_ik must be aligned to two elements");
         P.has_ik = 1;
         P.dI = a->ik_out->dim;
         P.raw_ik = a->raw_ik;

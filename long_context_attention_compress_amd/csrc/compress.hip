@@ -259,26 +259,98 @@ __global__ __launch_bounds__(64 * CW) void compress_kernel(CompressPlan p) {
 }
 
 // Blocks of at most SMALL_M tokens (the per-token window append, the CSA
-// block): every global load is issued before any arithmetic, so one memory
-// round trip precedes the encode, and each lane evaluates the gate softmax
-// itself. Same float64 arithmetic as the general kernel (for m = 1 the
-// pooling is skipped: it is the identity).
+// block). Three waves per block, one per output: wave 0 the K entry, wave 1
+// the V entry, wave 2 the indexer key, so the three encodes run side by side.
+// Every global load is issued before any arithmetic, so one memory round trip
+// precedes the encode. Lane l holds element pairs (2p, 2p + 1), p = l + 64 i,
+// of each row: a raw row is read as 32-bit words (two BF16 values) or 64-bit
+// ones (two float32 values), and the encoders take two dims per lane. The
+// float64 arithmetic is the general kernel's, in the same order per element
+// (for m = 1 the pooling is skipped: it is the identity).
 constexpr int SMALL_M = 4;
 
-// Raw bits of one activation (float32 or BF16) and its float32 value.
+// Float32 bit patterns of raw elements e and e + 1 (e even) of a float32 or
+// BF16 array.
 template <int ACT>
-__device__ __forceinline__ uint32_t load_bits(const char *base, int64_t i) {
-    if (ACT == 0) return ((const uint32_t *)base)[i];
-    return ((const uint16_t *)base)[i];
+__device__ __forceinline__ uint2 load_pair(const char *base, int64_t e) {
+    if (ACT == 0) return *(const uint2 *)(base + e * 4);
+    const uint32_t w = *(const uint32_t *)(base + e * 2);
+    return make_uint2(w << 16, w & 0xFFFF0000u);
 }
-template <int ACT>
-__device__ __forceinline__ float bits_val(uint32_t x) {
-    return ACT == 0 ? __uint_as_float(x) : __uint_as_float(x << 16);
+__device__ __forceinline__ double dval(uint32_t bits) { return (double)__uint_as_float(bits); }
+
+// Broadcast of lane r's double.
+__device__ __forceinline__ double lane_bcast(double x, int r) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), r);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// The other half's double (lane l gets lane l ^ 32's value).
+__device__ __forceinline__ double swap_halves(double x) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, x);
+    const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)u, 32, 64);
+    const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(u >> 32), 32, 64);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Three waves per block of tokens, one per output: wave 0 the K entry, wave
-// 1 the V entry, wave 2 the indexer key (each evaluates the gate softmax
-// itself), so the three encodes run side by side.
+// Encode pooled float32 pairs into a KV store row: no-RoPE pairs p = lane +
+// 64 i (valid where 2p < Dn) and, where `rope_on`, RoPE pair `rp`.
+__device__ __forceinline__ void store_kv_pairs(const KvView &s, int b, int64_t row, const float (&x0)[2],
+                                               const float (&x1)[2], int ni, bool rope_on, int rp, float rx, float ry) {
+    const int lane = lane_id();
+    const int Dn = s.dim - ROPE_DIM;
+    if (s.fmt == 0) {
+        float *dst = (float *)(s.f32 + b * s.f32_bs + row * s.f32_rs);
+        for (int i = 0; i < ni; ++i) {
+            const int pr = lane + 64 * i;
+            if (2 * pr < Dn) *(float2 *)&dst[2 * pr] = make_float2(x0[i], x1[i]);
+        }
+        if (rope_on) *(float2 *)&dst[Dn + 2 * rp] = make_float2(rx, ry);
+        return;
+    }
+    // E4M3_BF16: dim 192, so the 128 no-RoPE dims are one group of pairs p = lane
+    uint8_t c0, c1;
+    const float sc = e4m3_group128(x0[0], x1[0], &c0, &c1);
+    ((uint16_t *)(s.nope + b * s.nope_bs + row * s.nope_rs))[lane] = (uint16_t)(c0 | (c1 << 8));
+    if (lane == 0) *(float *)(s.scale + b * s.scale_bs + row * s.scale_rs) = sc;
+    if (rope_on)
+        ((uint32_t *)(s.rope + b * s.rope_bs + row * s.rope_rs))[rp] =
+            (uint32_t)bf16_encode(rx) | ((uint32_t)bf16_encode(ry) << 16);
+}
+
+// Encode pooled float32 pairs (dims 2p, 2p + 1, p = lane + 64 i) into the
+// indexer store; every lane of the wave calls it. An MX block of 32 dims is
+// one 16-lane row.
+__device__ __forceinline__ void store_ik_pairs(const IkView &s, int b, int64_t entry, const float (&x0)[2],
+                                               const float (&x1)[2], int ni, int dI) {
+    const int lane = lane_id();
+    for (int i = 0; i < ni; ++i) {
+        const int pr = lane + 64 * i;
+        const bool on = 2 * pr < dI;
+        if (s.fmt == 0) {
+            if (on) *(float2 *)&((float *)(s.f32 + b * s.f32_bs + entry * s.f32_rs))[2 * pr] = make_float2(x0[i], x1[i]);
+            continue;
+        }
+        const bool bad = on && !(__builtin_isfinite(x0[i]) && __builtin_isfinite(x1[i]));
+        float a = on ? amax_acc(amax_acc(0.0f, x0[i]), x1[i]) : 0.0f;
+        a = __uint_as_float(row_max_u32(__float_as_uint(a)));
+        const uint64_t row_bits = 0xFFFFull << (lane & 48);
+        const bool nbad = (__ballot(bad) & row_bits) != 0;
+        uint32_t code = 0;
+        int E = 0;
+        if (!nbad) {
+            E = mx_exponent(a);
+            code = e2m1_encode(__builtin_ldexpf(x0[i], -E)) | (e2m1_encode(__builtin_ldexpf(x1[i], -E)) << 4);
+        }
+        if (on) {
+            ((uint8_t *)(s.e2m1 + b * s.e2m1_bs + entry * s.e2m1_rs))[pr] = (uint8_t)code;
+            if ((lane & 15) == 0)
+                ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[pr >> 4] = nbad ? 0xFF : (uint8_t)(E + 127);
+        }
+    }
+}
+
 template <int ACT, int M>
 __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
     const int lane = lane_id(), role = threadIdx.x >> 6;
@@ -288,17 +360,23 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
     const int64_t entry = geo.entry;
     const bool do_kv = p.has_kv && (p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring);
     if (!geo.ok || (role < 2 ? !do_kv : !p.has_ik)) return;  // uniform per wave
-    const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
+    const int D = p.D, Dn = D - ROPE_DIM;
     const int dI = p.dI;
     const int width = role < 2 ? D : dI;
-    const bool rl = lane < ROPE_PAIRS;
-    // Every load is unconditional, so all of them are in flight together: an
-    // element past the row reads the row's first; the values are masked after
-    // the loads.
+    const int n_el = role < 2 ? Dn : dI;       // elements encoded as pairs by every lane
+    const int ni = n_el > 128 ? 2 : 1;         // pairs per lane (at most 256 elements)
+    // RoPE pairs: lanes 0..31 take the block's tokens 0 .. H-1, lanes 32..63
+    // tokens H .. M-1, of pair lane & 31 (K's rotation is the costly part)
+    constexpr int H = (M + 1) / 2;
+    const bool up = lane >= 32;
+    const int rp = lane & 31;
+    const int rlo = up ? H : 0, rn = up ? M - H : H;  // this lane's RoPE tokens
     const char *src = (const char *)(role == 0 ? p.raw_k : role == 1 ? p.raw_v : p.raw_ik);
-    double f = p.inv_freq[rl ? lane : 0];
+    const double f = p.inv_freq[rp];
+    // Every load is unconditional, so all of them are in flight together: an
+    // element past the row reads the row's first pair; values are masked after.
     float gz[M], gb[M];
-    uint32_t xn[M][4], xa[M], xb[M];
+    uint2 xn[M][2], xr[H];
 #pragma unroll
     for (int r = 0; r < M; ++r) {
         const int64_t t = (int64_t)b * p.t_new + tok0 + r;
@@ -306,103 +384,131 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
         gb[r] = p.pos_bias[r];
         const int64_t row = t * width;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool on = role < 2 ? i < nit : lane + 64 * i < dI;
-            xn[r][i] = load_bits<ACT>(src, on ? row + lane + 64 * i : row);
+        for (int i = 0; i < 2; ++i) {
+            const int pr = lane + 64 * i;
+            xn[r][i] = load_pair<ACT>(src, (i < ni && 2 * pr < n_el) ? row + 2 * pr : row);
         }
-        const int64_t xr = (role < 2 && rl) ? row + Dn + 2 * lane : row;
-        xa[r] = load_bits<ACT>(src, xr);
-        xb[r] = load_bits<ACT>(src, xr + ((role < 2 && rl) ? 1 : 0));
+    }
+    if (role < 2) {
+#pragma unroll
+        for (int u = 0; u < H; ++u) {
+            const int r = rlo + u < M ? rlo + u : M - 1;
+            xr[u] = load_pair<ACT>(src, ((int64_t)b * p.t_new + tok0 + r) * width + Dn + 2 * rp);
+        }
     }
     // no load is sunk into the branches that use it (the register fence also
     // pins the rotation frequency, a kernel-argument load, up here)
-    asm volatile("" : "+v"(f) :: "memory");
-    double z[M];
-#pragma unroll
-    for (int r = 0; r < M; ++r) z[r] = (double)gz[r] + (double)gb[r];
-    // alpha_r = softmax_r(gate + pos_bias), float64
-    double zmax = z[0];
-#pragma unroll
-    for (int r = 1; r < M; ++r) zmax = z[r] > zmax ? z[r] : zmax;
-    double e[M], zsum = 0.0;
-#pragma unroll
-    for (int r = 0; r < M; ++r) {
-        e[r] = exp(z[r] - zmax);
-        zsum += e[r];
-    }
-    double alpha[M];
-#pragma unroll
-    for (int r = 0; r < M; ++r) alpha[r] = e[r] / zsum;
+    double fx = f;
+    asm volatile("" : "+v"(fx) :: "memory");
 
-    if (role < 2) {
-        // K (rotated at each token's position) or V
-        float nx[4];
-        float rx = 0.f, ry = 0.f;
-        if constexpr (M == 1) {
-            // one token: the pooling is the identity (alpha = 1 for any finite
-            // gate) and the gate is not used. The attention kernels' fused
-            // window append computes this same row with the same operations.
+    // alpha_r = softmax_r(gate + pos_bias) in float64: lane r evaluates token
+    // r's exponential and quotient, the wave reads them back; the sum runs
+    // over r = 0 .. M-1 in order.
+    double alpha[M];
+    if constexpr (M > 1) {
+        double z[M];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) nx[i] = bits_val<ACT>(xn[0][i]);
-            if (rl) {
-                if (role == 0) {
-                    double sn, cs, xr, yr;
-                    rope_sincos((double)geo.first * f, &sn, &cs);
-                    rope_rotate((double)bits_val<ACT>(xa[0]), (double)bits_val<ACT>(xb[0]), sn, cs, &xr, &yr);
-                    rx = (float)xr;
-                    ry = (float)yr;
-                } else {
-                    rx = bits_val<ACT>(xa[0]);
-                    ry = bits_val<ACT>(xb[0]);
-                }
-            }
-        } else {
+        for (int r = 0; r < M; ++r) z[r] = (double)gz[r] + (double)gb[r];
+        double zmax = z[0];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                double a = 0.0;
+        for (int r = 1; r < M; ++r) zmax = z[r] > zmax ? z[r] : zmax;
+        double zl = z[0];
 #pragma unroll
-                for (int r = 0; r < M; ++r) a += alpha[r] * (double)bits_val<ACT>(xn[r][i]);
-                nx[i] = (float)a;
-            }
-            if (rl) {
-                double ax = 0.0, ay = 0.0;
+        for (int r = 1; r < M; ++r) zl = lane == r ? z[r] : zl;
+        const double el = exp(zl - zmax);
+        double e[M], zsum = 0.0;
 #pragma unroll
-                for (int r = 0; r < M; ++r) {
-                    double x = (double)bits_val<ACT>(xa[r]), y = (double)bits_val<ACT>(xb[r]);
-                    if (role == 0) {
-                        double sn, cs, xr, yr;
-                        rope_sincos((double)(geo.first + r) * f, &sn, &cs);
-                        rope_rotate(x, y, sn, cs, &xr, &yr);
-                        x = xr;
-                        y = yr;
-                    }
-                    ax += alpha[r] * x;
-                    ay += alpha[r] * y;
-                }
-                rx = (float)ax;
-                ry = (float)ay;
-            }
+        for (int r = 0; r < M; ++r) {
+            e[r] = lane_bcast(el, r);
+            zsum += e[r];
         }
-        const KvView &dst = role == 0 ? p.k : p.v;
-        store_kv_row(dst, b, kv_row(dst, entry), nx, nit, rx, ry);
+        double eo = e[0];
+#pragma unroll
+        for (int r = 1; r < M; ++r) eo = lane == r ? e[r] : eo;
+        const double al = eo / zsum;
+#pragma unroll
+        for (int r = 0; r < M; ++r) alpha[r] = lane_bcast(al, r);
     } else {
-        const int nit_i = (dI + 63) / 64;
+        alpha[0] = 1.0;
+    }
+
+    float x0[2] = {0.f, 0.f}, x1[2] = {0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i >= nit_i) break;
-            const int d = lane + 64 * i;
-            float x;
-            if constexpr (M == 1) {
-                x = bits_val<ACT>(d < dI ? xn[0][i] : 0u);
-            } else {
-                double acc = 0.0;
+    for (int i = 0; i < 2; ++i) {
+        if (i >= ni) break;
+        if constexpr (M == 1) {
+            x0[i] = __uint_as_float(xn[0][i].x);
+            x1[i] = __uint_as_float(xn[0][i].y);
+        } else {
+            double a0 = 0.0, a1 = 0.0;
 #pragma unroll
-                for (int r = 0; r < M; ++r) acc += alpha[r] * (double)bits_val<ACT>(d < dI ? xn[r][i] : 0u);
-                x = (float)acc;
+            for (int r = 0; r < M; ++r) {
+                a0 += alpha[r] * dval(xn[r][i].x);
+                a1 += alpha[r] * dval(xn[r][i].y);
             }
-            store_ik_value(p.ik, b, entry, d, d < dI, x);
+            x0[i] = (float)a0;
+            x1[i] = (float)a1;
         }
     }
+    if (role == 2) {
+        store_ik_pairs(p.ik, b, entry, x0, x1, ni, dI);
+        return;
+    }
+    // RoPE pair: K rotated at each token's position, V as it is; the lower
+    // half's partial sums go to the upper half, which adds its tokens after
+    // them (the order of a sequential sum over the block)
+    float rx = 0.f, ry = 0.f;
+    bool rope_on;
+    if constexpr (M == 1) {
+        if (role == 0) {
+            double sn, cs, xa, ya;
+            rope_sincos((double)geo.first * fx, &sn, &cs);
+            rope_rotate(dval(xr[0].x), dval(xr[0].y), sn, cs, &xa, &ya);
+            rx = (float)xa;
+            ry = (float)ya;
+        } else {
+            rx = __uint_as_float(xr[0].x);
+            ry = __uint_as_float(xr[0].y);
+        }
+        rope_on = !up;
+    } else {
+        double ax = 0.0, ay = 0.0;
+        double px[H], py[H];
+#pragma unroll
+        for (int u = 0; u < H; ++u) {
+            double x = dval(xr[u].x), y = dval(xr[u].y);
+            if (role == 0 && u < rn) {
+                double sn, cs, xa, ya;
+                rope_sincos((double)(geo.first + rlo + u) * fx, &sn, &cs);
+                rope_rotate(x, y, sn, cs, &xa, &ya);
+                x = xa;
+                y = ya;
+            }
+            px[u] = x;
+            py[u] = y;
+        }
+        // lower half: tokens 0 .. H-1 from zero
+#pragma unroll
+        for (int u = 0; u < H; ++u) {
+            ax += alpha[u] * px[u];
+            ay += alpha[u] * py[u];
+        }
+        const double sx = swap_halves(ax), sy = swap_halves(ay);
+        if (up) {
+            ax = sx;
+            ay = sy;
+#pragma unroll
+            for (int u = 0; u < M - H; ++u) {
+                ax += alpha[H + u] * px[u];
+                ay += alpha[H + u] * py[u];
+            }
+        }
+        rx = (float)ax;
+        ry = (float)ay;
+        rope_on = up;
+    }
+    const KvView &dst = role == 0 ? p.k : p.v;
+    store_kv_pairs(dst, b, kv_row(dst, entry), x0, x1, ni, rope_on, rp, rx, ry);
 }
 
 // ------------------------------------------------------------ variants ----

@@ -83,6 +83,7 @@ def test_compress_rejections():
         (dict(m=0), _abi.V4A_EINVAL), (dict(m=2000), _abi.V4A_EINVAL), (dict(pos0=2), _abi.V4A_EINVAL),
         (dict(t_new=6), _abi.V4A_EINVAL), (dict(gate=None), _abi.V4A_ENULL), (dict(act_fmt=7), _abi.V4A_EFORMAT),
         (dict(raw_ik=None), _abi.V4A_ENULL), (dict(pos0=4096 * 4), _abi.V4A_EINVAL), (dict(raw_k=FAKE + 1), _abi.V4A_EALIGN),
+        (dict(raw_v=FAKE + 2), _abi.V4A_EALIGN), (dict(raw_ik=FAKE + 2), _abi.V4A_EALIGN),
         (dict(k_out=None, v_out=None, ik_out=None, raw_ik=None), _abi.V4A_EINVAL), (dict(B=70000), _abi.V4A_EINVAL),
     ]
     for kw, want in cases:
