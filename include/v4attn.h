@@ -160,8 +160,9 @@ typedef struct {
  * how the window is filled.
  *
  *  B, t_new    batch size (1 .. 65535) and raw tokens per batch element
- *              (t_new % m == 0). t_new = 0 returns V4A_OK once B, m, pos0 and
- *              act_fmt are valid; then no pointer is read and nothing is
+ *              (t_new % m == 0, and at most V4A_MAX_COMPRESS_BLOCKS blocks:
+ *              t_new / m <= 2^21). t_new = 0 returns V4A_OK once B, m, pos0
+ *              and act_fmt are valid; then no pointer is read and nothing is
  *              enqueued.
  *  pos0        position of the first raw token (pos0 % m == 0, >= 0).
  *  m           1 .. 1024.
@@ -217,6 +218,9 @@ typedef struct {
  *              Every variant keeps the store formats and the visibility rule,
  *              so the attention calls read their entries unchanged.
  * ---------------------------------------------------------------------- */
+/* Blocks of m tokens one csa_compress call may compress per batch element. */
+#define V4A_MAX_COMPRESS_BLOCKS (1 << 21)
+
 typedef struct {
     int32_t B;
     int32_t t_new;

@@ -361,6 +361,10 @@ int csa_compress(const v4a_compress_args *a, v4a_stream stream) {
     if (a->m < 1 || a->m > 1024) return fail(V4A_EINVAL, "m must be in 1..1024 (got %d)", a->m);
     if (a->pos0 < 0 || a->pos0 % a->m || a->t_new % a->m)
         return fail(V4A_EINVAL, "pos0 and t_new must be non-negative multiples of m");
+    // a launch's grid holds 512 threads for each output of each block
+    if (a->t_new / a->m > V4A_MAX_COMPRESS_BLOCKS)
+        return fail(V4A_EINVAL, "at most %d blocks of m tokens per call (got %lld)", V4A_MAX_COMPRESS_BLOCKS,
+                    (long long)(a->t_new / a->m));
     if (a->variant < V4A_POOL_BLOCK || a->variant > V4A_POOL_CHANNEL_GATE)
         return fail(V4A_EFORMAT, "unknown compressor variant %d", a->variant);
     const int span = a->variant == V4A_POOL_OVERLAP ? 2 * a->m : a->m;  // tokens one entry pools

@@ -9,7 +9,8 @@
 //
 // Four waves per (entry, batch element, output) for long blocks (a quarter
 // of the tokens each), three waves (one per output) in one workgroup for
-// blocks of up to four tokens. The gate weights, the RoPE rotation and the
+// blocks of up to four tokens, and one wave per output for each two tokens of
+// a chunk of window rows (m = 1). The gate weights, the RoPE rotation and the
 // weighted sum are evaluated in float64 and the entry is rounded to float32
 // before it is encoded, so every encoding decision (FP8 scale and codes, BF16
 // rounding, MX exponent and E2M1 codes) is taken on a float32 value.
@@ -117,158 +118,6 @@ __device__ __forceinline__ void store_ik_value(const IkView &s, int b, int64_t e
         ((uint8_t *)(s.e8m0 + b * s.e8m0_bs + entry * s.e8m0_rs))[d >> 5] = nbad ? 0xFF : (uint8_t)(E + 127);
 }
 
-// sum_r alpha[r] * x(r) over r0 <= r < r1 in float64, as four interleaved
-// partial sums (independent FMA chains) added pairwise at the end.
-template <class F>
-__device__ __forceinline__ double pooled(const double *alpha, int r0, int r1, F x) {
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int r = r0;
-    for (; r + 4 <= r1; r += 4) {
-        a0 += alpha[r] * x(r);
-        a1 += alpha[r + 1] * x(r + 1);
-        a2 += alpha[r + 2] * x(r + 2);
-        a3 += alpha[r + 3] * x(r + 3);
-    }
-    for (; r < r1; ++r) a0 += alpha[r] * x(r);
-    return (a0 + a1) + (a2 + a3);
-}
-
-// Waves per (block, batch element, output) of the general kernel: wave w
-// pools the w-th quarter of the block's tokens, and wave 0 adds the four
-// float64 partial sums in a fixed order ((w0 + w1) + (w2 + w3)) before the
-// entry is rounded to float32 and encoded. (With one wave per output the
-// m = 128 blocks of a chunked prefill ran as 128 waves on the whole device,
-// each through 128 tokens and their float64 sin/cos: 120 us per call.)
-constexpr int CW = 4;
-
-// One workgroup per (block, batch element, output): blockIdx.z = 0 the K
-// entry, 1 the V entry, 2 the indexer key.
-template <int ACT>
-__global__ __launch_bounds__(64 * CW) void compress_kernel(CompressPlan p) {
-    __shared__ double alpha[MAX_M];
-    __shared__ double part[CW][6][64];  // per wave: up to four pooled dims per lane, then the RoPE pair
-    const int lane = lane_id();
-    const int wave = (int)(threadIdx.x >> 6);
-    const int j = blockIdx.x;  // block within the chunk
-    const int b = blockIdx.y;
-    const int role = blockIdx.z;
-    const int m = p.m;
-    const BlockGeo geo = block_geo(p, j, b, m);
-    const int64_t tok0 = geo.tok0;                       // first raw row of the block
-    const int64_t entry = geo.entry;
-    // A ring store keeps only the last `ring` entries written by one call.
-    const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
-    if (!geo.ok || (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik)) return;  // uniform per workgroup
-
-    // alpha_r = softmax_r(gate + pos_bias), float64, by wave 0
-    if (wave == 0) {
-        double zmax = -__builtin_inf();
-        for (int r = lane; r < m; r += 64) {
-            double z = (double)p.gate[(int64_t)b * p.t_new + tok0 + r] + (double)p.pos_bias[r];
-            alpha[r] = z;
-            zmax = z > zmax ? z : zmax;
-        }
-        zmax = wave_max(zmax);
-        double zsum = 0.0;
-        for (int r = lane; r < m; r += 64) {
-            double e = exp(alpha[r] - zmax);
-            alpha[r] = e;
-            zsum += e;
-        }
-        zsum = wave_sum(zsum);
-        for (int r = lane; r < m; r += 64) alpha[r] = alpha[r] / zsum;
-    }
-    __syncthreads();
-    // this wave's tokens
-    const int chunk = (m + CW - 1) / CW;
-    const int r0 = wave * chunk < m ? wave * chunk : m;
-    const int r1 = r0 + chunk < m ? r0 + chunk : m;
-
-    if (role < 2) {
-        // values (never rotated) and keys (rotated at each token's position)
-        const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
-        const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * D;
-        const void *src = role == 0 ? p.raw_k : p.raw_v;
-        for (int i = 0; i < nit; ++i)
-            part[wave][i][lane] = pooled(alpha, r0, r1, [&](int r) {
-                return load_act<ACT>(src, rowbase + (int64_t)r * D + lane + 64 * i);
-            });
-        if (lane < ROPE_PAIRS) {
-            const double f = p.inv_freq[lane];
-            auto pair = [&](int r, double *x, double *y) {
-                *x = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane);
-                *y = load_act<ACT>(src, rowbase + (int64_t)r * D + Dn + 2 * lane + 1);
-                if (role == 0) {
-                    double sn, cs, xr, yr;
-                    rope_sincos((double)(geo.first + r) * f, &sn, &cs);
-                    rope_rotate(*x, *y, sn, cs, &xr, &yr);
-                    *x = xr;
-                    *y = yr;
-                }
-            };
-            double ax[4] = {0.0, 0.0, 0.0, 0.0}, ay[4] = {0.0, 0.0, 0.0, 0.0};
-            int r = r0;
-            for (; r + 4 <= r1; r += 4)
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    double x, y;
-                    pair(r + u, &x, &y);
-                    ax[u] += alpha[r + u] * x;
-                    ay[u] += alpha[r + u] * y;
-                }
-            for (; r < r1; ++r) {
-                double x, y;
-                pair(r, &x, &y);
-                ax[0] += alpha[r] * x;
-                ay[0] += alpha[r] * y;
-            }
-            part[wave][4][lane] = (ax[0] + ax[1]) + (ax[2] + ax[3]);
-            part[wave][5][lane] = (ay[0] + ay[1]) + (ay[2] + ay[3]);
-        }
-        __syncthreads();
-        if (wave != 0) return;
-        auto total = [&](int k) {
-            return (part[0][k][lane] + part[1][k][lane]) + (part[2][k][lane] + part[3][k][lane]);
-        };
-        float nope[4];
-        for (int i = 0; i < nit; ++i) nope[i] = (float)total(i);
-        float rx = 0.0f, ry = 0.0f;
-        if (lane < ROPE_PAIRS) {
-            rx = (float)total(4);
-            ry = (float)total(5);
-        }
-        const KvView &dst = role == 0 ? p.k : p.v;
-        store_kv_row(dst, b, kv_row(dst, entry), nope, nit, rx, ry);
-    } else {
-        const int dI = p.dI, nit = dI / 64 + (dI % 64 ? 1 : 0);
-        const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * dI;
-        for (int i = 0; i < nit; ++i) {
-            const int d = lane + 64 * i;
-            part[wave][i][lane] = d < dI ? pooled(alpha, r0, r1, [&](int r) {
-                return load_act<ACT>(p.raw_ik, rowbase + (int64_t)r * dI + d);
-            }) : 0.0;
-        }
-        __syncthreads();
-        if (wave != 0) return;
-        for (int i = 0; i < nit; ++i) {
-            const int d = lane + 64 * i;
-            const double acc = (part[0][i][lane] + part[1][i][lane]) + (part[2][i][lane] + part[3][i][lane]);
-            store_ik_value(p.ik, b, entry, d, d < dI, (float)acc);
-        }
-    }
-}
-
-// Blocks of at most SMALL_M tokens (the per-token window append, the CSA
-// block). Three waves per block, one per output: wave 0 the K entry, wave 1
-// the V entry, wave 2 the indexer key, so the three encodes run side by side.
-// Every global load is issued before any arithmetic, so one memory round trip
-// precedes the encode. Lane l holds element pairs (2p, 2p + 1), p = l + 64 i,
-// of each row: a raw row is read as 32-bit words (two BF16 values) or 64-bit
-// ones (two float32 values), and the encoders take two dims per lane. The
-// float64 arithmetic is the general kernel's, in the same order per element
-// (for m = 1 the pooling is skipped: it is the identity).
-constexpr int SMALL_M = 4;
-
 // Float32 bit patterns of raw elements e and e + 1 (e even) of a float32 or
 // BF16 array.
 template <int ACT>
@@ -350,6 +199,194 @@ __device__ __forceinline__ void store_ik_pairs(const IkView &s, int b, int64_t e
         }
     }
 }
+
+// Waves per (block, batch element, output) of the general kernel: wave w
+// pools the w-th eighth of the block's tokens, and wave 0 adds the eight
+// float64 partial sums in a fixed order (((w0 + w1) + (w2 + w3)) + ((w4 +
+// w5) + (w6 + w7))) before the entry is rounded to float32 and encoded.
+// Within a wave each value is a sum of four interleaved partial sums
+// (independent FMA chains) over its tokens, added pairwise; its RoPE pair is
+// pooled by both halves of the wave, each over half of the tokens (so K's
+// float64 sin/cos run on every lane), the lower half's sum plus the upper's.
+// Raw rows are read as pairs of elements, TB tokens' worth of loads at a time.
+constexpr int CW = 8, TB = 8;
+
+// Four interleaved partial sums: token s (counted from the first token of
+// the run) goes to partial s % 4 while whole groups of four remain, to
+// partial 0 after; the total is (a0 + a1) + (a2 + a3).
+__device__ __forceinline__ double sum4(const double (&a)[4]) { return (a[0] + a[1]) + (a[2] + a[3]); }
+
+// One workgroup per (block, batch element, output); the outputs of a block
+// are adjacent in blockIdx.x (x = 3 j + output: 0 the K entry, 1 the V entry,
+// 2 the indexer key), so the costlier K workgroups spread over the device.
+template <int ACT>
+__global__ __launch_bounds__(64 * CW, 4) void compress_kernel(CompressPlan p) {
+    __shared__ double alpha[MAX_M];
+    __shared__ double part[CW][6][64];  // per wave: two pairs of pooled values per lane, then the RoPE pair
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x >> 6);
+    const int j = (int)(blockIdx.x / 3), role = (int)(blockIdx.x % 3);
+    const int b = blockIdx.y;
+    const int m = p.m;
+    const int64_t nblk = p.block_end ? 1 : p.t_new / m;
+    const BlockGeo geo = block_geo(p, j, b, m);
+    const int64_t tok0 = geo.tok0;                       // first raw row of the block
+    const int64_t entry = geo.entry;
+    // A ring store keeps only the last `ring` entries written by one call.
+    const bool kv_keep = p.k.ring == 0 || (int64_t)j >= nblk - p.k.ring;
+    if (!geo.ok || (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik)) return;  // uniform per workgroup
+
+    // alpha_r = softmax_r(gate + pos_bias), float64, by wave 0
+    if (wave == 0) {
+        double zmax = -__builtin_inf();
+        for (int r = lane; r < m; r += 64) {
+            double z = (double)p.gate[(int64_t)b * p.t_new + tok0 + r] + (double)p.pos_bias[r];
+            alpha[r] = z;
+            zmax = z > zmax ? z : zmax;
+        }
+        zmax = wave_max(zmax);
+        double zsum = 0.0;
+        for (int r = lane; r < m; r += 64) {
+            double e = exp(alpha[r] - zmax);
+            alpha[r] = e;
+            zsum += e;
+        }
+        zsum = wave_sum(zsum);
+        for (int r = lane; r < m; r += 64) alpha[r] = alpha[r] / zsum;
+    }
+    __syncthreads();
+    // this wave's tokens
+    const int chunk = (m + CW - 1) / CW;
+    const int r0 = wave * chunk < m ? wave * chunk : m;
+    const int r1 = r0 + chunk < m ? r0 + chunk : m;
+    const int n = r1 - r0, nfull = n & ~3;
+    const int D = p.D, Dn = D - ROPE_DIM, dI = p.dI;
+    const int width = role < 2 ? D : dI;
+    const int n_el = role < 2 ? Dn : dI;  // elements pooled as pairs by every lane
+    const int ni = n_el > 128 ? 2 : 1;
+    const char *src = (const char *)(role == 0 ? p.raw_k : role == 1 ? p.raw_v : p.raw_ik);
+    const int64_t rowbase = ((int64_t)b * p.t_new + tok0) * width;
+
+    double a[2][2][4] = {};  // [pair i][element][partial]
+    for (int rb = 0; rb < n; rb += TB) {
+        uint2 x[TB][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (i >= ni) break;  // uniform
+            const int pr = lane + 64 * i;
+            const int64_t off = 2 * pr < n_el ? 2 * pr : 0;
+#pragma unroll
+            for (int s = 0; s < TB; ++s) {
+                const int r = rb + s < n ? r0 + rb + s : r0;
+                x[s][i] = load_pair<ACT>(src, rowbase + (int64_t)r * width + off);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < TB; ++s) {
+            if (rb + s >= n) break;  // uniform
+            const double w = alpha[r0 + rb + s];
+            const bool grouped = rb + s < nfull;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if (i >= ni) break;
+                if (grouped) {
+                    a[i][0][s & 3] += w * dval(x[s][i].x);
+                    a[i][1][s & 3] += w * dval(x[s][i].y);
+                } else {
+                    a[i][0][0] += w * dval(x[s][i].x);
+                    a[i][1][0] += w * dval(x[s][i].y);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        part[wave][2 * i][lane] = sum4(a[i][0]);
+        part[wave][2 * i + 1][lane] = sum4(a[i][1]);
+    }
+    if (role < 2) {
+        // RoPE pair rp: the lower half pools tokens r0 .. r0 + nl - 1, the upper
+        // half the rest; K is rotated at each token's position
+        const bool up = lane >= 32;
+        const int rp = lane & 31;
+        const double f = p.inv_freq[rp];
+        const int nl = (n + 1) / 2;
+        const int ra = up ? r0 + nl : r0, nh = up ? n - nl : nl, nhf = nh & ~3;
+        double ax[4] = {0.0, 0.0, 0.0, 0.0}, ay[4] = {0.0, 0.0, 0.0, 0.0};
+        for (int rb = 0; rb < nl; rb += TB) {
+            uint2 x[TB];
+#pragma unroll
+            for (int s = 0; s < TB; ++s) {
+                const int r = rb + s < nh ? ra + rb + s : r0;
+                x[s] = load_pair<ACT>(src, rowbase + (int64_t)r * width + Dn + 2 * rp);
+            }
+#pragma unroll
+            for (int s = 0; s < TB; ++s) {
+                if (rb + s >= nl) break;  // uniform; the upper half's extra slot is skipped below
+                if (rb + s >= nh) continue;
+                const int r = ra + rb + s;
+                double xx = dval(x[s].x), yy = dval(x[s].y);
+                if (role == 0) {
+                    double sn, cs, xr, yr;
+                    rope_sincos((double)(geo.first + r) * f, &sn, &cs);
+                    rope_rotate(xx, yy, sn, cs, &xr, &yr);
+                    xx = xr;
+                    yy = yr;
+                }
+                const double w = alpha[r];
+                if (rb + s < nhf) {
+                    ax[s & 3] += w * xx;
+                    ay[s & 3] += w * yy;
+                } else {
+                    ax[0] += w * xx;
+                    ay[0] += w * yy;
+                }
+            }
+        }
+        const double hx = sum4(ax), hy = sum4(ay);
+        const double ox = swap_halves(hx), oy = swap_halves(hy);
+        if (!up) {
+            part[wave][4][lane] = hx + ox;
+            part[wave][5][lane] = hy + oy;
+        }
+    }
+    __syncthreads();
+    if (wave != 0) return;
+    auto total = [&](int k) {
+        return ((part[0][k][lane] + part[1][k][lane]) + (part[2][k][lane] + part[3][k][lane])) +
+               ((part[4][k][lane] + part[5][k][lane]) + (part[6][k][lane] + part[7][k][lane]));
+    };
+    float x0[2], x1[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        x0[i] = (float)total(2 * i);
+        x1[i] = (float)total(2 * i + 1);
+    }
+    if (role == 2) {
+        store_ik_pairs(p.ik, b, entry, x0, x1, ni, dI);
+        return;
+    }
+    float rx = 0.0f, ry = 0.0f;
+    if (lane < ROPE_PAIRS) {
+        rx = (float)total(4);
+        ry = (float)total(5);
+    }
+    const KvView &dst = role == 0 ? p.k : p.v;
+    store_kv_pairs(dst, b, kv_row(dst, entry), x0, x1, ni, lane < ROPE_PAIRS, lane, rx, ry);
+}
+
+
+// Blocks of at most SMALL_M tokens (the per-token window append, the CSA
+// block). Three waves per block, one per output: wave 0 the K entry, wave 1
+// the V entry, wave 2 the indexer key, so the three encodes run side by side.
+// Every global load is issued before any arithmetic, so one memory round trip
+// precedes the encode. Lane l holds element pairs (2p, 2p + 1), p = l + 64 i,
+// of each row: a raw row is read as 32-bit words (two BF16 values) or 64-bit
+// ones (two float32 values), and the encoders take two dims per lane. The
+// float64 arithmetic is the general kernel's (gate softmax, RoPE, weighted
+// sums, one rounding to float32), the sums running over the block's tokens
+// in order (for m = 1 the pooling is skipped: it is the identity).
+constexpr int SMALL_M = 4;
 
 template <int ACT, int M>
 __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
@@ -511,6 +548,89 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
     store_kv_pairs(dst, b, kv_row(dst, entry), x0, x1, ni, rope_on, rp, rx, ry);
 }
 
+// Window rows (m = 1, a chunk of raw tokens): the pooling is the identity, so
+// a wave encodes two consecutive tokens: both tokens' no-RoPE pairs on every
+// lane, token 2g's RoPE pair on lanes 0..31 and token 2g + 1's on lanes 32..63
+// (each half rotates its own token). One wave per output (K, V, indexer key),
+// two waves when no indexer key is written. Bitwise the rows that
+// compress_small_kernel<ACT, 1> writes.
+template <int ACT>
+__global__ __launch_bounds__(192) void compress_rows_kernel(CompressPlan p) {
+    const int lane = lane_id(), role = threadIdx.x >> 6;
+    const int b = blockIdx.y;
+    const int64_t t0 = 2 * (int64_t)blockIdx.x;              // first token of the pair
+    const int nt = t0 + 1 < p.t_new ? 2 : 1;                  // tokens of this pair (uniform)
+    const int orole = p.has_kv ? role : 2;                    // output of this wave
+    if (orole < 2 ? !p.has_kv : (!p.has_ik || role > (p.has_kv ? 2 : 0))) return;  // uniform per wave
+    const int D = p.D, Dn = D - ROPE_DIM;
+    const int dI = p.dI;
+    const int width = orole < 2 ? D : dI;
+    const int n_el = orole < 2 ? Dn : dI;
+    const int ni = n_el > 128 ? 2 : 1;
+    const bool up = lane >= 32;
+    const int rp = lane & 31;
+    const char *src = (const char *)(orole == 0 ? p.raw_k : orole == 1 ? p.raw_v : p.raw_ik);
+    const double f = p.inv_freq[rp];
+    uint2 xn[2][2], xr;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int64_t row = ((int64_t)b * p.t_new + t0 + (g < nt ? g : 0)) * width;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int pr = lane + 64 * i;
+            xn[g][i] = load_pair<ACT>(src, (i < ni && 2 * pr < n_el) ? row + 2 * pr : row);
+        }
+    }
+    if (orole < 2) {
+        const int g = up && nt > 1 ? 1 : 0;
+        xr = load_pair<ACT>(src, ((int64_t)b * p.t_new + t0 + g) * width + Dn + 2 * rp);
+    }
+    double fx = f;
+    asm volatile("" : "+v"(fx) :: "memory");
+    if (orole == 2) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if (g >= nt) break;
+            float x0[2], x1[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                x0[i] = __uint_as_float(xn[g][i].x);
+                x1[i] = __uint_as_float(xn[g][i].y);
+            }
+            store_ik_pairs(p.ik, b, p.pos0 + t0 + g, x0, x1, ni, dI);
+        }
+        return;
+    }
+    // this half's token: K rotated at its position, V as it is
+    const int64_t pos = p.pos0 + t0 + (up ? 1 : 0);
+    float rx, ry;
+    if (orole == 0) {
+        double sn, cs, xa, ya;
+        rope_sincos((double)pos * fx, &sn, &cs);
+        rope_rotate(dval(xr.x), dval(xr.y), sn, cs, &xa, &ya);
+        rx = (float)xa;
+        ry = (float)ya;
+    } else {
+        rx = __uint_as_float(xr.x);
+        ry = __uint_as_float(xr.y);
+    }
+    const KvView &dst = orole == 0 ? p.k : p.v;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        if (g >= nt) break;
+        // a ring store keeps only the chunk's last `ring` rows
+        const int64_t tok = t0 + g;
+        if (p.k.ring > 0 && tok < (int64_t)p.t_new - p.k.ring) continue;  // uniform
+        float x0[2], x1[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            x0[i] = __uint_as_float(xn[g][i].x);
+            x1[i] = __uint_as_float(xn[g][i].y);
+        }
+        store_kv_pairs(dst, b, kv_row(dst, p.pos0 + tok), x0, x1, ni, g == 0 ? !up : up, rp, rx, ry);
+    }
+}
+
 // ------------------------------------------------------------ variants ----
 // The compressor variants of v4a_pool_variant: overlapping windows of 2m,
 // RoPE applied after pooling, one gate per token and channel. One wave per
@@ -653,11 +773,18 @@ static void launch_variant(const CompressPlan &p, dim3 g3, hipStream_t s) {
 
 template <int ACT>
 static void launch_small(const CompressPlan &p, dim3 grid, hipStream_t s) {
+    if (p.m == 1 && !p.block_end) {  // a chunk of window rows: two tokens per wave
+        const dim3 g2((unsigned)((p.t_new + 1) / 2), grid.y);
+        const unsigned nt = (p.has_kv ? 128u : 0u) + (p.has_ik ? 64u : 0u);
+        hipLaunchKernelGGL((compress_rows_kernel<ACT>), g2, dim3(nt), 0, s, p);
+        return;
+    }
+    const dim3 blk(p.has_ik ? 192 : 128);  // the indexer-key wave only when there is one
     switch (p.m) {
-        case 1: hipLaunchKernelGGL((compress_small_kernel<ACT, 1>), grid, dim3(192), 0, s, p); break;
-        case 2: hipLaunchKernelGGL((compress_small_kernel<ACT, 2>), grid, dim3(192), 0, s, p); break;
-        case 3: hipLaunchKernelGGL((compress_small_kernel<ACT, 3>), grid, dim3(192), 0, s, p); break;
-        default: hipLaunchKernelGGL((compress_small_kernel<ACT, 4>), grid, dim3(192), 0, s, p); break;
+        case 1: hipLaunchKernelGGL((compress_small_kernel<ACT, 1>), grid, blk, 0, s, p); break;
+        case 2: hipLaunchKernelGGL((compress_small_kernel<ACT, 2>), grid, blk, 0, s, p); break;
+        case 3: hipLaunchKernelGGL((compress_small_kernel<ACT, 3>), grid, blk, 0, s, p); break;
+        default: hipLaunchKernelGGL((compress_small_kernel<ACT, 4>), grid, blk, 0, s, p); break;
     }
 }
 
@@ -672,9 +799,9 @@ hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
         if (p.act == 0) launch_small<0>(p, grid, s);
         else launch_small<1>(p, grid, s);
     } else {
-        const dim3 g3(grid.x, grid.y, 3);  // K, V, indexer key
-        if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, g3, dim3(64 * CW), 0, s, p);
-        else hipLaunchKernelGGL(compress_kernel<1>, g3, dim3(64 * CW), 0, s, p);
+        const dim3 gx(grid.x * 3, grid.y);  // K, V, indexer key of each block side by side
+        if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, gx, dim3(64 * CW), 0, s, p);
+        else hipLaunchKernelGGL(compress_kernel<1>, gx, dim3(64 * CW), 0, s, p);
     }
     return hipGetLastError();
 }
