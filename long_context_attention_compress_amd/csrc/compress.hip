@@ -216,16 +216,19 @@ constexpr int CW = 8, TB = 8;
 // partial 0 after; the total is (a0 + a1) + (a2 + a3).
 __device__ __forceinline__ double sum4(const double (&a)[4]) { return (a[0] + a[1]) + (a[2] + a[3]); }
 
-// One workgroup per (block, batch element, output); the outputs of a block
-// are adjacent in blockIdx.x (x = 3 j + output: 0 the K entry, 1 the V entry,
-// 2 the indexer key), so the costlier K workgroups spread over the device.
+// One workgroup per (block, batch element, output written); the outputs of a
+// block are adjacent in blockIdx.x (x = n_out j + output: the K entry, the V
+// entry, the indexer key, as far as they are written), so the costlier K
+// workgroups spread over the device.
 template <int ACT>
 __global__ __launch_bounds__(64 * CW, 4) void compress_kernel(CompressPlan p) {
     __shared__ double alpha[MAX_M];
     __shared__ double part[CW][6][64];  // per wave: two pairs of pooled values per lane, then the RoPE pair
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x >> 6);
-    const int j = (int)(blockIdx.x / 3), role = (int)(blockIdx.x % 3);
+    const int n_out = (p.has_kv ? 2 : 0) + (p.has_ik ? 1 : 0);
+    const int j = (int)(blockIdx.x / n_out);
+    const int role = p.has_kv ? (int)(blockIdx.x % n_out) : 2;  // 0 K, 1 V, 2 indexer key
     const int b = blockIdx.y;
     const int m = p.m;
     const int64_t nblk = p.block_end ? 1 : p.t_new / m;
@@ -634,36 +637,25 @@ __global__ __launch_bounds__(192) void compress_rows_kernel(CompressPlan p) {
 // ------------------------------------------------------------ variants ----
 // The compressor variants of v4a_pool_variant: overlapping windows of 2m,
 // RoPE applied after pooling, one gate per token and channel. One wave per
-// (block, batch element, output), as compress_kernel, with the same float64
-// arithmetic and float32 rounding before encoding.
+// (block, batch element, output written), with the general kernel's float64
+// arithmetic and one rounding to float32 before encoding. Lane l takes the
+// element pairs (2p, 2p + 1), p = l + 64 i, of each row; a RoPE pair is pooled
+// by both halves of the wave, each over half of the window's tokens (the
+// lower half's sum plus the upper's), so each token is rotated once.
 
 constexpr int MAX_VAR_WINDOW = 1024;  // tokens one entry pools (2m for overlapping windows)
-
-// sum over window tokens r0 .. n-1 of w(r) * x(r) in float64, four partial sums
-template <class Wf, class Xf>
-__device__ __forceinline__ double pool_window(int r0, int n, Wf w, Xf x) {
-    double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    int r = r0;
-    for (; r + 4 <= n; r += 4) {
-        a0 += w(r) * x(r);
-        a1 += w(r + 1) * x(r + 1);
-        a2 += w(r + 2) * x(r + 2);
-        a3 += w(r + 3) * x(r + 3);
-    }
-    for (; r < n; ++r) a0 += w(r) * x(r);
-    return (a0 + a1) + (a2 + a3);
-}
 
 template <int ACT, int VAR>
 __global__ __launch_bounds__(64) void compress_var_kernel(CompressPlan p) {
     __shared__ double alpha[MAX_VAR_WINDOW];
     const int lane = lane_id();
-    const int j = blockIdx.x, b = blockIdx.y, role = blockIdx.z;
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int role = p.has_kv ? (int)blockIdx.z : 2;  // 0 K, 1 V, 2 indexer key (z: the outputs written)
     const int m = p.m;
     const BlockGeo geo = block_geo(p, j, b, m);
     const bool kv_keep = p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring;
     if (!geo.ok || (role < 2 ? !(p.has_kv && kv_keep) : !p.has_ik)) return;  // uniform per workgroup
-    const bool overlap = VAR == V4A_POOL_OVERLAP;
+    constexpr bool overlap = VAR == V4A_POOL_OVERLAP, chan = VAR == V4A_POOL_CHANNEL_GATE;
     const int wm = overlap ? 2 * m : m;                          // tokens of the window
     const int64_t wpos0 = overlap ? geo.first - m : geo.first;   // position of window token 0
     const int r0 = wpos0 < 0 ? (int)-wpos0 : 0;                  // tokens before position 0 take no part
@@ -673,7 +665,7 @@ __global__ __launch_bounds__(64) void compress_var_kernel(CompressPlan p) {
     auto row = [&](int r) -> int64_t { return p.block_end ? (wpos0 + r) % p.t_new : (int64_t)j * m + r; };
     const int C = p.gate_c;
 
-    if (VAR != V4A_POOL_CHANNEL_GATE) {
+    if (!chan) {
         // alpha_r = softmax over the window of (gate + pos_bias[r]), float64
         double zmax = -__builtin_inf();
         for (int r = r0 + lane; r < wm; r += 64) {
@@ -692,74 +684,121 @@ __global__ __launch_bounds__(64) void compress_var_kernel(CompressPlan p) {
         for (int r = r0 + lane; r < wm; r += 64) alpha[r] = alpha[r] / zsum;
         __syncthreads();
     }
-    // pooled value of channel c (gate column c) of the rows given by x(r)
-    auto pooled_ch = [&](int c, auto x) -> double {
-        if (VAR != V4A_POOL_CHANNEL_GATE) return pool_window(r0, wm, [&](int r) { return alpha[r]; }, x);
-        double zmax = -__builtin_inf();
+    // per-channel gates: channel c's softmax over the window, its maximum and
+    // sum taken over the tokens in order, then each token's weight
+    auto zc = [&](int r, int c) -> double {
+        return (double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c];
+    };
+    struct Norm {
+        double zmax, zsum;
+    };
+    auto norm = [&](int c) -> Norm {
+        Norm n{-__builtin_inf(), 0.0};
+        if (!chan) return n;
         for (int r = r0; r < wm; ++r) {
-            const double z = (double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c];
-            zmax = z > zmax ? z : zmax;
+            const double z = zc(r, c);
+            n.zmax = z > n.zmax ? z : n.zmax;
         }
-        double zsum = 0.0;
-        for (int r = r0; r < wm; ++r)
-            zsum += exp((double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c] - zmax);
-        return pool_window(r0, wm, [&](int r) {
-            return exp((double)p.gate[((int64_t)b * rows_b + row(r)) * C + c] + (double)p.pos_bias[(int64_t)r * C + c] - zmax) / zsum;
-        }, x);
+        for (int r = r0; r < wm; ++r) n.zsum += exp(zc(r, c) - n.zmax);
+        return n;
+    };
+    auto weight = [&](int r, int c, const Norm &n) -> double {
+        return chan ? exp(zc(r, c) - n.zmax) / n.zsum : alpha[r];
     };
 
-    if (role < 2) {
-        const int D = p.D, Dn = D - ROPE_DIM, nit = Dn / 64;
-        const void *src = role == 0 ? p.raw_k : p.raw_v;
-        const int cbase = role == 0 ? 0 : D;  // gate column of dim 0 of this output
-        float nope[4];
-        for (int i = 0; i < nit; ++i) {
-            const int d = lane + 64 * i;
-            nope[i] = (float)pooled_ch(cbase + d, [&](int r) { return load_act<ACT>(src, ((int64_t)b * rows_b + row(r)) * D + d); });
-        }
-        float rx = 0.0f, ry = 0.0f;
-        if (lane < ROPE_PAIRS) {
-            const double f = p.inv_freq[lane];
-            const bool rot_each = role == 0 && VAR != V4A_POOL_ROPE_AFTER;  // keys rotated at each token's position
-            auto pair = [&](int r, double *x, double *y) {
-                const int64_t base = ((int64_t)b * rows_b + row(r)) * D + Dn + 2 * lane;
-                *x = load_act<ACT>(src, base);
-                *y = load_act<ACT>(src, base + 1);
-                if (rot_each) {
-                    double sn, cs, xr, yr;
-                    rope_sincos((double)(wpos0 + r) * f, &sn, &cs);
-                    rope_rotate(*x, *y, sn, cs, &xr, &yr);
-                    *x = xr;
-                    *y = yr;
-                }
-            };
-            double px = pooled_ch(cbase + Dn + 2 * lane, [&](int r) { double x, y; pair(r, &x, &y); return x; });
-            double py = pooled_ch(cbase + Dn + 2 * lane + 1, [&](int r) { double x, y; pair(r, &x, &y); return y; });
-            if (role == 0 && VAR == V4A_POOL_ROPE_AFTER) {
-                // the pooled key rotated once, at the block's last position
-                double sn, cs, xr, yr;
-                rope_sincos((double)(geo.first + m - 1) * f, &sn, &cs);
-                rope_rotate(px, py, sn, cs, &xr, &yr);
-                px = xr;
-                py = yr;
+    const int D = p.D, Dn = D - ROPE_DIM, dI = p.dI;
+    const int width = role < 2 ? D : dI;
+    const int n_el = role < 2 ? Dn : dI;  // elements pooled as pairs by every lane
+    const int ni = n_el > 128 ? 2 : 1;
+    const char *src = (const char *)(role == 0 ? p.raw_k : role == 1 ? p.raw_v : p.raw_ik);
+    const int cbase = role == 0 ? 0 : role == 1 ? D : (p.has_kv ? 2 * D : 0);  // gate column of dim 0
+    auto elem = [&](int r, int64_t e) { return load_pair<ACT>(src, ((int64_t)b * rows_b + row(r)) * width + e); };
+
+    // pairs: four interleaved partial sums over the window from r0, whole
+    // groups of four, then the rest into partial 0
+    float x0[2] = {0.f, 0.f}, x1[2] = {0.f, 0.f};
+    for (int i = 0; i < ni; ++i) {
+        const int pr = lane + 64 * i;
+        const bool on = 2 * pr < n_el;
+        const int64_t e = on ? 2 * pr : 0;
+        const int c0 = cbase + (int)e, c1 = c0 + 1;
+        const Norm n0 = norm(c0), n1 = norm(c1);
+        double a0[4] = {0.0, 0.0, 0.0, 0.0}, a1[4] = {0.0, 0.0, 0.0, 0.0};
+        int r = r0;
+        for (; r + 4 <= wm; r += 4) {
+            uint2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = elem(r + u, e);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                a0[u] += weight(r + u, c0, n0) * dval(v[u].x);
+                a1[u] += weight(r + u, c1, n1) * dval(v[u].y);
             }
-            rx = (float)px;
-            ry = (float)py;
         }
-        const KvView &dst = role == 0 ? p.k : p.v;
-        store_kv_row(dst, b, kv_row(dst, geo.entry), nope, nit, rx, ry);
-    } else {
-        const int dI = p.dI, nit = dI / 64 + (dI % 64 ? 1 : 0);
-        const int cbase = p.has_kv ? 2 * p.D : 0;
-        for (int i = 0; i < nit; ++i) {
-            const int d = lane + 64 * i;
-            const bool on = d < dI;
-            const double acc = on ? pooled_ch(cbase + d, [&](int r) {
-                return load_act<ACT>(p.raw_ik, ((int64_t)b * rows_b + row(r)) * dI + d);
-            }) : 0.0;
-            store_ik_value(p.ik, b, geo.entry, d, on, (float)acc);
+        for (; r < wm; ++r) {
+            const uint2 v = elem(r, e);
+            a0[0] += weight(r, c0, n0) * dval(v.x);
+            a1[0] += weight(r, c1, n1) * dval(v.y);
+        }
+        x0[i] = (float)sum4(a0);
+        x1[i] = (float)sum4(a1);
+    }
+    if (role == 2) {
+        store_ik_pairs(p.ik, b, geo.entry, x0, x1, ni, dI);
+        return;
+    }
+    // RoPE pair rp: the lower half pools the window's first tokens, the upper
+    // half the rest; keys rotated at each token's position, or (RoPE after
+    // pooling) the pooled key once at the block's last position
+    const bool up = lane >= 32;
+    const int rp = lane & 31;
+    const double f = p.inv_freq[rp];
+    const bool rot_each = role == 0 && VAR != V4A_POOL_ROPE_AFTER;
+    const int n = wm - r0, nl = (n + 1) / 2;
+    const int ra = up ? r0 + nl : r0, nh = up ? n - nl : nl;
+    const int cx = cbase + Dn + 2 * rp, cy = cx + 1;
+    const Norm nx = norm(cx), ny = norm(cy);
+    double ax[4] = {0.0, 0.0, 0.0, 0.0}, ay[4] = {0.0, 0.0, 0.0, 0.0};
+    auto rope_tok = [&](int r, double *x, double *y) {
+        const uint2 v = elem(r, Dn + 2 * rp);
+        *x = dval(v.x);
+        *y = dval(v.y);
+        if (rot_each) {
+            double sn, cs, xr, yr;
+            rope_sincos((double)(wpos0 + r) * f, &sn, &cs);
+            rope_rotate(*x, *y, sn, cs, &xr, &yr);
+            *x = xr;
+            *y = yr;
+        }
+    };
+    int s = 0;
+    for (; s + 4 <= nh; s += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            double x, y;
+            rope_tok(ra + s + u, &x, &y);
+            ax[u] += weight(ra + s + u, cx, nx) * x;
+            ay[u] += weight(ra + s + u, cy, ny) * y;
         }
     }
+    for (; s < nh; ++s) {
+        double x, y;
+        rope_tok(ra + s, &x, &y);
+        ax[0] += weight(ra + s, cx, nx) * x;
+        ay[0] += weight(ra + s, cy, ny) * y;
+    }
+    const double hx = sum4(ax), hy = sum4(ay);
+    const double ox = swap_halves(hx), oy = swap_halves(hy);
+    double px = hx + ox, py = hy + oy;  // used on the lower half: its sum plus the upper's
+    if (role == 0 && VAR == V4A_POOL_ROPE_AFTER) {
+        double sn, cs, xr, yr;
+        rope_sincos((double)(geo.first + m - 1) * f, &sn, &cs);
+        rope_rotate(px, py, sn, cs, &xr, &yr);
+        px = xr;
+        py = yr;
+    }
+    const KvView &dst = role == 0 ? p.k : p.v;
+    store_kv_pairs(dst, b, kv_row(dst, geo.entry), x0, x1, ni, !up, rp, (float)px, (float)py);
 }
 
 template <int ACT>
@@ -792,14 +831,15 @@ hipError_t launch_compress(const CompressPlan &p, hipStream_t s) {
     dim3 grid(p.block_end ? 1 : p.t_new / p.m, p.B);  // block mode: one block per batch element
     if (grid.x == 0 || grid.y == 0) return hipSuccess;
     if (p.variant != V4A_POOL_BLOCK) {
-        const dim3 g3(grid.x, grid.y, 3);  // K, V, indexer key
+        const dim3 g3(grid.x, grid.y, (p.has_kv ? 2u : 0u) + (p.has_ik ? 1u : 0u));  // the outputs written
         if (p.act == 0) launch_variant<0>(p, g3, s);
         else launch_variant<1>(p, g3, s);
     } else if (p.m <= SMALL_M) {
         if (p.act == 0) launch_small<0>(p, grid, s);
         else launch_small<1>(p, grid, s);
     } else {
-        const dim3 gx(grid.x * 3, grid.y);  // K, V, indexer key of each block side by side
+        const unsigned n_out = (p.has_kv ? 2u : 0u) + (p.has_ik ? 1u : 0u);
+        const dim3 gx(grid.x * n_out, grid.y);  // the outputs of each block side by side
         if (p.act == 0) hipLaunchKernelGGL(compress_kernel<0>, gx, dim3(64 * CW), 0, s, p);
         else hipLaunchKernelGGL(compress_kernel<1>, gx, dim3(64 * CW), 0, s, p);
     }
