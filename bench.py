@@ -30,6 +30,10 @@ buffer and attending for every new token (the CSA layers through the indexer's
 top-1024). Its roofline line is the indexer's FP4 contraction against the
 MXFP4 MFMA peak.
 
+--workload compress times every compressor form (CSA blocks of 4, HCA blocks of
+128, window rows, the three variants) over 4 x 65,536 new raw tokens at 1M
+positions, each with its own roofline line.
+
 --workload stack runs the decode step through a 43-layer attention stack (two
 window-only layers, then CSA and HCA alternating) at 1M context, four steps
 captured in one HIP graph, and reports the graph's time per step next to the
