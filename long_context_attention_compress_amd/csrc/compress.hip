@@ -380,8 +380,9 @@ __global__ __launch_bounds__(64 * CW, 4) void compress_kernel(CompressPlan p) {
 
 
 // Blocks of at most SMALL_M tokens (the per-token window append, the CSA
-// block). Three waves per block, one per output: wave 0 the K entry, wave 1
-// the V entry, wave 2 the indexer key, so the three encodes run side by side.
+// block). One wave per block and output written (the K entry, the V entry,
+// the indexer key), so the encodes run side by side; the first wave evaluates
+// the gate softmax for all of them.
 // Every global load is issued before any arithmetic, so one memory round trip
 // precedes the encode. Lane l holds element pairs (2p, 2p + 1), p = l + 64 i,
 // of each row: a raw row is read as 32-bit words (two BF16 values) or 64-bit
@@ -393,13 +394,18 @@ constexpr int SMALL_M = 4;
 
 template <int ACT, int M>
 __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
-    const int lane = lane_id(), role = threadIdx.x >> 6;
+    // one wave per output written: K, V (when given), then the indexer key
+    const int lane = lane_id(), wave = threadIdx.x >> 6;
+    const int role = p.has_kv ? wave : 2;
     const int j = blockIdx.x, b = blockIdx.y;
     const BlockGeo geo = block_geo(p, j, b, M);
     const int64_t tok0 = geo.tok0;
     const int64_t entry = geo.entry;
     const bool do_kv = p.has_kv && (p.k.ring == 0 || (int64_t)j >= (int64_t)gridDim.x - p.k.ring);
-    if (!geo.ok || (role < 2 ? !do_kv : !p.has_ik)) return;  // uniform per wave
+    if (!geo.ok) return;  // uniform per workgroup
+    // K and V of an entry outside a ring store's kept rows are not written;
+    // such waves still reach the barrier below and leave after it
+    const bool active = role < 2 ? do_kv : true;
     const int D = p.D, Dn = D - ROPE_DIM;
     const int dI = p.dI;
     const int width = role < 2 ? D : dI;
@@ -441,36 +447,43 @@ __global__ __launch_bounds__(192) void compress_small_kernel(CompressPlan p) {
     double fx = f;
     asm volatile("" : "+v"(fx) :: "memory");
 
-    // alpha_r = softmax_r(gate + pos_bias) in float64: lane r evaluates token
-    // r's exponential and quotient, the wave reads them back; the sum runs
-    // over r = 0 .. M-1 in order.
+    // alpha_r = softmax_r(gate + pos_bias) in float64, by the first wave for
+    // all: lane r evaluates token r's exponential and quotient, the wave reads
+    // them back (the sum runs over r = 0 .. M-1 in order) and lanes 0..M-1
+    // publish the weights in LDS.
+    __shared__ double s_alpha[SMALL_M];
     double alpha[M];
-    if constexpr (M > 1) {
-        double z[M];
-#pragma unroll
-        for (int r = 0; r < M; ++r) z[r] = (double)gz[r] + (double)gb[r];
-        double zmax = z[0];
-#pragma unroll
-        for (int r = 1; r < M; ++r) zmax = z[r] > zmax ? z[r] : zmax;
-        double zl = z[0];
-#pragma unroll
-        for (int r = 1; r < M; ++r) zl = lane == r ? z[r] : zl;
-        const double el = exp(zl - zmax);
-        double e[M], zsum = 0.0;
-#pragma unroll
-        for (int r = 0; r < M; ++r) {
-            e[r] = lane_bcast(el, r);
-            zsum += e[r];
-        }
-        double eo = e[0];
-#pragma unroll
-        for (int r = 1; r < M; ++r) eo = lane == r ? e[r] : eo;
-        const double al = eo / zsum;
-#pragma unroll
-        for (int r = 0; r < M; ++r) alpha[r] = lane_bcast(al, r);
-    } else {
+    if constexpr (M == 1) {
         alpha[0] = 1.0;
+    } else {
+        if (wave == 0) {
+            double z[M];
+#pragma unroll
+            for (int r = 0; r < M; ++r) z[r] = (double)gz[r] + (double)gb[r];
+            double zmax = z[0];
+#pragma unroll
+            for (int r = 1; r < M; ++r) zmax = z[r] > zmax ? z[r] : zmax;
+            double zl = z[0];
+#pragma unroll
+            for (int r = 1; r < M; ++r) zl = lane == r ? z[r] : zl;
+            const double el = exp(zl - zmax);
+            double e[M], zsum = 0.0;
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                e[r] = lane_bcast(el, r);
+                zsum += e[r];
+            }
+            double eo = e[0];
+#pragma unroll
+            for (int r = 1; r < M; ++r) eo = lane == r ? e[r] : eo;
+            const double al = eo / zsum;
+            if (lane < M) s_alpha[lane] = al;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < M; ++r) alpha[r] = s_alpha[r];
     }
+    if (!active) return;
 
     float x0[2] = {0.f, 0.f}, x1[2] = {0.f, 0.f};
 #pragma unroll
@@ -818,7 +831,7 @@ static void launch_small(const CompressPlan &p, dim3 grid, hipStream_t s) {
         hipLaunchKernelGGL((compress_rows_kernel<ACT>), g2, dim3(nt), 0, s, p);
         return;
     }
-    const dim3 blk(p.has_ik ? 192 : 128);  // the indexer-key wave only when there is one
+    const dim3 blk((p.has_kv ? 128 : 0) + (p.has_ik ? 64 : 0));  // one wave per output written
     switch (p.m) {
         case 1: hipLaunchKernelGGL((compress_small_kernel<ACT, 1>), grid, blk, 0, s, p); break;
         case 2: hipLaunchKernelGGL((compress_small_kernel<ACT, 2>), grid, blk, 0, s, p); break;
