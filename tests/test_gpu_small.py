@@ -24,7 +24,10 @@ pytestmark = pytest.mark.gpu
 
 # ------------------------------------------------------------- compress ----
 
-@pytest.mark.parametrize('m,pos0,T,ring', [(4, 256, 64, 0), (1, 8, 40, 64), (1, 8, 200, 64), (128, 0, 384, 0)])
+# (1, 7, 63, 32): an odd number of window rows (the last pair of tokens has one) into a ring
+# that keeps the last 32
+@pytest.mark.parametrize('m,pos0,T,ring', [(4, 256, 64, 0), (1, 8, 40, 64), (1, 8, 200, 64), (1, 7, 63, 32),
+                                           (128, 0, 384, 0)])
 def test_compress_f32(m, pos0, T, ring):
     print(f'compress f32 m={m} pos0={pos0} T={T} ring={ring}', flush=True)
     raw = synth.raw_tokens(100 + m, 2, T, 128, m, 64, std=0.09, bf16=False)
@@ -52,7 +55,8 @@ def test_compress_f32(m, pos0, T, ring):
     assert_close_rms(gu[:, e0:], u32, 1e-6, 'ik')
 
 
-@pytest.mark.parametrize('m,pos0,T', [(4, 1024, 256), (1, 4000, 128), (128, 131072, 512)])
+# (1, 4001, 201): an odd number of window rows at an odd position, the ring keeping the last 128
+@pytest.mark.parametrize('m,pos0,T', [(4, 1024, 256), (1, 4000, 128), (1, 4001, 201), (128, 131072, 512)])
 def test_compress_fp8_mxfp4(m, pos0, T):
     print(f'compress fp8 m={m} pos0={pos0} T={T}', flush=True)
     B = 2
