@@ -92,6 +92,38 @@ def test_compress_fp8_mxfp4(m, pos0, T):
     assert np.array_equal(gi['e2m1'][:, e0:e0 + ne], packed)
 
 
+@pytest.mark.parametrize('m,variant', [(1, 'block'), (4, 'block'), (128, 'block'), (4, 'overlap')])
+def test_compress_wide_rows(m, variant):
+    """Rows wider than one pair per lane: float32 K and V of dim 256 (192 no-RoPE dims, two
+    pair iterations) and MXFP4 indexer keys of dim 192 (the second iteration half full), in
+    BF16 activations, against the oracle: the float32 entries within float32 rounding, the
+    MX scales and E2M1 codes exactly."""
+    print(f'compress wide rows m={m} {variant}', flush=True)
+    B, D, dI, pos0 = 2, 256, 192, 4 * 128
+    T = 4 * m if m > 1 else 37
+    extra = m if variant == 'overlap' else 0
+    raw = synth.raw_tokens(300 + m, B, T + extra, D, m, dI, bf16=True, prefix=f'wide/{variant}')
+    bias = raw['pos_bias'] if variant == 'block' else synth.normal(301, f'wide/b/{m}', (2 * m,), 0.1)
+    rows = (pos0 + T) // m
+    ks, vs = v4.KVStore.empty(B, rows, D, v4.KV_F32), v4.KVStore.empty(B, rows, D, v4.KV_F32)
+    iks = v4.IKStore.empty(B, rows, dI, v4.IK_MXFP4)
+    v4.csa_compress(dev(raw['gate']), dev(bias), pos0, bf16_dev(raw['raw_k']), bf16_dev(raw['raw_v']), ks, vs,
+                    bf16_dev(raw['raw_ik']), iks, variant=v4.POOL_OVERLAP if variant == 'overlap' else v4.POOL_BLOCK)
+    torch.cuda.synchronize()
+    if variant == 'block':
+        k32, v32, u32 = OC.compress(raw['raw_k'], raw['raw_v'], raw['gate'], bias, pos0, raw_ik=raw['raw_ik'])
+    else:
+        k32, v32, u32 = OC.compress_variant(variant, raw['raw_k'], raw['raw_v'], raw['gate'], bias, pos0,
+                                            raw_ik=raw['raw_ik'])
+    e0 = pos0 // m
+    assert_close_rms(host_kv(ks)['f32'][:, e0:], k32, 1e-6, 'k')
+    assert_close_rms(host_kv(vs)['f32'][:, e0:], v32, 1e-6, 'v')
+    packed, scales = F.mxfp4_quantize(u32)
+    gi = host_ik(iks)
+    assert np.array_equal(gi['e8m0'][:, e0:], scales)
+    assert np.array_equal(gi['e2m1'][:, e0:], packed)
+
+
 @pytest.mark.parametrize('m', [1, 4, 128])
 def test_compress_block_mode_device_positions(m):
     """Block mode: each batch element's block ends at a device position, raw inputs are a
