@@ -7,15 +7,16 @@
 // große Wirkung", section "Komprimierte Erinnerung für längere Kontexte"]: the
 // last 64 values carry RoPE and stay BF16, the rest is FP8.
 //
-// Four waves per (entry, batch element, output) for long blocks (a quarter
-// of the tokens each), three waves (one per output) in one workgroup for
-// blocks of up to four tokens, and one wave per output for each two tokens of
-// a chunk of window rows (m = 1). The gate weights, the RoPE rotation and the
-// weighted sum are evaluated in float64 and the entry is rounded to float32
-// before it is encoded, so every encoding decision (FP8 scale and codes, BF16
-// rounding, MX exponent and E2M1 codes) is taken on a float32 value.
-// Compression is a small share of decode time (one block per m tokens), so the
-// kernels favour exactness over speed.
+// Eight waves per (entry, batch element, output) for long blocks (an eighth
+// of the tokens each), one wave per output in one workgroup for blocks of up
+// to four tokens, and one wave per output for each two tokens of a chunk of
+// window rows (m = 1); every lane holds pairs of adjacent elements of a row.
+// The gate weights, the RoPE rotation and the weighted sum are evaluated in
+// float64 and the entry is rounded to float32 before it is encoded, so every
+// encoding decision (FP8 scale and codes, BF16 rounding, MX exponent and E2M1
+// codes) is taken on a float32 value. That float64 work, not HBM, bounds these
+// kernels; compression is a small share of decode time (one block per m
+// tokens), so they keep the exact path.
 
 #include "common.hpp"
 
